@@ -1,0 +1,53 @@
+"""Seeded synthetic inputs: identical bits run to run, and the stated distributions."""
+import numpy as np
+
+import workloads as W
+
+
+def test_seeded_bits_repeat():
+    for wid in (1, 2, 3, 4, 5):
+        wl = W.SMALL[wid]
+        for gi in range(len(wl.groups)):
+            a = W.make_grad(wl, gi, 2)
+            b = W.make_grad(wl, gi, 2)
+            assert a.tobytes() == b.tobytes()
+            c = W.make_grad(wl, gi, 3)
+            assert a.tobytes() != c.tobytes()        # fresh gradient every step
+            X1, M1, Q1 = W.make_state(wl, gi)
+            X2, M2, Q2 = W.make_state(wl, gi)
+            assert X1.tobytes() == X2.tobytes() and Q1.tobytes() == Q2.tobytes()
+            assert not M1.any()
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125, -3.0e-5, 65504.0], dtype=np.float32)
+    b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins; 1 + 1.5 * 2^-8 rounds up
+    assert b[0] == 1.0 and b[1] == 1.0 and b[2] == 1.0078125 and b[3] == 1.0078125
+    assert abs(b[4] - x[4]) <= abs(x[4]) * 2 ** -8
+
+
+def test_distributions():
+    wl = W.SMALL[1]
+    X, M, Q = W.make_state(wl, 0)
+    assert abs(X.std() - 0.02) < 0.002
+    assert np.allclose(np.linalg.norm(Q[0].astype(np.float64), axis=0), 1.0, atol=1e-6)
+    G = W.make_grad(wl, 0, 1)
+    assert abs(G.std() - 1e-2) < 1e-3
+    # low-rank + noise: rank-k signal dominates, noise floor at noise_std
+    wl2 = W.SMALL[2]
+    G2 = W.make_grad(wl2, 0, 1)[0].astype(np.float64)
+    s = np.linalg.svd(G2, compute_uv=False)
+    k = wl2.grad_args["k"]
+    assert s[k - 1] > 100 * s[k]
+    # per-matrix log-uniform scale within [lo, hi]
+    wl3 = W.SMALL[3]
+    G3 = W.to_f64(W.make_grad(wl3, 0, 1), "bf16")
+    sd = G3.reshape(G3.shape[0], -1).std(axis=1)
+    assert np.all(sd > 0.5e-5) and np.all(sd < 2e-2)
+    # decaying spectrum: 10^(-6 i / n)
+    wl5 = W.SMALL[5]
+    G5 = W.make_grad(wl5, 0, 1)[0].astype(np.float64)
+    s5 = np.linalg.svd(G5, compute_uv=False)
+    n = G5.shape[0]
+    assert abs(np.log10(s5[0] / s5[n // 2]) - 3.0) < 0.05

@@ -1,0 +1,250 @@
+"""Seeded synthetic inputs for the Dion step.
+
+This module is shared by the fp64 oracle's tests and by the GPU path's tests
+and benchmark.  It holds the workload definitions and the random draws only:
+none of the optimizer's arithmetic lives here.  Every value is drawn in fp64
+from numpy's PCG64 and rounded once (round-to-nearest-even) to its storage type,
+so both sides read identical bits.
+
+The five workloads are stacks of same-shape 2-D weight matrices, the batching
+unit used by the DASH page ("Batched Block Preconditioning", 3-D tensor
+stacking); the shapes stand in for the models the pages train (a 2048-hidden
+Llama on the DASH page's "Experimentele Resultaten", 10^8 to 10^9 parameter
+models on the rivista.ai Dion page).  No dataset is read: gradients are
+synthetic with the distributions listed per workload.
+
+Stream keys: every array is drawn from
+``Generator(PCG64(SeedSequence([seed, wid, group, matrix, step, tag, block])))``
+so that any matrix (and any 1024-row block of it) can be regenerated alone.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+# stream tags
+_T_X, _T_Q, _T_G, _T_U, _T_V, _T_NOISE, _T_SCALE = 0, 1, 2, 3, 4, 5, 6
+_ROW_BLOCK = 1024
+
+
+# ----------------------------------------------------------------------------
+# bf16 storage helpers (encoding only)
+# ----------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits (uint16) to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of a stored array (``dtype`` is 'f32' or 'bf16')."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def store(a64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to the storage type (f32 RNE, then bf16 RNE)."""
+    f = a64.astype(np.float32)
+    return f32_to_bf16_bits(f) if dtype == "bf16" else f
+
+
+# ----------------------------------------------------------------------------
+# workload definitions
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Group:
+    """One stack of ``batch`` matrices of shape m x n, updated at rank ``rank``."""
+    batch: int
+    m: int
+    n: int
+    rank: int
+
+
+@dataclass(frozen=True)
+class Workload:
+    wid: int                 # workload id (1..5), part of every stream key
+    name: str
+    groups: tuple
+    mu: float
+    lr: float = 0.01
+    eps: float = 1e-8
+    steps: int = 3
+    x_dtype: str = "f32"     # storage type of X (and of G)
+    grad: str = "gauss"      # gradient recipe, see make_grad
+    grad_args: dict = field(default_factory=dict)
+
+    @property
+    def g_dtype(self) -> str:
+        return self.x_dtype
+
+    def with_groups(self, *groups: Group, name: str | None = None, steps: int | None = None) -> "Workload":
+        return replace(self, groups=tuple(groups), name=name or self.name + "-small",
+                       steps=self.steps if steps is None else steps)
+
+    def params(self) -> int:
+        return sum(g.batch * g.m * g.n for g in self.groups)
+
+
+def _frac_rank(m: int, n: int, num: int, den: int) -> int:
+    return (num * min(m, n)) // den
+
+
+WORKLOADS = {
+    1: Workload(1, "single-256x512-r32", (Group(1, 256, 512, 32),), mu=0.95, steps=10,
+                grad="gauss", grad_args={"std": 1e-2}),
+    2: Workload(2, "attn-24x1024x1024-r256", (Group(24, 1024, 1024, 256),), mu=0.95, steps=5,
+                grad="lowrank_noise", grad_args={"k": 16, "noise_std": 1e-3}),
+    3: Workload(3, "llama2048-bf16-r1/8",
+                (Group(64, 2048, 2048, 256), Group(32, 5632, 2048, 256), Group(16, 2048, 5632, 256)),
+                mu=0.95, steps=3, x_dtype="bf16",
+                grad="loguniform_gauss", grad_args={"lo": 1e-5, "hi": 1e-2}),
+    4: Workload(4, "mlp-8192x28672-r512", (Group(1, 8192, 28672, 512),), mu=0.95, steps=3,
+                grad="student_t", grad_args={"nu": 3.0, "scale": 1e-3}),
+    5: Workload(5, "fullrank-8x4096x4096", (Group(8, 4096, 4096, 4096),), mu=0.9, steps=3,
+                grad="decaying_spectrum", grad_args={"decades": 6.0}),
+}
+
+
+def get(wid: int) -> Workload:
+    return WORKLOADS[wid]
+
+
+# Reduced-size versions with the same recipes, for CPU-speed parity tests.
+# Shapes span several 64/128 tiles and leave ragged tails.
+SMALL = {
+    1: WORKLOADS[1].with_groups(Group(1, 256, 512, 32), name="single-256x512-r32", steps=4),
+    2: WORKLOADS[2].with_groups(Group(3, 320, 288, 72), steps=3),
+    3: WORKLOADS[3].with_groups(Group(2, 200, 136, 17), Group(2, 136, 200, 24), steps=2),
+    4: WORKLOADS[4].with_groups(Group(1, 192, 1000, 40), steps=2),
+    5: WORKLOADS[5].with_groups(Group(2, 160, 160, 160), steps=2),
+}
+
+
+# ----------------------------------------------------------------------------
+# draws
+# ----------------------------------------------------------------------------
+def _rng(seed: int, wid: int, gi: int, mi: int, step: int, tag: int, block: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wid, gi, mi, step, tag, block])))
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill_blocks(out: np.ndarray, fn, nthreads: int | None = None) -> None:
+    """Run fn(mi, r0, r1) -> fp64 block for every matrix and 1024-row block, in threads."""
+    b, m, _ = out.shape
+    tasks = [(mi, r0, min(m, r0 + _ROW_BLOCK)) for mi in range(b) for r0 in range(0, m, _ROW_BLOCK)]
+
+    def run(t):
+        mi, r0, r1 = t
+        out[mi, r0:r1] = fn(mi, r0, r1)
+
+    with ThreadPoolExecutor(nthreads or _workers()) as ex:
+        list(ex.map(run, tasks))
+
+
+def make_state(wl: Workload, gi: int, seed: int = 0):
+    """Initial (X, M, Q) of group ``gi``.
+
+    X ~ N(0, 0.02^2) in the workload's storage type, M = 0 (fp32),
+    Q = Gaussian n x r with each column scaled to unit norm (fp32).
+    """
+    g = wl.groups[gi]
+    xdt = np.uint16 if wl.x_dtype == "bf16" else np.float32
+    X = np.empty((g.batch, g.m, g.n), dtype=xdt)
+
+    def xblock(mi, r0, r1):
+        return store(0.02 * _rng(seed, wl.wid, gi, mi, 0, _T_X, r0 // _ROW_BLOCK).standard_normal((r1 - r0, g.n)),
+                     wl.x_dtype)
+
+    _fill_blocks(X, xblock)
+    M = np.zeros((g.batch, g.m, g.n), dtype=np.float32)
+    Q = np.empty((g.batch, g.n, g.rank), dtype=np.float32)
+    for mi in range(g.batch):
+        q = _rng(seed, wl.wid, gi, mi, 0, _T_Q).standard_normal((g.n, g.rank))
+        if g.rank:
+            q /= np.linalg.norm(q, axis=0, keepdims=True)
+        Q[mi] = q.astype(np.float32)
+    return X, M, Q
+
+
+def _haar(rng: np.random.Generator, n: int) -> np.ndarray:
+    z = rng.standard_normal((n, n))
+    q, t = np.linalg.qr(z)
+    return q * np.sign(np.diag(t))[None, :]
+
+
+def make_grad(wl: Workload, gi: int, step: int, seed: int = 0) -> np.ndarray:
+    """Gradient G_t of group ``gi`` at step ``step`` (1-based), fresh every step.
+
+    Recipes (N(0, v) names a variance):
+      gauss             G ~ N(0, std^2)
+      lowrank_noise     G = U V^T + N(0, noise_std^2), U (m x k), V (n x k) ~ N(0, 1)
+      loguniform_gauss  G = c_i N(0, 1), c_i ~ LogUniform(lo, hi) drawn once per matrix
+      student_t         G = scale * t_nu
+      decaying_spectrum G = U diag(10^(-decades i / n)) V^T, U, V Haar orthogonal
+    """
+    g = wl.groups[gi]
+    a = wl.grad_args
+    dt = wl.g_dtype
+    out = np.empty((g.batch, g.m, g.n), dtype=np.uint16 if dt == "bf16" else np.float32)
+    kind = wl.grad
+
+    if kind == "gauss":
+        def fn(mi, r0, r1):
+            return store(a["std"] * _rng(seed, wl.wid, gi, mi, step, _T_G, r0 // _ROW_BLOCK)
+                         .standard_normal((r1 - r0, g.n)), dt)
+        _fill_blocks(out, fn)
+    elif kind == "lowrank_noise":
+        k = a["k"]
+        UV = []
+        for mi in range(g.batch):
+            U = _rng(seed, wl.wid, gi, mi, step, _T_U).standard_normal((g.m, k))
+            V = _rng(seed, wl.wid, gi, mi, step, _T_V).standard_normal((g.n, k))
+            UV.append((U, V))
+
+        def fn(mi, r0, r1):
+            U, V = UV[mi]
+            noise = _rng(seed, wl.wid, gi, mi, step, _T_NOISE, r0 // _ROW_BLOCK).standard_normal((r1 - r0, g.n))
+            return store(U[r0:r1] @ V.T + a["noise_std"] * noise, dt)
+        _fill_blocks(out, fn)
+    elif kind == "loguniform_gauss":
+        lo, hi = math.log(a["lo"]), math.log(a["hi"])
+        scales = [math.exp(_rng(seed, wl.wid, gi, mi, 0, _T_SCALE).uniform(lo, hi)) for mi in range(g.batch)]
+
+        def fn(mi, r0, r1):
+            return store(scales[mi] * _rng(seed, wl.wid, gi, mi, step, _T_G, r0 // _ROW_BLOCK)
+                         .standard_normal((r1 - r0, g.n)), dt)
+        _fill_blocks(out, fn)
+    elif kind == "student_t":
+        def fn(mi, r0, r1):
+            return store(a["scale"] * _rng(seed, wl.wid, gi, mi, step, _T_G, r0 // _ROW_BLOCK)
+                         .standard_t(a["nu"], (r1 - r0, g.n)), dt)
+        _fill_blocks(out, fn)
+    elif kind == "decaying_spectrum":
+        if g.m != g.n:
+            raise ValueError("decaying_spectrum needs square matrices")
+        n = g.n
+        sig = 10.0 ** (-a["decades"] * np.arange(n) / n)
+
+        def one(mi):
+            U = _haar(_rng(seed, wl.wid, gi, mi, step, _T_U), n)
+            V = _haar(_rng(seed, wl.wid, gi, mi, step, _T_V), n)
+            out[mi] = store((U * sig[None, :]) @ V.T, dt)
+        with ThreadPoolExecutor(max(1, min(g.batch, _workers() // 4 or 1))) as ex:
+            list(ex.map(one, range(g.batch)))
+    else:
+        raise ValueError(f"unknown gradient recipe {kind!r}")
+    return out
