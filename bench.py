@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the Dion step on one MI355X.
+
+A "step" is one Dion update of every matrix of the workload (all stacks),
+with gradients already resident in HBM.  The default workload is the
+rank-fraction-1/4 attention stack: 24 fp32 matrices of 1024 x 1024 at r = 256
+with low-rank-plus-noise gradients (see workloads/).  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+
+Metric: updates/s (steps per second over the whole workload), with the
+effective parameter bandwidth (algorithmic bytes / step time) and its share of
+the 8 TB/s HBM peak alongside.  The "roofline" entry times the dominant kernel
+live (HIP events recorded by the library at its phase boundaries, on the
+stream the kernels run on); the "cpu_baseline" entry times the fp64 oracle on
+the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3, "bf16": 2500.0}
+
+
+def algorithmic_bytes(wl) -> float:
+    """Per step: read G, read+write M (fp32), read+write X, read+write Q (fp32)."""
+    bx = 2 if wl.x_dtype == "bf16" else 4
+    tot = 0.0
+    for g in wl.groups:
+        tot += g.batch * (g.m * g.n * (bx + 8 + 2 * bx) + 8 * g.n * g.rank)
+    return tot
+
+
+def algorithmic_flops(wl) -> float:
+    """Per step: four rank-r contractions plus CholeskyQR2 (two Grams, Cholesky, solves)."""
+    tot = 0.0
+    for g in wl.groups:
+        m, n, r = g.m, g.n, g.rank
+        tot += g.batch * (8.0 * m * n * r + 6.0 * m * r * r + 2.0 * r ** 3 / 3.0)
+    return tot
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return int(max(n)) if n else (os.cpu_count() or 1)
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample of the workload.
+
+    Every matrix of every stack is stepped once (step-1 inputs); the per-stack pass is
+    repeated while the budget lasts, then the mean time per full step is reported.
+    Stacks whose single matrix already exceeds the budget are sampled: the per-matrix
+    time of the matrices that fit is scaled to the whole stack.
+    """
+    import numpy as np
+
+    import workloads as W
+    from oracle import dion_step
+    t_all = time.perf_counter()
+    per_group = []
+    for gi, g in enumerate(wl.groups):
+        X, M, Q = W.make_state(wl, gi)
+        G = W.make_grad(wl, gi, 1)
+        args = [(W.to_f64(X[i], wl.x_dtype), W.to_f64(G[i], wl.g_dtype), M[i].astype(np.float64),
+                 Q[i].astype(np.float64)) for i in range(g.batch)]
+        share = budget_s / len(wl.groups)
+        times, t0 = [], time.perf_counter()
+        while True:
+            for i in range(g.batch):
+                t1 = time.perf_counter()
+                dion_step(*args[i], wl.mu, wl.lr, wl.eps)
+                times.append(time.perf_counter() - t1)
+                if time.perf_counter() - t0 > share and len(times) >= 1:
+                    break
+            if time.perf_counter() - t0 > share:
+                break
+        per_group.append((g, float(np.mean(times)), len(times)))
+    step_s = sum(g.batch * t for g, t, _ in per_group)
+    sample = "; ".join(f"{k} matrix steps of the {g.batch}x{g.m}x{g.n} r={g.rank} stack"
+                       for g, _, k in per_group)
+    return {"value": 1.0 / step_s, "unit": "updates/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": sample + f" (step-1 inputs, fp64 numpy/OpenBLAS; mean time per matrix x stack size; "
+                               f"{time.perf_counter() - t_all:.1f} s of CPU work)",
+            "s_per_step": step_s}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--grads", type=int, default=3, help="distinct resident gradients cycled through")
+    ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the Dion step here has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import rank_orthonormalized_optimizer_amd as dion
+    import workloads as W
+    from rank_orthonormalized_optimizer_amd._lib import NUM_PHASES, PHASES
+    from rank_orthonormalized_optimizer_amd.api import workspace_for
+
+    dev = torch.device("cuda:0")
+    wl = W.get(args.workload)
+    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    stacks = []
+    for gi, g in enumerate(wl.groups):
+        X, M, Q = W.make_state(wl, gi)
+        grads = [dev_t(W.make_grad(wl, gi, t)) for t in range(1, args.grads + 1)]
+        stacks.append(dict(g=g, X=dev_t(X), M=dev_t(M), Q=dev_t(Q), G=grads,
+                           flags=torch.zeros(g.batch, dtype=torch.int32, device=dev),
+                           ws=workspace_for(g.m, g.n, g.batch, g.rank, dev)))
+    opts = 0 if args.no_sticky else dion.OPT_STICKY_F64
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(k, events=None):
+        for si, s in enumerate(stacks):
+            g = s["g"]
+            dion.step_(s["X"], s["G"][k % len(s["G"])], s["M"], s["Q"], g.rank, wl.mu, wl.lr, wl.eps,
+                       workspace=s["ws"], flags=s["flags"], options=opts, stream=stream,
+                       events=None if events is None else events[si])
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for k in range(args.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+
+    # phase events for every call of the timed region (created by one record each beforehand)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(NUM_PHASES + 1)] for _ in stacks]
+           for _ in range(args.steps)]
+    for step_e in evs:
+        for call_e in step_e:
+            for e in call_e:
+                e.record(stream)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        one_step(args.warmup + k, events=evs[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # per-phase device times, averaged over the timed steps (summed over stacks)
+    phase_ms = {p: 0.0 for p in PHASES}
+    for step_e in evs:
+        for call_e in step_e:
+            for i, p in enumerate(PHASES):
+                phase_ms[p] += call_e[i].elapsed_time(call_e[i + 1]) / args.steps
+    n64 = int(sum(int((s["flags"] & dion.FLAG_F64).ne(0).sum()) for s in stacks))
+    nbad = int(sum(int((s["flags"] & dion.FLAG_NONFINITE).ne(0).sum()) for s in stacks))
+    nmat = sum(g.batch for g in wl.groups)
+
+    # dominant single-kernel phase and its algorithmic flops per launch
+    mnr64 = sum(int((s["flags"] & dion.FLAG_F64).ne(0).sum()) * s["g"].m * s["g"].n * s["g"].rank
+                for s in stacks)
+    mnr = sum(g.batch * g.m * g.n * g.rank for g in wl.groups)
+    kernels = {
+        "f64_product": ("f64", 2.0 * mnr64, "P0 = (M+G) Q, fp64 MFMA"),
+        "f64_backproject": ("f64", 2.0 * mnr64, "R = (M+G)^T P, fp64 MFMA"),
+        "f32_product": ("f32", 2.0 * (mnr - mnr64), "P0 = (M+G) Q, fp32 MFMA"),
+        "f32_backproject": ("f32", 2.0 * (mnr - mnr64), "R = (M+G)^T P, fp32 MFMA"),
+        "update": ("f32", 4.0 * mnr, "M, X update pass, fp32 MFMA"),
+    }
+    dom = max(kernels, key=lambda k: phase_ms[k])
+    dt_, flops, what = kernels[dom]
+    launches = len(stacks)
+    achieved = flops / (phase_ms[dom] * 1e-3) / 1e12 if phase_ms[dom] > 0 else 0.0
+
+    eff_gbs = algorithmic_bytes(wl) / (ms * 1e-3) / 1e9
+    dtype = "f32" if n64 == 0 else ("f64+f32" if n64 == nmat else "f32|f64+f32")
+    if wl.x_dtype == "bf16":
+        dtype += " (bf16 X, G)"
+    out = {
+        "metric": "Dion updates/s and effective param GB/s (% HBM roofline) at rank frac 1/4",
+        "value": 1000.0 / ms,
+        "unit": "updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name,
+                   "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],
+                   "mu": wl.mu, "lr": wl.lr, "eps": wl.eps, "grad": wl.grad,
+                   "sticky_fp64": not args.no_sticky},
+        "effective_param_GBps": eff_gbs,
+        "pct_hbm_roofline": 100.0 * eff_gbs / HBM_PEAK_GBS,
+        "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,
+        "matrices": nmat, "fp64_chain_matrices": n64, "nonfinite_matrices": nbad,
+        "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "mfma", "kernel": dom, "what": what, "dtype": dt_,
+                     "achieved": achieved, "peak": PEAK_TFLOPS[dt_], "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_TFLOPS[dt_],
+                     "flops_per_launch": flops / launches, "avg_launch_ms": phase_ms[dom] / launches,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,173 @@
+/*
+ * dion.h — C ABI of the MI355X (gfx950) Dion optimizer step.
+ *
+ * One call performs one Dion step on a stack of `batch` same-shape m x n
+ * matrices, entirely on the GPU:
+ *
+ *     B  = M + G                              (error-feedback buffer)
+ *     P0 = B Q                                (one warm-started power-iteration step)
+ *     P  = orth(P0)                           (Q-factor of the thin QR, diag > 0)
+ *     R  = B^T P
+ *     M <- B - (1 - mu) P R^T                 (error feedback into the momentum)
+ *     Q <- R / (||r_j||_2 + eps)              (column-normalized, next step's warm start)
+ *     X <- X - lr * sqrt(m / n) * P Q^T       (orthonormalized low-rank weight update)
+ *
+ * Passages defining the operation:
+ *   - "Dion e la fine del monopolio di Adam negli optimizer AI distribuiti"
+ *     (rivista.ai): only the first r singular directions are orthonormalized
+ *     (the paragraph that introduces rank as a new scaling dimension); the
+ *     full-versus-low-rank difference is kept and re-injected by error feedback
+ *     (the paragraph on FSDP traffic); amortized power iteration with QR and
+ *     Cholesky decompositions replaces Newton-Schulz, and only 2-D parameters
+ *     are routed to Dion, 1-D ones to AdamW or Lion (the paragraph beginning
+ *     "Tecnicamente"); the rank fraction is the cost/accuracy knob (the
+ *     paragraph on the "default" optimizer).
+ *   - "DASH: Faster Shampoo via Batched Block Preconditioning ..." (gist.science,
+ *     "Methodologie", 1. Batched Block Preconditioning): same-shape blocks are
+ *     stacked into one 3-D tensor and processed by one batched call.
+ *   Readings where the pages are silent: s = sqrt(m/n); eps is used only as
+ *   ||r_j|| + eps; "orth" is the unpivoted thin-QR Q-factor with a positive
+ *   diagonal, reached here by Cholesky-based QR (CholeskyQR2) with an fp64
+ *   fallback chain for ill-conditioned P0.
+ *
+ * Memory and ownership
+ *   Every buffer is device memory owned by the caller; the library allocates
+ *   nothing and keeps no state between calls.  Layouts are row-major and
+ *   contiguous: X, G, M as [batch][m][n]; Q as [batch][n][rank].
+ *   X, M and Q are updated in place; G is read only.  X and G are fp32 or
+ *   bf16 (independently); M and Q are fp32.  The workspace is scratch owned by
+ *   the caller, at least dion_workspace_size() bytes; after the call it begins
+ *   with P as fp32 [batch][m][rank] (the orthonormal factor of this step).
+ *   Pointers must be 16-byte aligned (256-byte for the workspace) and the
+ *   state buffers must not overlap each other or the workspace.
+ *
+ * Execution
+ *   Asynchronous: everything is enqueued on `stream` (a hipStream_t, NULL =
+ *   the default stream) and the call returns without a host synchronization.
+ *   Results are bitwise reproducible for the same inputs on the same device
+ *   (no floating-point atomics).  Calls that share a workspace must be
+ *   ordered on one stream.
+ *
+ * Errors
+ *   0 = success.  A negative status below -99 is a HIP launch error
+ *   (status = -100 - hipError_t).  Other negative statuses are argument errors
+ *   detected on the host before anything is enqueued; the state is then
+ *   untouched.  NaN / Inf inputs are not rejected: they propagate and are
+ *   reported in `flags`.
+ */
+#ifndef DION_MI355X_H
+#define DION_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage type of X and G */
+typedef enum { DION_F32 = 0, DION_BF16 = 1 } dion_dtype;
+
+/* status codes */
+enum {
+    DION_OK = 0,
+    DION_ERR_NULL = -1,       /* a required pointer is NULL */
+    DION_ERR_SHAPE = -2,      /* m < 1, n < 1, batch < 0, or a size overflows */
+    DION_ERR_RANK = -3,       /* rank outside [0, min(m, n)] */
+    DION_ERR_HYPER = -4,      /* mu outside [0, 1), lr not finite, eps < 0 or not finite */
+    DION_ERR_ALIGN = -5,      /* a pointer is not 16-byte (workspace: 256-byte) aligned */
+    DION_ERR_OVERLAP = -6,    /* two of X, G, M, Q, workspace, flags overlap */
+    DION_ERR_WORKSPACE = -7,  /* workspace smaller than dion_workspace_size() */
+    DION_ERR_DTYPE = -8,      /* x_dtype or g_dtype not a dion_dtype */
+    DION_ERR_OPTION = -9,     /* unknown option bit, or contradictory options */
+    DION_ERR_HIP = -100       /* -100 - hipError_t for a failed HIP call */
+};
+
+/* `options` bits */
+enum {
+    DION_OPT_STICKY_F64 = 1,  /* matrices whose flags word has DION_FLAG_F64 set on entry
+                                 skip the fp32 attempt and go straight to the fp64 chain */
+    DION_OPT_FORCE_F64 = 2,   /* every matrix uses the fp64 chain */
+    DION_OPT_FORCE_F32 = 4    /* never fall back; an fp32 breakdown is reported as
+                                 DION_FLAG_NONFINITE and its results are undefined */
+};
+
+/* per-matrix `flags` bits written by the step (device int32 [batch]) */
+enum {
+    DION_FLAG_F64 = 1,        /* this step's P and R came from the fp64 chain */
+    DION_FLAG_NONFINITE = 2,  /* a NaN/Inf was met, or the factorization broke down */
+    DION_FLAG_SHIFTED = 4     /* the fp64 chain needed the shifted first pass */
+};
+
+/* phases of one step, in launch order (for dion_step_batched_profiled) */
+enum {
+    DION_PHASE_INIT = 0,             /* per-matrix state words */
+    DION_PHASE_F32_PRODUCT = 1,      /* fp32 chain: P0 = (M + G) Q */
+    DION_PHASE_F32_QR = 2,           /* fp32 chain: CholeskyQR2 of P0 */
+    DION_PHASE_F32_BACKPROJECT = 3,  /* fp32 chain: R = (M + G)^T P */
+    DION_PHASE_F64_PRODUCT = 4,      /* fp64 chain: P0 = (M + G) Q */
+    DION_PHASE_F64_QR = 5,           /* fp64 chain: (shifted) CholeskyQR */
+    DION_PHASE_F64_BACKPROJECT = 6,  /* fp64 chain: R = (M + G)^T P */
+    DION_PHASE_NORMS = 7,            /* column norms, next Q, fp64 -> fp32 rounding */
+    DION_PHASE_UPDATE = 8,           /* M <- B - (1-mu) P R^T and X <- X - lr s P Q^T */
+    DION_PHASE_FLAGS = 9,            /* per-matrix flags */
+    DION_NUM_PHASES = 10
+};
+
+/*
+ * Bytes of device workspace one dion_step_batched call with these sizes needs.
+ * Pure host arithmetic (no HIP call).  Returns 0 for invalid sizes.
+ */
+size_t dion_workspace_size(int64_t m, int64_t n, int64_t batch, int64_t rank);
+
+/*
+ * One Dion step on a stack of `batch` matrices (see the top of this file).
+ *   X        device, [batch][m][n], x_dtype, updated in place
+ *   G        device, [batch][m][n], g_dtype, read only
+ *   M        device, [batch][m][n], fp32, updated in place (momentum / error feedback)
+ *   Q        device, [batch][n][rank], fp32, updated in place; may be NULL iff rank == 0
+ *   m, n     matrix shape (X is m x n); batch >= 0 (0 is a no-op)
+ *   rank     r in [0, min(m, n)]; r == 0 gives M <- M + G and leaves X, Q untouched
+ *   mu       momentum in [0, 1); lr finite; eps >= 0 (column-norm guard)
+ *   workspace, workspace_bytes   device scratch, >= dion_workspace_size(m, n, batch, rank)
+ *   flags    device int32 [batch] or NULL: per-matrix DION_FLAG_* bits on exit
+ *            (read on entry only with DION_OPT_STICKY_F64)
+ *   options  DION_OPT_* bits
+ *   stream   hipStream_t to enqueue on (NULL = default stream)
+ * Returns DION_OK or a negative status (see above).
+ */
+int dion_step_batched(void* X, const void* G, float* M, float* Q,
+                      int64_t m, int64_t n, int64_t batch, int64_t rank,
+                      float mu, float lr, float eps,
+                      int x_dtype, int g_dtype,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t* flags, uint32_t options, void* stream);
+
+/*
+ * dion_step_batched with phase markers, for profiling.  `events` holds
+ * DION_NUM_PHASES + 1 hipEvent_t handles created by the caller; events[i] is
+ * recorded on `stream` where phase i starts and events[DION_NUM_PHASES] after
+ * the last launch, so hipEventElapsedTime(events[i], events[i + 1]) is the
+ * device time of phase i.  The single-kernel phases (the four products, the
+ * update) time one kernel each.  A chain that does not run records its three
+ * events back to back.  No host synchronization; same results and status
+ * codes as dion_step_batched.  `events` may be NULL.
+ */
+int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q,
+                               int64_t m, int64_t n, int64_t batch, int64_t rank,
+                               float mu, float lr, float eps,
+                               int x_dtype, int g_dtype,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* flags, uint32_t options, void* stream,
+                               void* const* events);
+
+/* Static text for a status code (never NULL). */
+const char* dion_strerror(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int dion_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DION_MI355X_H */

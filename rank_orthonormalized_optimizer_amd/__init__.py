@@ -1,0 +1,18 @@
+"""MI355X-native Dion optimizer step: gfx950 HIP kernels behind a C ABI.
+
+Dion ("Dion: Distributed Orthonormalized Updates", reviewed on rivista.ai in
+"Dion e la fine del monopolio di Adam negli optimizer AI distribuiti")
+orthonormalizes only the top-r directions of each 2-D weight's update by one
+amortized power-iteration step with QR/Cholesky, and keeps the rest in an
+error-feedback momentum.  This package is the thin Python face of the C ABI:
+torch supplies device memory and the current stream, and every step of the
+computation runs in the library's kernels.  1-D parameters (biases, norms) are
+not Dion's: ``group_matrices`` rejects them so callers route them to AdamW or
+Lion, as the page describes.
+"""
+from __future__ import annotations
+
+from ._lib import (BF16, EXPORTS, F32, FLAG_F64, FLAG_NONFINITE, FLAG_SHIFTED,  # noqa: F401
+                   OPT_FORCE_F32, OPT_FORCE_F64, OPT_STICKY_F64, DionError, load,
+                   step_batched_raw, strerror, version, workspace_size)
+from .api import DionStack, group_matrices, step_  # noqa: F401

@@ -1,0 +1,116 @@
+"""torch-facing wrappers of dion_step_batched (marshalling only, no arithmetic)."""
+from __future__ import annotations
+
+from collections import OrderedDict
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _check(t: torch.Tensor, name: str, shape, dtypes) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def workspace_for(m: int, n: int, batch: int, rank: int, device) -> torch.Tensor:
+    """Device scratch for one call (allocated by torch; 256-byte aligned)."""
+    nbytes = _lib.workspace_size(m, n, batch, rank)
+    ws = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + max(nbytes, 256)]
+
+
+def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | None, rank: int,
+          mu: float, lr: float, eps: float = 1e-8, *, workspace: torch.Tensor | None = None,
+          flags: torch.Tensor | None = None, options: int = 0, stream=None, events=None) -> None:
+    """One Dion step on a stack, in place on X, M and Q.
+
+    X, G: [b, m, n] float32 or bfloat16; M: [b, m, n] float32; Q: [b, n, rank] float32.
+    ``flags`` (int32 [b], optional) receives the per-matrix FLAG_* bits.
+    Enqueued on ``stream`` (default: torch's current stream) with no host sync.
+    ``events``: optional NUM_PHASES + 1 recorded torch.cuda.Event objects, re-recorded at the
+    phase boundaries of the step (profiling).
+    """
+    if X.dim() != 3:
+        raise ValueError("X must be a stack [batch, m, n]; route 1-D parameters to AdamW or Lion")
+    b, m, n = X.shape
+    _check(X, "X", (b, m, n), tuple(_DT))
+    _check(G, "G", (b, m, n), tuple(_DT))
+    _check(M, "M", (b, m, n), (torch.float32,))
+    if rank > 0:
+        _check(Q, "Q", (b, n, rank), (torch.float32,))
+    if flags is not None:
+        _check(flags, "flags", (b,), (torch.int32,))
+    if workspace is None:
+        workspace = workspace_for(m, n, b, rank, X.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = _lib.step_batched_raw(X.data_ptr(), G.data_ptr(), M.data_ptr(), Q.data_ptr() if rank > 0 else 0,
+                               m, n, b, rank, float(mu), float(lr), float(eps), _DT[X.dtype], _DT[G.dtype],
+                               workspace.data_ptr(), workspace.numel(),
+                               flags.data_ptr() if flags is not None else 0, int(options),
+                               int(stream.cuda_stream),
+                               None if events is None else [e.cuda_event for e in events])
+    if st != _lib.OK:
+        raise _lib.DionError(st)
+
+
+class DionStack:
+    """Optimizer state (M, Q, flags, workspace) of one stack of same-shape matrices.
+
+    ``rank_fraction`` picks r = floor(fraction * min(m, n)) (the rank-fraction
+    knob of the rivista.ai Dion page) unless ``rank`` is given.  The fp64
+    fallback is sticky by default: a matrix that needed it keeps it.
+    """
+
+    def __init__(self, batch: int, m: int, n: int, *, rank: int | None = None, rank_fraction: float = 0.25,
+                 mu: float = 0.95, lr: float = 0.01, eps: float = 1e-8, device="cuda", sticky: bool = True,
+                 seed: int = 0):
+        self.batch, self.m, self.n = batch, m, n
+        self.rank = int(rank if rank is not None else int(rank_fraction * min(m, n)))
+        self.mu, self.lr, self.eps = mu, lr, eps
+        self.options = _lib.OPT_STICKY_F64 if sticky else 0
+        dev = torch.device(device)
+        self.M = torch.zeros(batch, m, n, dtype=torch.float32, device=dev)
+        gen = torch.Generator(device="cpu").manual_seed(seed)
+        q = torch.randn(batch, n, self.rank, generator=gen, dtype=torch.float64)
+        if self.rank:
+            q /= q.norm(dim=1, keepdim=True)
+        self.Q = q.to(torch.float32).to(dev).contiguous()
+        self.flags = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.workspace = workspace_for(m, n, batch, self.rank, dev)
+
+    def step(self, X: torch.Tensor, G: torch.Tensor) -> None:
+        step_(X, G, self.M, self.Q, self.rank, self.mu, self.lr, self.eps, workspace=self.workspace,
+              flags=self.flags, options=self.options)
+
+    @property
+    def P(self) -> torch.Tensor:
+        """This step's orthonormal factor P [b, m, r] (fp32), read from the workspace."""
+        n = self.batch * self.m * self.rank
+        return self.workspace[:4 * n].view(torch.float32).view(self.batch, self.m, self.rank)
+
+
+def group_matrices(params) -> "OrderedDict[tuple, list]":
+    """Group 2-D tensors by (shape, dtype) into stackable lists; reject anything else.
+
+    Dion updates 2-D weight matrices only; biases and other 1-D tensors go to
+    AdamW or Lion, so they raise here instead of being silently skipped.
+    """
+    groups: "OrderedDict[tuple, list]" = OrderedDict()
+    for i, p in enumerate(params):
+        if p.dim() != 2:
+            raise ValueError(f"parameter {i} has shape {tuple(p.shape)}: only 2-D matrices go to Dion")
+        groups.setdefault((tuple(p.shape), p.dtype), []).append(p)
+    return groups

@@ -1,0 +1,100 @@
+// extern "C" entry points of the Dion step library: argument validation (pure
+// host code, no HIP call before every check has passed), workspace sizing,
+// status strings.  The launch sequence itself lives in dion_step.hip.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "dion.h"
+#include "dion_plan.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+Range span(const void* p, double bytes) {
+    const uintptr_t lo = (uintptr_t)p;
+    return Range{lo, lo + (uintptr_t)bytes};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dion_workspace_size(int64_t m, int64_t n, int64_t batch, int64_t rank) {
+    dion::Plan p;
+    if (!dion::make_plan(m, n, batch, rank, &p)) return 0;
+    return p.total;
+}
+
+int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch,
+                               int64_t rank, float mu, float lr, float eps, int x_dtype, int g_dtype,
+                               void* workspace, size_t workspace_bytes, int32_t* flags, uint32_t options,
+                               void* stream, void* const* events) {
+    if (m < 1 || n < 1 || batch < 0) return DION_ERR_SHAPE;
+    if (rank < 0 || rank > (m < n ? m : n)) return DION_ERR_RANK;
+    if (!(mu >= 0.0f && mu < 1.0f) || !isfinite(lr) || !isfinite(eps) || !(eps >= 0.0f)) return DION_ERR_HYPER;
+    if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
+        return DION_ERR_DTYPE;
+    const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32;
+    if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)))
+        return DION_ERR_OPTION;
+    dion::Plan p;
+    if (!dion::make_plan(m, n, batch, rank, &p)) return DION_ERR_SHAPE;
+    if (batch == 0) return DION_OK;
+    if (!X || !G || !M || (rank > 0 && !Q) || !workspace) return DION_ERR_NULL;
+    if (((uintptr_t)X | (uintptr_t)G | (uintptr_t)M | (uintptr_t)Q | (uintptr_t)flags) & 15u) return DION_ERR_ALIGN;
+    if ((uintptr_t)workspace & 255u) return DION_ERR_ALIGN;
+    if (workspace_bytes < p.total) return DION_ERR_WORKSPACE;
+    const double mn = (double)batch * (double)m * (double)n;
+    const Range rs[6] = {
+        span(X, mn * (x_dtype == DION_BF16 ? 2 : 4)),
+        span(G, mn * (g_dtype == DION_BF16 ? 2 : 4)),
+        span(M, mn * 4),
+        span(Q, rank > 0 ? (double)batch * (double)n * (double)rank * 4 : 0.0),
+        span(workspace, (double)p.total),
+        span(flags, flags ? (double)batch * 4 : 0.0),
+    };
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    const int e = dion::run_step(p, X, G, M, Q, mu, lr, eps, x_dtype == DION_BF16, g_dtype == DION_BF16,
+                                 (char*)workspace, flags, options, stream, events);
+    return e ? DION_ERR_HIP - e : DION_OK;
+}
+
+int dion_step_batched(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch, int64_t rank,
+                      float mu, float lr, float eps, int x_dtype, int g_dtype, void* workspace,
+                      size_t workspace_bytes, int32_t* flags, uint32_t options, void* stream) {
+    return dion_step_batched_profiled(X, G, M, Q, m, n, batch, rank, mu, lr, eps, x_dtype, g_dtype, workspace,
+                                      workspace_bytes, flags, options, stream, nullptr);
+}
+
+const char* dion_strerror(int status) {
+    switch (status) {
+        case DION_OK: return "success";
+        case DION_ERR_NULL: return "a required pointer is NULL";
+        case DION_ERR_SHAPE: return "invalid shape (m, n >= 1, batch >= 0) or size overflow";
+        case DION_ERR_RANK: return "rank outside [0, min(m, n)]";
+        case DION_ERR_HYPER: return "invalid hyper-parameter (mu in [0,1), finite lr, finite eps >= 0)";
+        case DION_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
+        case DION_ERR_OVERLAP: return "overlapping buffers";
+        case DION_ERR_WORKSPACE: return "workspace smaller than dion_workspace_size()";
+        case DION_ERR_DTYPE: return "unsupported dtype (DION_F32 or DION_BF16)";
+        case DION_ERR_OPTION: return "unknown or contradictory option bits";
+        default: break;
+    }
+    if (status <= DION_ERR_HIP) return "HIP runtime error (status = -100 - hipError_t)";
+    return "unknown status";
+}
+
+int dion_version(void) { return 100; }
+
+}  // extern "C"

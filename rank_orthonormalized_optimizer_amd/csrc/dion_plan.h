@@ -1,0 +1,69 @@
+// Workspace planner and internal launch interface of the Dion step.
+// Pure host code: the sizes and offsets below are computed without any HIP call.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dion {
+
+// Block size of the blocked Cholesky / triangular solves (rank is cut into
+// column blocks of this width; the last one may be narrower).
+constexpr int kNB = 64;
+// Row chunk of the column-norm partial sums.
+constexpr int kNormChunk = 256;
+
+// Per-matrix state word kept in the workspace during a call.
+enum : int {
+    ST_PATH64 = 1,   // the fp64 chain owns this matrix
+    ST_SHIFT = 2,    // the fp64 chain needs the shifted first pass (and a third pass)
+    ST_FAIL = 4,     // a factorization broke down with no further fallback
+};
+
+struct Plan {
+    int64_t m, n, b, r;
+    int64_t nblk;      // number of rank column blocks
+    int64_t nchunk;    // row chunks of the column-norm reduction
+    // byte offsets into the workspace (all 256-byte aligned)
+    size_t P32, R32, cs, st, kap, W, L, Td, Tf, P64, P64b, R64, part;
+    size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Returns false when the sizes overflow or are invalid.
+inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
+    if (m < 1 || n < 1 || b < 0 || r < 0 || r > (m < n ? m : n)) return false;
+    const int64_t lim = (int64_t)1 << 40;
+    if (m > lim || n > lim || b > lim || (double)m * (double)n * (double)(b ? b : 1) > 9.0e15) return false;
+    Plan q{};
+    q.m = m; q.n = n; q.b = b; q.r = r;
+    q.nblk = (r + kNB - 1) / kNB;
+    q.nchunk = (n + kNormChunk - 1) / kNormChunk;
+    size_t off = 0;
+    auto take = [&](double bytes) { size_t o = off; off = align256(off + (size_t)bytes); return o; };
+    const double B = (double)b;
+    q.P32 = take(B * m * r * 4);           // fp32 P (fp32 chain works in place here)
+    q.R32 = take(B * n * r * 4);           // fp32 R
+    q.cs = take(B * r * 8);                // 1 / (||r_j|| + eps), fp64
+    q.st = take(B * 4);                    // state words
+    q.kap = take(B * 2 * 8);               // running min / max Cholesky diagonal
+    q.W = take(B * r * r * 8);             // Gram matrix (fp32 or fp64)
+    q.L = take(B * r * r * 8);             // Cholesky factor, in place
+    q.Td = take(B * q.nblk * kNB * kNB * 8);   // inverses of the diagonal blocks
+    q.Tf = take(B * r * r * 8);            // full inverse L^-1 (lower)
+    q.P64 = take(B * m * r * 8);           // fp64 chain P
+    q.P64b = take(B * m * r * 8);          // second P buffer (fp64 chain; fp32 chain's scratch)
+    q.R64 = take(B * n * r * 8);           // fp64 chain R
+    q.part = take(B * q.nchunk * r * 8);   // column-norm partial sums (fp64)
+    q.total = off;
+    if (q.total > ((size_t)1 << 46)) return false;
+    *p = q;
+    return true;
+}
+
+// Run the step (arguments already validated).  Returns a hipError_t value.
+int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
+             float mu, float lr, float eps, int x_bf16, int g_bf16,
+             char* ws, int32_t* flags, uint32_t options, void* stream, void* const* events);
+
+}  // namespace dion

@@ -1,0 +1,891 @@
+// Kernels and launch sequence of the Dion step on gfx950.
+//
+// Per matrix of the stack (shapes m x n, rank r), the step is
+//   B = M + G;  P0 = B Q;  P = orth(P0);  R = B^T P;
+//   M <- B - (1 - mu) P R^T;  Q <- R / (||r_j|| + eps);  X <- X - lr sqrt(m/n) P Q^T
+// ("Dion e la fine del monopolio di Adam negli optimizer AI distribuiti",
+// rivista.ai: low-rank orthonormalized update with error feedback, amortized
+// power iteration with QR and Cholesky).
+//
+// orth() is CholeskyQR2: W = P0^T P0, L = chol(W), P1 = P0 L^-T, repeated once.
+// In exact arithmetic it gives the same Q-factor (positive diagonal) as a
+// Householder QR.  Two precision chains share the kernels:
+//   fp32 chain  B rounded once to fp32, fp32 MFMA everywhere.  If a Cholesky
+//               pivot fails or the diagonal ratio max(L_ii)/min(L_ii) of the
+//               first pass exceeds kTau32, the matrix is handed to
+//   fp64 chain  B = M + G exact in fp64, P0, the QR and R in fp64 MFMA.  If its
+//               first Cholesky fails or its diagonal ratio exceeds kTau64, the
+//               first pass is redone on W + s I (shifted CholeskyQR, Fukaya,
+//               Kannan, Nakatsukasa, Yamamoto and Yanagisawa, SIAM J. Sci.
+//               Comput. 2020) followed by two plain passes.
+// The hand-over is a per-matrix state word in device memory: every kernel of a
+// chain tests it and returns at once for matrices it does not own, so the host
+// never synchronizes.  The momentum/weight pass then runs once for all
+// matrices in fp32 from P and R rounded to fp32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "dion.h"
+#include "dion_plan.h"
+#include "gemm_mfma.hpp"
+
+namespace dion {
+
+// Diagonal-ratio thresholds of the first Cholesky pass (see the header comment).
+constexpr double kTau32 = 64.0;
+constexpr double kTau64 = 1.0e7;
+
+// ---------------------------------------------------------------------------
+// generic batched GEMM:  C = alpha * A B + beta * C
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+    Operand a, b;              // per-matrix views (batch 0)
+    int64_t sa0, sa1, sb0;     // batch strides in bytes of a.p0, a.p1, b.p0
+    void* c;
+    int64_t ldc, sc;           // ldc in elements, sc in bytes
+    int M, N, K;
+    double alpha, beta;
+    const int* st;             // per-matrix state word; matrix runs iff (st & mask) == val
+    int st_mask, st_val;
+    int lower;                 // skip tiles strictly above the diagonal
+    int zdiv;                  // blockIdx.z = matrix * zdiv + group (0 or 1: no groups)
+    int64_t ga0, gb0, gc;      // byte offsets between groups for a.p0, b.p0, c
+    int kskip;                 // K range of a tile: 0 all; 1 k < n0 + BN (B = lower^T);
+                               // 2 k >= n0 (B lower); 3 k < m0 + BM (A lower)
+};
+
+template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+    using C = TileCfg<T, BM, BN>;
+    const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
+    const int bz = blockIdx.z / zdiv, grp = blockIdx.z % zdiv;
+    if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    if (g.lower && n0 >= m0 + BM) return;
+    int kbeg = 0, kend = g.K;
+    if (g.kskip == 1) kend = min(g.K, n0 + BN);
+    else if (g.kskip == 2) kbeg = (n0 / C::BK) * C::BK;
+    else if (g.kskip == 3) kend = min(g.K, m0 + BM);
+
+    __shared__ T As[C::BK * C::LDA];
+    __shared__ T Bs[C::BK * C::LDB];
+
+    Operand A = g.a, B = g.b;
+    A.p0 = (const char*)A.p0 + bz * g.sa0 + grp * g.ga0;
+    if (A.p1) A.p1 = (const char*)A.p1 + bz * g.sa1;
+    B.p0 = (const char*)B.p0 + bz * g.sb0 + grp * g.gb0;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    typename C::acc_t acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{0, 0, 0, 0};
+
+    TileLoader<T, BM, C::BK, AKC, ASRC> la;
+    TileLoader<T, BN, C::BK, BKC, BSRC> lb;
+    if (kbeg < kend) { la.load(A, m0, kbeg); lb.load(B, n0, kbeg); }
+    for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
+        la.template store<C::LDA>(As);
+        lb.template store<C::LDB>(Bs);
+        __syncthreads();
+        if (k0 + C::BK < kend) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
+        mma_slab<T, C>(As, Bs, acc, wm, wn, lane);
+        __syncthreads();
+    }
+
+    T* Cp = (T*)((char*)g.c + bz * g.sc + grp * g.gc);
+    const T alpha = (T)g.alpha, beta = (T)g.beta;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm * C::WTM + i * 16 + Mfma<T>::row(lane, v);
+                const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
+                if (row < g.M && col < g.N) {
+                    T* cp = Cp + (int64_t)row * g.ldc + col;
+                    T val = alpha * acc[i][j][v];
+                    if (beta != T(0)) val += beta * *cp;
+                    *cp = val;
+                }
+            }
+}
+
+template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
+static hipError_t launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+    const int64_t zdiv = g.zdiv > 1 ? g.zdiv : 1;
+    dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, (unsigned)(batch * zdiv));
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AKC, ASRC, BKC, BSRC>), grid, dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// diagonal block of the blocked Cholesky: factor, track the diagonal ratio,
+// and invert the factor (both kept in LDS)
+// ---------------------------------------------------------------------------
+struct PotrfArgs {
+    void* L; int64_t ldl, sL;   // factor in place (elements)
+    void* Td; int64_t sTd;      // [nblk][kNB][kNB] inverses of the diagonal blocks
+    int j0, nbj, jblk;
+    int* st; int st_mask, st_val;
+    double* kap;                // [batch][2] running min / max of diag(L)
+    int first, last;
+    double tau;                 // diagonal-ratio limit tested on the last block (<= 0: off)
+    int fail_bit, tau_bit;
+};
+
+// One column step of the diagonal-block factorization (see potrf_diag_kernel), with the column
+// index K a compile-time constant so every register slot below is static.
+template <typename T>
+struct DiagCtx {
+    T a[kNB / 4], x[kNB / 4];
+    T (*col)[kNB];
+    T (*xrow)[kNB];
+    T* piv;
+    T* dg;
+    T* Lrow;
+    int i, part, nbj, tid;
+    bool row_ok, ok;
+};
+
+template <typename T, int K>
+__device__ __forceinline__ void diag_step(DiagCtx<T>& c) {
+    constexpr int NS = kNB / 4, b = K & 1, sk = K >> 2, q = K & 3;
+    const bool own = c.part == q;
+    if (own) {
+        c.col[b][c.i] = (c.row_ok && c.i > K) ? c.a[sk] : T(0);
+        if (c.i == K) c.piv[b] = c.a[sk];
+    }
+    if (c.i == K) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) c.xrow[b][4 * s + c.part] = c.x[s];
+    }
+    __syncthreads();
+    const T d = c.piv[b];
+    const T ci = c.col[b][c.i];
+    T cj[NS], xk[NS];
+#pragma unroll
+    for (int s = sk; s < NS; ++s) cj[s] = c.col[b][4 * s + c.part];
+#pragma unroll
+    for (int s = 0; s <= sk; ++s) xk[s] = c.xrow[b][4 * s + c.part];
+    if (!(d > T(0)) || !isfinite(d)) { c.ok = false; return; }   // same value in every thread
+    const T lkk = sqrt(d), inv = T(1) / lkk;
+    const T lik = ci * inv;            // zero unless i > K
+    const T coef = lik * inv;
+#pragma unroll
+    for (int s = sk; s < NS; ++s) c.a[s] -= coef * cj[s];
+#pragma unroll
+    for (int s = 0; s <= sk; ++s) c.x[s] -= coef * xk[s];
+    if (own && c.row_ok && c.i >= K) c.Lrow[K] = (c.i == K) ? lkk : lik;
+    if (c.tid == 0) c.dg[K] = lkk;
+}
+
+template <typename T, int K>
+struct DiagSteps {
+    static __device__ __forceinline__ void run(DiagCtx<T>& c) {
+        if constexpr (K < kNB) {
+            if (c.ok && K < c.nbj) {
+                diag_step<T, K>(c);
+                DiagSteps<T, K + 1>::run(c);
+            }
+        }
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
+    // One fused right-looking sweep over the columns k of the block:
+    //   Cholesky   l_ik = a_ik / l_kk,  a_ij -= l_ik l_jk      (k < j <= i)
+    //   inverse    x_i  -= l_ik (x_k / l_kk)                   (rows of X = L^-1, columns c <= k)
+    // Thread t owns row i = t / 4 and, in registers, the 16 columns j = 4 s + t % 4 of that row of
+    // the working matrix and of X.  Per column, the raw column k (zero at rows <= k), the pivot and
+    // row k of X (zero right of the diagonal) travel through double-buffered LDS, so the updates
+    // need no predicates and one barrier per column suffices.  L_ik goes straight to global memory.
+    constexpr int NB = kNB, NS = NB / 4;
+    static_assert(NB * 4 == 256, "one row per four threads");
+    const int bz = blockIdx.x;
+    if ((p.st[bz] & p.st_mask) != p.st_val) return;
+    __shared__ T col[2][NB];
+    __shared__ T xrow[2][NB];
+    __shared__ T piv[2];
+    __shared__ T dg[NB];
+    T* L = (T*)p.L + bz * p.sL;
+    DiagCtx<T> c;
+    c.col = col; c.xrow = xrow; c.piv = piv; c.dg = dg;
+    c.nbj = p.nbj; c.tid = threadIdx.x;
+    c.i = c.tid >> 2; c.part = c.tid & 3;
+    c.row_ok = c.i < c.nbj;
+    c.ok = true;
+    c.Lrow = L + (int64_t)(p.j0 + (c.row_ok ? c.i : 0)) * p.ldl + p.j0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int j = 4 * s + c.part;
+        c.a[s] = (c.row_ok && j <= c.i) ? c.Lrow[j] : T(0);
+        c.x[s] = (j == c.i) ? T(1) : T(0);
+    }
+    DiagSteps<T, 0>::run(c);
+    const int tid = c.tid, i = c.i, part = c.part, nbj = c.nbj;
+    if (!c.ok) {
+        if (tid == 0) p.st[bz] |= p.fail_bit;
+        return;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double mn = (double)dg[0], mx = (double)dg[0];
+        for (int q = 1; q < nbj; ++q) {
+            const double d = (double)dg[q];
+            mn = d < mn ? d : mn;
+            mx = d > mx ? d : mx;
+        }
+        double* kp = p.kap + 2 * bz;
+        if (!p.first) { mn = kp[0] < mn ? kp[0] : mn; mx = kp[1] > mx ? kp[1] : mx; }
+        kp[0] = mn; kp[1] = mx;
+        if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
+    }
+    T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * NB * NB;
+    const T rinv = c.row_ok ? T(1) / dg[i] : T(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int j = 4 * s + part;
+        Td[i * NB + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
+    }
+}
+
+// L = W (+ s I), s = c_shift * trace(W) when shifting.
+template <typename T>
+__global__ __launch_bounds__(256) void copy_shift_kernel(const T* W, T* L, int64_t r, const int* st, int st_mask,
+                                                         int st_val, int shift, double c_shift) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    W += bz * r * r;
+    L += bz * r * r;
+    T sv = 0;
+    if (shift) {
+        __shared__ double red[256];
+        double tr = 0;
+        for (int64_t i = threadIdx.x; i < r; i += 256) tr += (double)W[i * r + i];
+        red[threadIdx.x] = tr;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+            __syncthreads();
+        }
+        sv = (T)(c_shift * red[0]);
+    }
+    const int64_t total = r * r;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t i = idx / r, k = idx % r;
+        L[idx] = W[idx] + ((i == k) ? sv : T(0));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// column norms of R, the next Q, and rounding of the fp64 chain to fp32
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void colnorm_partial_kernel(const float* R32, const double* R64, double* part,
+                                                              int64_t n, int64_t r, int nchunk, const int* st) {
+    const int bz = blockIdx.z, chunk = blockIdx.y;
+    const bool p64 = (st[bz] & ST_PATH64) != 0;
+    const int64_t col = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const int rg = threadIdx.x >> 6;
+    const int64_t row0 = (int64_t)chunk * kNormChunk, row1 = row0 + kNormChunk < n ? row0 + kNormChunk : n;
+    double s = 0;
+    if (col < r) {
+        if (p64) {
+            const double* R = R64 + bz * n * r;
+            for (int64_t i = row0 + rg; i < row1; i += 4) { const double v = R[i * r + col]; s += v * v; }
+        } else {
+            const float* R = R32 + bz * n * r;
+            for (int64_t i = row0 + rg; i < row1; i += 4) { const double v = (double)R[i * r + col]; s += v * v; }
+        }
+    }
+    __shared__ double red[256];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    if (rg == 0 && col < r) {
+        const double t = ((red[threadIdx.x] + red[threadIdx.x + 64]) + red[threadIdx.x + 128]) + red[threadIdx.x + 192];
+        part[((int64_t)bz * nchunk + chunk) * r + col] = t;
+    }
+}
+
+__global__ __launch_bounds__(256) void colscale_kernel(const double* part, double* cs, int64_t r, int nchunk,
+                                                       double eps) {
+    const int bz = blockIdx.y;
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= r) return;
+    double s = 0;
+    for (int c = 0; c < nchunk; ++c) s += part[((int64_t)bz * nchunk + c) * r + col];
+    cs[bz * r + col] = 1.0 / (sqrt(s) + eps);
+}
+
+// Q <- R * c (fp32), and for fp64-chain matrices R32 <- R64 rounded.
+__global__ __launch_bounds__(256) void next_q_kernel(const double* R64, float* R32, const double* cs, float* Q,
+                                                     int64_t n, int64_t r, const int* st) {
+    const int bz = blockIdx.y;
+    const bool p64 = (st[bz] & ST_PATH64) != 0;
+    const int64_t total = n * r;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t k = idx % r;
+        const double c = cs[bz * r + k];
+        double v;
+        if (p64) {
+            v = R64[bz * total + idx];
+            R32[bz * total + idx] = (float)v;
+        } else {
+            v = (double)R32[bz * total + idx];
+        }
+        Q[bz * total + idx] = (float)(v * c);
+    }
+}
+
+__global__ __launch_bounds__(256) void round_p_kernel(const double* P64, float* P32, int64_t total, const int* st) {
+    const int bz = blockIdx.y;
+    if (!(st[bz] & ST_PATH64)) return;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256)
+        P32[bz * total + idx] = (float)P64[bz * total + idx];
+}
+
+// ---------------------------------------------------------------------------
+// momentum / weight pass:  M <- (M + G) - (1 - mu) P R^T,  X <- X - lr s P diag(c) R^T
+// ---------------------------------------------------------------------------
+struct UpdArgs {
+    const float* P; const float* R; const double* cs;
+    float* M; const void* G; void* X;
+    int m, n, r;
+    float one_minus_mu, lr_s;
+    int vec;   // r % 4 == 0
+};
+
+template <int BM, int BN, bool G_BF16, bool X_BF16>
+__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
+    using C = TileCfg<float, BM, BN>;
+    const int bz = blockIdx.z;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    __shared__ float As[C::BK * C::LDA];
+    __shared__ float Bs[C::BK * C::LDB];
+    __shared__ float Cs[C::BK];
+    const int64_t mr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r, mn = (int64_t)u.m * u.n;
+    Operand A{u.P + bz * mr, nullptr, u.r, u.m, u.r, u.vec != 0};
+    Operand B{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec != 0};
+    const double* cs = u.cs + (int64_t)bz * u.r;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    typename C::acc_t acc1[C::FM][C::FN], acc2[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
+
+    TileLoader<float, BM, C::BK, true, SRC_F32> la;
+    TileLoader<float, BN, C::BK, true, SRC_F32> lb;
+    la.load(A, m0, 0);
+    lb.load(B, n0, 0);
+    for (int k0 = 0; k0 < u.r; k0 += C::BK) {
+        la.template store<C::LDA>(As);
+        lb.template store<C::LDB>(Bs);
+        if (threadIdx.x < C::BK) Cs[threadIdx.x] = (k0 + (int)threadIdx.x < u.r) ? (float)cs[k0 + threadIdx.x] : 0.f;
+        __syncthreads();
+        if (k0 + C::BK < u.r) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
+#pragma unroll
+        for (int kk = 0; kk < C::BK; kk += 4) {
+            float a[C::FM], a2[C::FM], b[C::FN];
+            const float ck = Cs[kk + lk];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) {
+                a[i] = As[(kk + lk) * C::LDA + wm * C::WTM + i * 16 + lr];
+                a2[i] = a[i] * ck;
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) b[j] = Bs[(kk + lk) * C::LDB + wn * C::WTN + j * 16 + lr];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    acc1[i][j] = Mfma<float>::mma(a[i], b[j], acc1[i][j]);
+                    acc2[i][j] = Mfma<float>::mma(a2[i], b[j], acc2[i][j]);
+                }
+        }
+        __syncthreads();
+    }
+
+    float* Mp = u.M + bz * mn;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm * C::WTM + i * 16 + Mfma<float>::row(lane, v);
+                const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
+                if (row < u.m && col < u.n) {
+                    const int64_t off = bz * mn + (int64_t)row * u.n + col;
+                    float g;
+                    if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
+                    else g = ((const float*)u.G)[off];
+                    const float bv = Mp[off - bz * mn] + g;
+                    Mp[off - bz * mn] = bv - u.one_minus_mu * acc1[i][j][v];
+                    if constexpr (X_BF16) {
+                        uint16_t* X = (uint16_t*)u.X;
+                        const float xv = bf16_bits_to_float(X[off]);
+                        X[off] = float_to_bf16_bits(xv - u.lr_s * acc2[i][j][v]);
+                    } else {
+                        float* X = (float*)u.X;
+                        X[off] = X[off] - u.lr_s * acc2[i][j][v];
+                    }
+                }
+            }
+}
+
+// rank 0: M <- M + G
+template <bool G_BF16>
+__global__ __launch_bounds__(256) void add_grad_kernel(float* M, const void* G, int64_t total) {
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        float g;
+        if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)G)[idx]);
+        else g = ((const float*)G)[idx];
+        M[idx] += g;
+    }
+}
+
+__global__ void zero_flags_kernel(int32_t* flags, int64_t b) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < b) flags[i] = 0;
+}
+
+__global__ void init_state_kernel(int* st, const int32_t* flags, int64_t b, int force64, int sticky) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= b) return;
+    const bool f64 = force64 || (sticky && flags && (flags[i] & DION_FLAG_F64));
+    st[i] = f64 ? ST_PATH64 : 0;
+}
+
+__global__ __launch_bounds__(256) void flags_out_kernel(const int* st, const double* cs, int64_t r,
+                                                        int32_t* flags) {
+    const int bz = blockIdx.x;
+    __shared__ int bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int64_t k = threadIdx.x; k < r; k += 256) mine |= !isfinite(cs[bz * r + k]);
+    if (mine) bad = 1;   // benign same-value race
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int s = st[bz];
+        int f = 0;
+        if (s & ST_PATH64) f |= DION_FLAG_F64;
+        if (s & ST_SHIFT) f |= DION_FLAG_SHIFTED;
+        if ((s & ST_FAIL) || bad) f |= DION_FLAG_NONFINITE;
+        flags[bz] = f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+#define DION_TRY(expr)                              \
+    do {                                            \
+        hipError_t e_ = (expr);                     \
+        if (e_ != hipSuccess) return (int)e_;       \
+    } while (0)
+
+static bool aligned4(const void* p, int esz) { return ((uintptr_t)p % (uintptr_t)(4 * esz)) == 0; }
+
+static unsigned grid_1d(int64_t total, int64_t cap = 2048) {
+    int64_t g = (total + 255) / 256;
+    if (g < 1) g = 1;
+    return (unsigned)(g < cap ? g : cap);
+}
+
+template <typename T> struct SrcOf;
+template <> struct SrcOf<float> { static constexpr int v = SRC_F32; };
+template <> struct SrcOf<double> { static constexpr int v = SRC_F64; };
+
+struct ChainCtx {
+    const Plan* p;
+    char* ws;
+    int* st;
+    hipStream_t s;
+};
+
+// CholeskyQR building blocks on P [b][m][r], for the matrices with (st & mask) == val.
+// gram:    W = P^T P (lower tiles)
+// factor:  L = chol(W (+ s I)) by blocks of kNB columns (right-looking), with the inverse
+//          of every diagonal block kept in Td; a failed pivot sets `fail_bit`, a diagonal
+//          ratio above `tau` (tau > 0) sets `tau_bit`
+// invert:  Tf = L^-1;   apply: Pout = Pin Tf^T
+template <typename T>
+static int gram(const ChainCtx& c, const T* P, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r;
+    constexpr int S = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    GemmArgs g{};
+    g.a = Operand{P, nullptr, r, (int)r, (int)m, vr};   // A(i,k) = P[k][i]
+    g.b = Operand{P, nullptr, r, (int)r, (int)m, vr};   // B(k,j) = P[k][j]
+    g.sa0 = g.sb0 = m * r * (int64_t)sizeof(T);
+    g.c = c.ws + p.W; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
+    g.M = g.N = (int)r; g.K = (int)m;
+    g.alpha = 1; g.beta = 0;
+    g.st = c.st; g.st_mask = mask; g.st_val = val; g.lower = 1;
+    DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
+    return 0;
+}
+
+template <typename T>
+static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r, b = p.b;
+    T* W = (T*)(c.ws + p.W);
+    T* L = (T*)(c.ws + p.L);
+    T* Td = (T*)(c.ws + p.Td);
+    double* kap = (double*)(c.ws + p.kap);
+    constexpr int S = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    {
+        const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
+        const double c_shift = 11.0 * ((double)m * r + (double)r * (r + 1)) * u;
+        dim3 grid(grid_1d(r * r, 1024), (unsigned)b);
+        hipLaunchKernelGGL((copy_shift_kernel<T>), grid, dim3(256), 0, c.s, W, L, r, c.st, mask, val, shift, c_shift);
+        DION_TRY(hipGetLastError());
+    }
+    for (int64_t jb = 0; jb < p.nblk; ++jb) {
+        const int j0 = (int)(jb * kNB);
+        const int nbj = (int)((r - j0) < kNB ? (r - j0) : kNB);
+        const int rest = (int)(r - j0 - nbj);
+        PotrfArgs pa{};
+        pa.L = L; pa.ldl = r; pa.sL = r * r;
+        pa.Td = Td; pa.sTd = p.nblk * kNB * kNB;
+        pa.j0 = j0; pa.nbj = nbj; pa.jblk = (int)jb;
+        pa.st = c.st; pa.st_mask = mask; pa.st_val = val;
+        pa.kap = kap; pa.first = jb == 0; pa.last = jb == p.nblk - 1;
+        pa.tau = tau; pa.fail_bit = fail_bit; pa.tau_bit = tau_bit;
+        hipLaunchKernelGGL((potrf_diag_kernel<T>), dim3((unsigned)b), dim3(256), 0, c.s, pa);
+        DION_TRY(hipGetLastError());
+        if (rest > 0) {
+            T* below = L + (int64_t)(j0 + nbj) * r + j0;
+            // panel: L21 <- L21 Td^T (in place; one column tile covers all nbj columns)
+            GemmArgs g{};
+            g.a = Operand{below, nullptr, r, rest, nbj, vr};
+            g.b = Operand{Td + jb * kNB * kNB, nullptr, kNB, nbj, nbj, true};
+            g.sa0 = r * r * (int64_t)sizeof(T);
+            g.sb0 = p.nblk * kNB * kNB * (int64_t)sizeof(T);
+            g.c = below; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
+            g.M = rest; g.N = nbj; g.K = nbj;
+            g.alpha = 1; g.beta = 0;
+            g.st = c.st; g.st_mask = mask; g.st_val = val;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+            // trailing: L22 <- L22 - L21 L21^T (lower tiles only)
+            GemmArgs h = g;
+            h.b = Operand{below, nullptr, r, rest, nbj, vr};
+            h.sb0 = r * r * (int64_t)sizeof(T);
+            h.c = L + (int64_t)(j0 + nbj) * r + (j0 + nbj);
+            h.M = rest; h.N = rest; h.K = nbj;
+            h.alpha = -1; h.beta = 1; h.lower = 1;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(h, b, c.s)));
+        }
+    }
+    return 0;
+}
+
+// Tf = L^-1 (lower, [b][r][r]) from the factor L and the inverted diagonal blocks Td, by
+// recursive doubling over the blocks: for neighbouring block ranges U (above) and V (below)
+// whose inverses are known, T_VU = -T_VV (L_VU T_UU).  log2(nblk) levels of two batched GEMMs;
+// the product L_VU T_UU is parked in W (free once the factor is accepted).
+template <typename T>
+__global__ __launch_bounds__(256) void init_tinv_kernel(const T* Td, T* Tf, int64_t r, int64_t nblk, const int* st,
+                                                        int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    Tf += bz * r * r;
+    Td += bz * nblk * kNB * kNB;
+    const int64_t total = r * r;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t i = idx / r, k = idx % r;
+        const int64_t bi = i / kNB, bk = k / kNB;
+        Tf[idx] = (bi == bk) ? Td[(bi * kNB + (i % kNB)) * kNB + (k % kNB)] : T(0);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void copy_pred_kernel(const T* src, T* dst, int64_t total, const int* st,
+                                                        int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256)
+        dst[bz * total + idx] = src[bz * total + idx];
+}
+
+template <typename T>
+static int invert(const ChainCtx& c, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t r = p.r, b = p.b;
+    const T* L = (const T*)(c.ws + p.L);
+    T* Tf = (T*)(c.ws + p.Tf);
+    T* Y = (T*)(c.ws + p.W);
+    constexpr int S = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    {
+        dim3 grid(grid_1d(r * r, 1024), (unsigned)b);
+        hipLaunchKernelGGL((init_tinv_kernel<T>), grid, dim3(256), 0, c.s, (const T*)(c.ws + p.Td), Tf, r, p.nblk,
+                           c.st, mask, val);
+        DION_TRY(hipGetLastError());
+    }
+    const int64_t rr = r * r * (int64_t)sizeof(T);
+    for (int64_t s = 1; s < p.nblk; s *= 2) {
+        const int64_t span = 2 * s * kNB;               // rows/cols of one group
+        const int64_t gfull = r / span;                 // groups with U and V entirely inside r
+        // (U0, V0, |U|, |V|, number of groups) for the full groups and the trailing partial one
+        struct Part { int64_t u0, nu, nv, ng; } parts[2];
+        int np = 0;
+        if (gfull > 0) parts[np++] = Part{0, s * kNB, s * kNB, gfull};
+        const int64_t u0 = gfull * span;
+        if (u0 + s * kNB < r) parts[np++] = Part{u0, s * kNB, r - (u0 + s * kNB), 1};
+        for (int q = 0; q < np; ++q) {
+            const Part& pt = parts[q];
+            const int64_t v0 = pt.u0 + pt.nu;
+            const int64_t gstep = span * (r + 1) * (int64_t)sizeof(T);
+            // Y = L_VU T_UU   (T_UU lower: only k >= n contributes)
+            GemmArgs g{};
+            g.a = Operand{L + v0 * r + pt.u0, nullptr, r, (int)pt.nv, (int)pt.nu, vr};
+            g.b = Operand{Tf + pt.u0 * r + pt.u0, nullptr, r, (int)pt.nu, (int)pt.nu, vr};
+            g.sa0 = g.sb0 = g.sc = rr;
+            g.ga0 = g.gb0 = g.gc = gstep;
+            g.zdiv = (int)pt.ng;
+            g.c = Y + v0 * r + pt.u0; g.ldc = r;
+            g.M = (int)pt.nv; g.N = (int)pt.nu; g.K = (int)pt.nu;
+            g.alpha = 1; g.beta = 0; g.kskip = 2;
+            g.st = c.st; g.st_mask = mask; g.st_val = val;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(g, b, c.s)));
+            // T_VU = -T_VV Y   (T_VV lower: only k <= i contributes)
+            GemmArgs h = g;
+            h.a = Operand{Tf + v0 * r + v0, nullptr, r, (int)pt.nv, (int)pt.nv, vr};
+            h.b = Operand{Y + v0 * r + pt.u0, nullptr, r, (int)pt.nu, (int)pt.nv, vr};
+            h.c = Tf + v0 * r + pt.u0;
+            h.K = (int)pt.nv;
+            h.alpha = -1; h.kskip = 3;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(h, b, c.s)));
+        }
+    }
+    return 0;
+}
+
+// Pout = Pin Tf^T = Pin L^-T  (Tf lower: output column tile n0 needs only k < n0 + BN)
+template <typename T>
+static int apply(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r;
+    constexpr int S = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    GemmArgs g{};
+    g.a = Operand{Pin, nullptr, r, (int)m, (int)r, vr};                     // A(i,k) = Pin[i][k]
+    g.b = Operand{c.ws + p.Tf, nullptr, r, (int)r, (int)r, vr};             // B(k,j) = Tf[j][k]
+    g.sa0 = m * r * (int64_t)sizeof(T);
+    g.sb0 = r * r * (int64_t)sizeof(T);
+    g.c = Pout; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T);
+    g.M = (int)m; g.N = (int)r; g.K = (int)r;
+    g.alpha = 1; g.beta = 0; g.kskip = 1;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, p.b, c.s)));
+    return 0;
+}
+
+// One CholeskyQR pass Pin -> Pout: W = Pin^T Pin, L = chol(W), Pout = Pin L^-T.
+template <typename T>
+static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, double tau, int fail_bit,
+                       int tau_bit) {
+    int e;
+    if ((e = gram<T>(c, Pin, mask, val))) return e;
+    if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, 0))) return e;
+    if ((e = invert<T>(c, mask, val))) return e;
+    return apply<T>(c, Pin, Pout, mask, val);
+}
+
+// P0 = (M + G) Q  and  R = (M + G)^T P for one chain.
+template <typename T, int ASRC>
+static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, const float* Q, T* P, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, n = p.n, r = p.r;
+    GemmArgs g{};
+    const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
+    g.a = Operand{M, G, n, (int)m, (int)n, va};                    // A(i,k) = B[i][k]
+    g.b = Operand{Q, nullptr, r, (int)r, (int)n, (r % 4) == 0};    // B(k,j) = Q[k][j]
+    g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = n * r * 4;
+    g.c = P; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T);
+    g.M = (int)m; g.N = (int)r; g.K = (int)n;
+    g.alpha = 1; g.beta = 0;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    DION_TRY((launch_gemm<T, 64, 64, true, ASRC, false, SRC_F32>(g, p.b, c.s)));
+    return 0;
+}
+
+template <typename T, int ASRC>
+static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, const T* P, T* R, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, n = p.n, r = p.r;
+    GemmArgs g{};
+    const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
+    g.a = Operand{M, G, n, (int)n, (int)m, va};                    // A(i,k) = B[k][i]
+    g.b = Operand{P, nullptr, r, (int)r, (int)m, (r % 4) == 0};    // B(k,j) = P[k][j]
+    g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = m * r * (int64_t)sizeof(T);
+    g.c = R; g.ldc = r; g.sc = n * r * (int64_t)sizeof(T);
+    g.M = (int)n; g.N = (int)r; g.K = (int)m;
+    g.alpha = 1; g.beta = 0;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    DION_TRY((launch_gemm<T, 64, 64, false, ASRC, false, SrcOf<T>::v>(g, p.b, c.s)));
+    return 0;
+}
+
+template <typename T>
+static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf16, const float* Q,
+                     bool force32, void* const* ev) {
+    // ev: events marking the starts of the chain's three phases (product, QR, back-projection)
+    auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], c.s) : hipSuccess; };
+    const Plan& p = *c.p;
+    const bool is64 = sizeof(T) == 8;
+    T* P = (T*)(c.ws + (is64 ? p.P64 : p.P32));
+    T* R = (T*)(c.ws + (is64 ? p.R64 : p.R32));
+    const int gsz = g_bf16 ? 2 : 4;
+    int e;
+    if (!is64) {
+        // fp32 chain: matrices not (yet) owned by the fp64 chain; P32 -> tmp -> P32
+        T* tmp = (T*)(c.ws + p.P64b);
+        const int mask = ST_PATH64 | ST_FAIL, val = 0;
+        const int fail = force32 ? ST_FAIL : ST_PATH64;
+        DION_TRY(mark(0));
+        if ((e = g_bf16 ? bq_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, Q, P, mask, val)
+                        : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, mask, val))) return e;
+        DION_TRY(mark(1));
+        if ((e = cholqr_pass<T>(c, P, tmp, mask, val, force32 ? 0.0 : kTau32, fail, ST_PATH64))) return e;
+        if ((e = cholqr_pass<T>(c, tmp, P, mask, val, 0.0, fail, 0))) return e;
+        DION_TRY(mark(2));
+        return g_bf16 ? btp_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, P, R, mask, val)
+                      : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, mask, val);
+    }
+    // fp64 chain: P64 -> P64b -> P64 (-> P64b -> P64 after a shifted first pass)
+    T* Pb = (T*)(c.ws + p.P64b);
+    const int A64 = ST_PATH64, SH = ST_SHIFT, F = ST_FAIL;
+    DION_TRY(mark(0));
+    if ((e = g_bf16 ? bq_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, Q, P, A64, A64)
+                    : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, A64, A64))) return e;
+    DION_TRY(mark(1));
+    // pass 1: unshifted attempt; a failed pivot or a large diagonal ratio marks SHIFT,
+    // and the marked matrices factor W + s I instead (W is kept by the factorization)
+    if ((e = gram<T>(c, P, A64 | F, A64))) return e;
+    if ((e = factor<T>(c, A64 | SH | F, A64, kTau64, SH, SH, 0))) return e;
+    if ((e = factor<T>(c, A64 | SH | F, A64 | SH, 0.0, F, 0, 1))) return e;
+    if ((e = invert<T>(c, A64 | F, A64))) return e;
+    if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
+    // pass 2
+    if ((e = cholqr_pass<T>(c, Pb, P, A64 | F, A64, 0.0, F, 0))) return e;
+    // pass 3, only after a shifted first pass
+    if ((e = cholqr_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, 0.0, F, 0))) return e;
+    {
+        dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
+        hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st, A64 | SH | F,
+                           A64 | SH);
+        DION_TRY(hipGetLastError());
+    }
+    DION_TRY(mark(2));
+    return g_bf16 ? btp_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, P, R, A64, A64)
+                  : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, A64, A64);
+}
+
+template <bool GB, bool XB>
+static hipError_t launch_update(const Plan& p, const char* ws, float* M, const void* G, void* X, float mu,
+                                float lr, hipStream_t s) {
+    UpdArgs u{};
+    u.P = (const float*)(ws + p.P32);
+    u.R = (const float*)(ws + p.R32);
+    u.cs = (const double*)(ws + p.cs);
+    u.M = M; u.G = G; u.X = X;
+    u.m = (int)p.m; u.n = (int)p.n; u.r = (int)p.r;
+    u.one_minus_mu = 1.0f - mu;
+    u.lr_s = (float)((double)lr * sqrt((double)p.m / (double)p.n));
+    u.vec = (p.r % 4) == 0;
+    dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
+    hipLaunchKernelGGL((update_kernel<64, 64, GB, XB>), grid, dim3(256), 0, s, u);
+    return hipGetLastError();
+}
+
+int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps, int x_bf16,
+             int g_bf16, char* ws, int32_t* flags, uint32_t options, void* stream, void* const* ev) {
+    hipStream_t s = (hipStream_t)stream;
+    auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
+    if (p.b == 0) return 0;
+    const int64_t mn = p.m * p.n;
+    if (p.r == 0) {
+        for (int i = 0; i < DION_NUM_PHASES; ++i) DION_TRY(mark(i));
+        dim3 grid(grid_1d(p.b * mn, 8192));
+        if (g_bf16) hipLaunchKernelGGL((add_grad_kernel<true>), grid, dim3(256), 0, s, M, G, p.b * mn);
+        else hipLaunchKernelGGL((add_grad_kernel<false>), grid, dim3(256), 0, s, M, G, p.b * mn);
+        DION_TRY(hipGetLastError());
+        if (flags) {  // a fill kernel rather than a memset node, so callers may capture the step in a graph
+            hipLaunchKernelGGL(zero_flags_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, flags, p.b);
+            DION_TRY(hipGetLastError());
+        }
+        DION_TRY(mark(DION_NUM_PHASES));
+        return 0;
+    }
+    const bool force64 = options & DION_OPT_FORCE_F64;
+    const bool force32 = options & DION_OPT_FORCE_F32;
+    const bool sticky = options & DION_OPT_STICKY_F64;
+    ChainCtx c{&p, ws, (int*)(ws + p.st), s};
+    DION_TRY(mark(DION_PHASE_INIT));
+    hipLaunchKernelGGL(init_state_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, c.st, (const int32_t*)flags, p.b,
+                       (int)force64, (int)sticky);
+    DION_TRY(hipGetLastError());
+    int e;
+    if (!force64 && (e = run_chain<float>(c, M, G, g_bf16, Q, force32, ev ? ev + DION_PHASE_F32_PRODUCT : nullptr)))
+        return e;
+    if (force64 && ev)
+        for (int i = DION_PHASE_F32_PRODUCT; i <= DION_PHASE_F32_BACKPROJECT; ++i) DION_TRY(mark(i));
+    if (!force32 && (e = run_chain<double>(c, M, G, g_bf16, Q, force32, ev ? ev + DION_PHASE_F64_PRODUCT : nullptr)))
+        return e;
+    if (force32 && ev)
+        for (int i = DION_PHASE_F64_PRODUCT; i <= DION_PHASE_F64_BACKPROJECT; ++i) DION_TRY(mark(i));
+    DION_TRY(mark(DION_PHASE_NORMS));
+
+    // column norms -> c = 1 / (||r_j|| + eps); Q <- R c; fp64-chain P, R rounded to fp32
+    {
+        dim3 grid((unsigned)((p.r + 63) / 64), (unsigned)p.nchunk, (unsigned)p.b);
+        hipLaunchKernelGGL(colnorm_partial_kernel, grid, dim3(256), 0, s, (const float*)(ws + p.R32),
+                           (const double*)(ws + p.R64), (double*)(ws + p.part), p.n, p.r, (int)p.nchunk, c.st);
+        DION_TRY(hipGetLastError());
+        dim3 g2((unsigned)((p.r + 255) / 256), (unsigned)p.b);
+        hipLaunchKernelGGL(colscale_kernel, g2, dim3(256), 0, s, (const double*)(ws + p.part), (double*)(ws + p.cs),
+                           p.r, (int)p.nchunk, (double)eps);
+        DION_TRY(hipGetLastError());
+        dim3 g3(grid_1d(p.n * p.r, 1024), (unsigned)p.b);
+        hipLaunchKernelGGL(next_q_kernel, g3, dim3(256), 0, s, (const double*)(ws + p.R64), (float*)(ws + p.R32),
+                           (const double*)(ws + p.cs), Q, p.n, p.r, c.st);
+        DION_TRY(hipGetLastError());
+        dim3 g4(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
+        hipLaunchKernelGGL(round_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
+                           p.m * p.r, c.st);
+        DION_TRY(hipGetLastError());
+    }
+    DION_TRY(mark(DION_PHASE_UPDATE));
+    hipError_t he;
+    if (g_bf16) he = x_bf16 ? launch_update<true, true>(p, ws, M, G, X, mu, lr, s)
+                            : launch_update<true, false>(p, ws, M, G, X, mu, lr, s);
+    else he = x_bf16 ? launch_update<false, true>(p, ws, M, G, X, mu, lr, s)
+                     : launch_update<false, false>(p, ws, M, G, X, mu, lr, s);
+    DION_TRY(he);
+    DION_TRY(mark(DION_PHASE_FLAGS));
+    if (flags) {
+        hipLaunchKernelGGL(flags_out_kernel, dim3((unsigned)p.b), dim3(256), 0, s, c.st,
+                           (const double*)(ws + p.cs), p.r, flags);
+        DION_TRY(hipGetLastError());
+    }
+    DION_TRY(mark(DION_NUM_PHASES));
+    return 0;
+}
+
+}  // namespace dion
