@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import math
 import os
+import sys
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
@@ -239,12 +240,14 @@ def make_grad(wl: Workload, gi: int, step: int, seed: int = 0) -> np.ndarray:
         n = g.n
         sig = 10.0 ** (-a["decades"] * np.arange(n) / n)
 
-        def one(mi):
+        # one matrix at a time: the QRs and the product already use every BLAS thread
+        for mi in range(g.batch):
+            if n >= 1024:
+                print(f"[workloads] {wl.name} step {step}: Haar factors of matrix {mi + 1}/{g.batch}",
+                      file=sys.stderr, flush=True)
             U = _haar(_rng(seed, wl.wid, gi, mi, step, _T_U), n)
             V = _haar(_rng(seed, wl.wid, gi, mi, step, _T_V), n)
             out[mi] = store((U * sig[None, :]) @ V.T, dt)
-        with ThreadPoolExecutor(max(1, min(g.batch, _workers() // 4 or 1))) as ex:
-            list(ex.map(one, range(g.batch)))
     else:
         raise ValueError(f"unknown gradient recipe {kind!r}")
     return out
