@@ -103,6 +103,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--grads", type=int, default=3, help="distinct resident gradients cycled through")
     ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
+    ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -140,7 +141,7 @@ def main() -> int:
         stacks.append(dict(g=g, X=dev_t(X), M=dev_t(M), Q=dev_t(Q), G=grads,
                            flags=torch.zeros(g.batch, dtype=torch.int32, device=dev),
                            ws=workspace_for(g.m, g.n, g.batch, g.rank, dev)))
-    opts = 0 if args.no_sticky else dion.OPT_STICKY_F64
+    opts = (0 if args.no_sticky else dion.OPT_STICKY_F64) | ((args.chunks & 15) << 8)
     stream = torch.cuda.current_stream(dev)
 
     def one_step(k, events=None):
@@ -223,7 +224,7 @@ def main() -> int:
         "config": {"workload": wl.name,
                    "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],
                    "mu": wl.mu, "lr": wl.lr, "eps": wl.eps, "grad": wl.grad,
-                   "sticky_fp64": not args.no_sticky},
+                   "sticky_fp64": not args.no_sticky, "chunks": args.chunks or "auto"},
         "effective_param_GBps": eff_gbs,
         "pct_hbm_roofline": 100.0 * eff_gbs / HBM_PEAK_GBS,
         "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,

@@ -32,7 +32,7 @@
  *
  * Memory and ownership
  *   Every buffer is device memory owned by the caller; the library allocates
- *   nothing and keeps no state between calls.  Layouts are row-major and
+ *   no device memory and keeps no data between calls.  Layouts are row-major and
  *   contiguous: X, G, M as [batch][m][n]; Q as [batch][n][rank].
  *   X, M and Q are updated in place; G is read only.  X and G are fp32 or
  *   bf16 (independently); M and Q are fp32.  The workspace is scratch owned by
@@ -42,11 +42,16 @@
  *   state buffers must not overlap each other or the workspace.
  *
  * Execution
- *   Asynchronous: everything is enqueued on `stream` (a hipStream_t, NULL =
- *   the default stream) and the call returns without a host synchronization.
- *   Results are bitwise reproducible for the same inputs on the same device
- *   (no floating-point atomics).  Calls that share a workspace must be
- *   ordered on one stream.
+ *   Asynchronous: the call returns without a host synchronization.  The stack
+ *   may be split into chunks of whole matrices that run concurrently on the
+ *   library's own streams (a per-device set of default-priority HIP streams
+ *   and events, created on first use and kept): they start after the work
+ *   already enqueued on `stream` (a hipStream_t, NULL = the default stream)
+ *   and `stream` waits for them before anything enqueued after the call, so
+ *   the call behaves as if everything ran on `stream`.  Results are bitwise
+ *   reproducible for the same inputs on the same device whatever the chunking
+ *   (no floating-point atomics; matrices are independent).  Calls that share
+ *   a workspace must be ordered on one stream.
  *
  * Errors
  *   0 = success.  A negative status below -99 is a HIP launch error
@@ -88,8 +93,10 @@ enum {
     DION_OPT_STICKY_F64 = 1,  /* matrices whose flags word has DION_FLAG_F64 set on entry
                                  skip the fp32 attempt and go straight to the fp64 chain */
     DION_OPT_FORCE_F64 = 2,   /* every matrix uses the fp64 chain */
-    DION_OPT_FORCE_F32 = 4    /* never fall back; an fp32 breakdown is reported as
+    DION_OPT_FORCE_F32 = 4,   /* never fall back; an fp32 breakdown is reported as
                                  DION_FLAG_NONFINITE and its results are undefined */
+    DION_OPT_CHUNKS_SHIFT = 8 /* bits 8..11: number of concurrent chunks the stack is split into
+                                 (0 = automatic, 1 = everything on `stream`); see Execution */
 };
 
 /* per-matrix `flags` bits written by the step (device int32 [batch]) */
@@ -146,9 +153,10 @@ int dion_step_batched(void* X, const void* G, float* M, float* Q,
 /*
  * dion_step_batched with phase markers, for profiling.  `events` holds
  * DION_NUM_PHASES + 1 hipEvent_t handles created by the caller; events[i] is
- * recorded on `stream` where phase i starts and events[DION_NUM_PHASES] after
- * the last launch, so hipEventElapsedTime(events[i], events[i + 1]) is the
- * device time of phase i.  The single-kernel phases (the four products, the
+ * recorded where phase i of the first chunk starts (on the stream that runs
+ * that chunk) and events[DION_NUM_PHASES] after its last launch, so
+ * hipEventElapsedTime(events[i], events[i + 1]) is the device time of phase i
+ * for the first chunk's matrices (all matrices when the step is not split).  The single-kernel phases (the four products, the
  * update) time one kernel each.  A chain that does not run records its three
  * events back to back.  No host synchronization; same results and status
  * codes as dion_step_batched.  `events` may be NULL.

@@ -24,6 +24,12 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_HYPER, ERR_ALIGN = -1, -2, -3, -4, -5
 ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_HIP = -6, -7, -8, -9, -100
 OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32 = 1, 2, 4
+OPT_CHUNKS_SHIFT = 8
+
+
+def opt_chunks(n: int) -> int:
+    """Option bits asking for n concurrent chunks (1 = everything on the caller's stream)."""
+    return (int(n) & 15) << OPT_CHUNKS_SHIFT
 FLAG_F64, FLAG_NONFINITE, FLAG_SHIFTED = 1, 2, 4
 
 NUM_PHASES = 10

@@ -26,7 +26,20 @@ struct Plan {
     // byte offsets into the workspace (all 256-byte aligned)
     size_t P32, R32, cs, st, kap, W, L, Td, Tf, P64, P64b, R64, part;
     size_t total;
+    // bytes per matrix of each region (a region is [batch][...] and contiguous)
+    size_t sP32, sR32, scs, sst, skap, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart;
 };
+
+// The sub-plan of matrices [c0, c0 + cb): same sizes, region offsets advanced to matrix c0.
+inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
+    Plan q = p;
+    q.b = cb;
+    const size_t c = (size_t)c0;
+    q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap;
+    q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
+    q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart;
+    return q;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -57,6 +70,9 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.part = take(B * q.nchunk * r * 8);   // column-norm partial sums (fp64)
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
+    q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16;
+    q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
+    q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
     *p = q;
     return true;
 }

@@ -26,6 +26,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dion.h"
 #include "dion_plan.h"
 #include "gemm_mfma.hpp"
@@ -181,7 +183,9 @@ __device__ __forceinline__ void diag_step(DiagCtx<T>& c) {
     for (int s = sk; s < NS; ++s) c.a[s] -= coef * cj[s];
 #pragma unroll
     for (int s = 0; s <= sk; ++s) c.x[s] -= coef * xk[s];
-    if (own && c.row_ok && c.i >= K) c.Lrow[K] = (c.i == K) ? lkk : lik;
+    // L_iK replaces the consumed column K in its owner's register slot (stored once at the end:
+    // a global store inside the sweep would make the next column wait for it)
+    if (own) c.a[sk] = (c.i == K) ? lkk : lik;
     if (c.tid == 0) c.dg[K] = lkk;
 }
 
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
     // Thread t owns row i = t / 4 and, in registers, the 16 columns j = 4 s + t % 4 of that row of
     // the working matrix and of X.  Per column, the raw column k (zero at rows <= k), the pivot and
     // row k of X (zero right of the diagonal) travel through double-buffered LDS, so the updates
-    // need no predicates and one barrier per column suffices.  L_ik goes straight to global memory.
+    // need no predicates and one barrier per column suffices.
     constexpr int NB = kNB, NS = NB / 4;
     static_assert(NB * 4 == 256, "one row per four threads");
     const int bz = blockIdx.x;
@@ -252,6 +256,7 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int j = 4 * s + part;
+        if (c.row_ok && j <= i) c.Lrow[j] = c.a[s];
         Td[i * NB + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
     }
 }
@@ -493,6 +498,11 @@ __global__ __launch_bounds__(256) void flags_out_kernel(const int* st, const dou
     do {                                            \
         hipError_t e_ = (expr);                     \
         if (e_ != hipSuccess) return (int)e_;       \
+    } while (0)
+#define DION_TRY_HIP(expr)                          \
+    do {                                            \
+        hipError_t e_ = (expr);                     \
+        if (e_ != hipSuccess) return e_;            \
     } while (0)
 
 static bool aligned4(const void* p, int esz) { return ((uintptr_t)p % (uintptr_t)(4 * esz)) == 0; }
@@ -814,9 +824,10 @@ static hipError_t launch_update(const Plan& p, const char* ws, float* M, const v
     return hipGetLastError();
 }
 
-int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps, int x_bf16,
-             int g_bf16, char* ws, int32_t* flags, uint32_t options, void* stream, void* const* ev) {
-    hipStream_t s = (hipStream_t)stream;
+// The whole step for the matrices of one chunk, on stream s.
+static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps,
+                     int x_bf16, int g_bf16, char* ws, int32_t* flags, uint32_t options, hipStream_t s,
+                     void* const* ev) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (p.b == 0) return 0;
     const int64_t mn = p.m * p.n;
@@ -885,6 +896,69 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu
         DION_TRY(hipGetLastError());
     }
     DION_TRY(mark(DION_NUM_PHASES));
+    return 0;
+}
+
+// Streams and events of the internal fork/join, one set per device, created on first use
+// (default priority).  A step is split into chunks of whole matrices, each run on its own
+// stream, so that one chunk's latency-bound CholeskyQR overlaps another chunk's GEMMs.
+constexpr int kMaxChunks = 8;
+struct StreamSet {
+    bool ready = false;
+    hipStream_t s[kMaxChunks];
+    hipEvent_t fork, join[kMaxChunks];
+};
+static std::mutex g_stream_mu;
+static StreamSet g_streams[64];
+
+static hipError_t stream_set(StreamSet** out) {
+    int dev = 0;
+    DION_TRY_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    StreamSet& ss = g_streams[dev];
+    if (!ss.ready) {
+        for (int i = 0; i < kMaxChunks; ++i) {
+            DION_TRY_HIP(hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking));
+            DION_TRY_HIP(hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming));
+        }
+        DION_TRY_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+        ss.ready = true;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
+static int auto_chunks(const Plan& p) {
+    // two chunks give the overlap; more would shrink the GEMM grids
+    return p.b >= 2 && p.r > 0 ? 2 : 1;
+}
+
+int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps, int x_bf16,
+             int g_bf16, char* ws, int32_t* flags, uint32_t options, void* stream, void* const* ev) {
+    hipStream_t s = (hipStream_t)stream;
+    if (p.b == 0) return 0;
+    int nc = (int)((options >> DION_OPT_CHUNKS_SHIFT) & 15u);
+    if (nc == 0) nc = auto_chunks(p);
+    if (nc > kMaxChunks) nc = kMaxChunks;
+    if (nc > p.b) nc = (int)p.b;
+    if (nc <= 1)
+        return run_chunk(p, X, G, M, Q, mu, lr, eps, x_bf16, g_bf16, ws, flags, options, s, ev);
+    std::lock_guard<std::mutex> lock(g_stream_mu);
+    StreamSet* ss = nullptr;
+    DION_TRY(stream_set(&ss));
+    DION_TRY(hipEventRecord(ss->fork, s));
+    const int64_t mn = p.m * p.n, xs = x_bf16 ? 2 : 4, gs = g_bf16 ? 2 : 4;
+    for (int c = 0; c < nc; ++c) {
+        const int64_t c0 = p.b * c / nc, c1 = p.b * (c + 1) / nc;
+        const Plan q = chunk_plan(p, c0, c1 - c0);
+        DION_TRY(hipStreamWaitEvent(ss->s[c], ss->fork, 0));
+        int e = run_chunk(q, (char*)X + c0 * mn * xs, (const char*)G + c0 * mn * gs, M + c0 * mn,
+                          Q ? Q + c0 * p.n * p.r : nullptr, mu, lr, eps, x_bf16, g_bf16, ws, flags ? flags + c0 : nullptr,
+                          options, ss->s[c], c == 0 ? ev : nullptr);
+        if (e) return e;
+        DION_TRY(hipEventRecord(ss->join[c], ss->s[c]));
+        DION_TRY(hipStreamWaitEvent(s, ss->join[c], 0));
+    }
     return 0;
 }
 

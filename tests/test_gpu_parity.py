@@ -87,3 +87,25 @@ def test_many_rank_blocks(cuda, recipe, options):
     opts = dion.OPT_FORCE_F64 if options == "f64" else 0
     rep = run_teacher_forced(wl, cuda, options=opts)
     check(rep, tol_for(wl))
+
+
+def test_chunking_is_bitwise_invariant(cuda):
+    """Splitting the stack into concurrent chunks changes nothing: matrices are independent."""
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    from rank_orthonormalized_optimizer_amd._lib import opt_chunks
+    wl = W.SMALL[2].with_groups(W.Group(5, 320, 288, 72), name="chunks")
+    X, M, Q = W.make_state(wl, 0)
+    outs = []
+    for nc in (1, 2, 3, 5):
+        Xd, Md, Qd = to_torch(X, cuda), to_torch(M, cuda), to_torch(Q, cuda)
+        flags = torch.zeros(5, dtype=torch.int32, device=cuda)
+        for t in (1, 2):
+            Gd = to_torch(W.make_grad(wl, 0, t), cuda)
+            dion.step_(Xd, Gd, Md, Qd, 72, wl.mu, wl.lr, wl.eps, flags=flags,
+                       options=dion.OPT_STICKY_F64 | opt_chunks(nc))
+        torch.cuda.synchronize()
+        outs.append((to_numpy(Xd), to_numpy(Md), to_numpy(Qd), to_numpy(flags)))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
