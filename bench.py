@@ -105,6 +105,8 @@ def main() -> int:
     ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
     ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -151,6 +153,13 @@ def main() -> int:
                        workspace=s["ws"], flags=s["flags"], options=opts, stream=stream,
                        events=None if events is None else events[si])
 
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written", file=sys.stderr, flush=True)
+        del src, dst
     print("[bench] warmup", file=sys.stderr, flush=True)
     for k in range(args.warmup):
         one_step(k)
@@ -174,6 +183,7 @@ def main() -> int:
     for k in range(args.steps):
         one_step(args.warmup + k, events=evs[k])
     t1.record(stream)
+    enqueue = time.perf_counter() - w0
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = t0.elapsed_time(t1) / args.steps
@@ -231,6 +241,7 @@ def main() -> int:
         "matrices": nmat, "fp64_chain_matrices": n64, "nonfinite_matrices": nbad,
         "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
         "wall_s_timed_region": wall,
+        "host_enqueue_ms_per_step": 1000.0 * enqueue / args.steps,
         "roofline": {"bound": "mfma", "kernel": dom, "what": what, "dtype": dt_,
                      "achieved": achieved, "peak": PEAK_TFLOPS[dt_], "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TFLOPS[dt_],

@@ -17,17 +17,19 @@ enum : int {
     ST_PATH64 = 1,   // the fp64 chain owns this matrix
     ST_SHIFT = 2,    // the fp64 chain needs the shifted first pass (and a third pass)
     ST_FAIL = 4,     // a factorization broke down with no further fallback
+    ST_CHOL2 = 8,    // this re-orthonormalization pass uses the Cholesky path (P^T P far from I)
 };
 
 struct Plan {
     int64_t m, n, b, r;
     int64_t nblk;      // number of rank column blocks
     int64_t nchunk;    // row chunks of the column-norm reduction
+    int64_t gsplit;    // K-splits of the Gram products (partials reduced in fixed order)
     // byte offsets into the workspace (all 256-byte aligned)
-    size_t P32, R32, cs, st, kap, W, L, Td, Tf, P64, P64b, R64, part;
+    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart;
     size_t total;
     // bytes per matrix of each region (a region is [batch][...] and contiguous)
-    size_t sP32, sR32, scs, sst, skap, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart;
+    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart;
 };
 
 // The sub-plan of matrices [c0, c0 + cb): same sizes, region offsets advanced to matrix c0.
@@ -35,9 +37,9 @@ inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     Plan q = p;
     q.b = cb;
     const size_t c = (size_t)c0;
-    q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap;
+    q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
-    q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart;
+    q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart; q.gpart += c * p.sgpart;
     return q;
 }
 
@@ -52,6 +54,15 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.m = m; q.n = n; q.b = b; q.r = r;
     q.nblk = (r + kNB - 1) / kNB;
     q.nchunk = (n + kNormChunk - 1) / kNormChunk;
+    {   // split the Gram's long K (= m) until the grid has ~1024 tiles, keeping >= 128 rows per split
+        const int64_t nt = (r + 63) / 64;
+        const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
+        int64_t s = (1024 + tiles - 1) / tiles;
+        if (s > 16) s = 16;
+        if (s > m / 128) s = m / 128;
+        while (s > 1 && (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20)) --s;
+        q.gsplit = s < 1 ? 1 : s;
+    }
     size_t off = 0;
     auto take = [&](double bytes) { size_t o = off; off = align256(off + (size_t)bytes); return o; };
     const double B = (double)b;
@@ -60,6 +71,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.cs = take(B * r * 8);                // 1 / (||r_j|| + eps), fp64
     q.st = take(B * 4);                    // state words
     q.kap = take(B * 2 * 8);               // running min / max Cholesky diagonal
+    q.emax = take(B * 8);                  // max |P^T P - I| of a re-orthonormalization pass
     q.W = take(B * r * r * 8);             // Gram matrix (fp32 or fp64)
     q.L = take(B * r * r * 8);             // Cholesky factor, in place
     q.Td = take(B * q.nblk * kNB * kNB * 8);   // inverses of the diagonal blocks
@@ -68,11 +80,13 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.P64b = take(B * m * r * 8);          // second P buffer (fp64 chain; fp32 chain's scratch)
     q.R64 = take(B * n * r * 8);           // fp64 chain R
     q.part = take(B * q.nchunk * r * 8);   // column-norm partial sums (fp64)
+    q.gpart = take(q.gsplit > 1 ? B * q.gsplit * r * r * 8 : 0);   // Gram partials
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
-    q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16;
+    q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = 8;
     q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
+    q.sgpart = q.gsplit > 1 ? (size_t)(q.gsplit * r * r * 8) : 0;
     *p = q;
     return true;
 }

@@ -37,6 +37,12 @@ namespace dion {
 // Diagonal-ratio thresholds of the first Cholesky pass (see the header comment).
 constexpr double kTau32 = 64.0;
 constexpr double kTau64 = 1.0e7;
+// Re-orthonormalization passes: largest max|P^T P - I| handled by the near-identity series, and
+// the series lengths.  fp32: F = Phi(E), S = F (error ~ E^2 <= 1e-8, below fp32 rounding).
+// fp64: two fixed-point steps (error ~ E^2 (2E)^2 <= 4e-12) and S up to F^3 (error E^4 <= 1e-12).
+constexpr double kNearId32 = 1.0e-4;
+constexpr double kNearId64 = 1.0e-3;
+constexpr int kNearIdIters64 = 2, kNearIdTerms64 = 2;
 
 // ---------------------------------------------------------------------------
 // generic batched GEMM:  C = alpha * A B + beta * C
@@ -54,12 +60,17 @@ struct GemmArgs {
     int zdiv;                  // blockIdx.z = matrix * zdiv + group (0 or 1: no groups)
     int64_t ga0, gb0, gc;      // byte offsets between groups for a.p0, b.p0, c
     int kskip;                 // K range of a tile: 0 all; 1 k < n0 + BN (B = lower^T);
-                               // 2 k >= n0 (B lower); 3 k < m0 + BM (A lower)
+                               // 2 k >= n0 (B lower); 3 k < m0 + BM (A lower); 4 both 2 and 3
+    int ksplit_total;          // > 0: group g covers K rows [g K, min((g + 1) K, ksplit_total)) of
+                               // the operands (their base advanced by ga0 / gb0 per group)
+    const void* csrc;          // beta term read from here instead of c (same layout), if set
+    int phi;                   // epilogue c = Phi(csrc - I + alpha acc): strictly lower part kept,
+                               // diagonal halved, upper part zero (square outputs only)
 };
 
-template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
+template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-    using C = TileCfg<T, BM, BN>;
+    using C = TileCfg<T, BM, BN, BK>;
     const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
     const int bz = blockIdx.z / zdiv, grp = blockIdx.z % zdiv;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
@@ -69,14 +80,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     if (g.kskip == 1) kend = min(g.K, n0 + BN);
     else if (g.kskip == 2) kbeg = (n0 / C::BK) * C::BK;
     else if (g.kskip == 3) kend = min(g.K, m0 + BM);
+    else if (g.kskip == 4) { kbeg = (n0 / C::BK) * C::BK; kend = min(g.K, m0 + BM); }
+    int kext = 0;
+    if (g.ksplit_total > 0) {
+        kext = min(g.K, g.ksplit_total - grp * g.K);
+        kend = min(kend, kext);
+    }
 
-    __shared__ T As[C::BK * C::LDA];
-    __shared__ T Bs[C::BK * C::LDB];
+    __shared__ T As[2 * C::A_STAGE];
+    __shared__ T Bs[2 * C::B_STAGE];
 
     Operand A = g.a, B = g.b;
     A.p0 = (const char*)A.p0 + bz * g.sa0 + grp * g.ga0;
     if (A.p1) A.p1 = (const char*)A.p1 + bz * g.sa1;
     B.p0 = (const char*)B.p0 + bz * g.sb0 + grp * g.gb0;
+    if (g.ksplit_total > 0) { A.kext = kext; B.kext = kext; }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -86,19 +104,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{0, 0, 0, 0};
 
-    TileLoader<T, BM, C::BK, AKC, ASRC> la;
-    TileLoader<T, BN, C::BK, BKC, BSRC> lb;
-    if (kbeg < kend) { la.load(A, m0, kbeg); lb.load(B, n0, kbeg); }
-    for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
-        la.template store<C::LDA>(As);
-        lb.template store<C::LDB>(Bs);
-        __syncthreads();
-        if (k0 + C::BK < kend) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
-        mma_slab<T, C>(As, Bs, acc, wm, wn, lane);
-        __syncthreads();
-    }
+    mainloop<T, C, AKC, ASRC, BKC, BSRC>(A, B, m0, n0, kbeg, kend, As, Bs, acc, [](int, int) {});
 
     T* Cp = (T*)((char*)g.c + bz * g.sc + grp * g.gc);
+    const T* Sp = g.csrc ? (const T*)((const char*)g.csrc + bz * g.sc + grp * g.gc) : Cp;
     const T alpha = (T)g.alpha, beta = (T)g.beta;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -109,21 +118,74 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                 const int row = m0 + wm * C::WTM + i * 16 + Mfma<T>::row(lane, v);
                 const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
                 if (row < g.M && col < g.N) {
-                    T* cp = Cp + (int64_t)row * g.ldc + col;
+                    const int64_t off = (int64_t)row * g.ldc + col;
                     T val = alpha * acc[i][j][v];
-                    if (beta != T(0)) val += beta * *cp;
-                    *cp = val;
+                    if (g.phi) {
+                        val += Sp[off] - (row == col ? T(1) : T(0));
+                        val = row > col ? val : (row == col ? T(0.5) * val : T(0));
+                    } else if (beta != T(0)) {
+                        val += beta * Sp[off];
+                    }
+                    Cp[off] = val;
                 }
             }
 }
 
-template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
-static hipError_t launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t s) {
+template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
+static hipError_t launch_gemm_tile(const GemmArgs& g, int64_t batch, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
     const int64_t zdiv = g.zdiv > 1 ? g.zdiv : 1;
     dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, (unsigned)(batch * zdiv));
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AKC, ASRC, BKC, BSRC>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, AKC, ASRC, BKC, BSRC>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
+}
+
+// Tile choice.  The large tile is used when the grid still has at least kBigTileMinTiles
+// tiles; otherwise (and for in-place column-panel updates, which need N <= 64) 64 x 64.
+#ifndef DION_F64_BM
+#define DION_F64_BM 64
+#endif
+#ifndef DION_F64_BN
+#define DION_F64_BN 64
+#endif
+#ifndef DION_F64_BK
+#define DION_F64_BK 16
+#endif
+#ifndef DION_F32_BM
+#define DION_F32_BM 64
+#endif
+#ifndef DION_F32_BN
+#define DION_F32_BN 64
+#endif
+#ifndef DION_F32_BK
+#define DION_F32_BK 32
+#endif
+#ifndef DION_BIG_MIN_TILES
+#define DION_BIG_MIN_TILES 256
+#endif
+#ifndef DION_UPD_BM
+#define DION_UPD_BM 64
+#endif
+#ifndef DION_UPD_BN
+#define DION_UPD_BN 64
+#endif
+#ifndef DION_UPD_BK
+#define DION_UPD_BK 16
+#endif
+constexpr int kBigTileMinTiles = DION_BIG_MIN_TILES;
+
+template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
+static hipError_t launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t s) {
+    constexpr bool d = sizeof(T) == 8;
+    constexpr int LBM = d ? DION_F64_BM : DION_F32_BM, LBN = d ? DION_F64_BN : DION_F32_BN;
+    constexpr int LBK = d ? DION_F64_BK : DION_F32_BK, SBK = d ? 16 : 32;
+    const int64_t zdiv = g.zdiv > 1 ? g.zdiv : 1;
+    const int64_t big_tiles = ((g.M + LBM - 1) / LBM) * ((g.N + LBN - 1) / LBN) * batch * zdiv;
+    if constexpr (LBM != 64 || LBN != 64 || LBK != SBK) {
+        if (BM == 64 && BN == 64 && g.M >= LBM && g.N >= LBN && big_tiles >= kBigTileMinTiles)
+            return launch_gemm_tile<T, LBM, LBN, LBK, AKC, ASRC, BKC, BSRC>(g, batch, s);
+    }
+    return launch_gemm_tile<T, 64, 64, SBK, AKC, ASRC, BKC, BSRC>(g, batch, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -366,14 +428,16 @@ struct UpdArgs {
     int vec;   // r % 4 == 0
 };
 
-template <int BM, int BN, bool G_BF16, bool X_BF16>
+template <int BM, int BN, int BK, bool G_BF16, bool X_BF16>
 __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
-    using C = TileCfg<float, BM, BN>;
+    // Two accumulators share every LDS fragment: acc1 = P R^T and acc2 = P diag(c) R^T, the
+    // second from the A fragment scaled by the column scale of its k index.
+    using C = TileCfg<float, BM, BN, BK>;
     const int bz = blockIdx.z;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    __shared__ float As[C::BK * C::LDA];
-    __shared__ float Bs[C::BK * C::LDB];
-    __shared__ float Cs[C::BK];
+    __shared__ float As[2 * C::A_STAGE];
+    __shared__ float Bs[2 * C::B_STAGE];
+    __shared__ float Cs[2][BK];
     const int64_t mr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r, mn = (int64_t)u.m * u.n;
     Operand A{u.P + bz * mr, nullptr, u.r, u.m, u.r, u.vec != 0};
     Operand B{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec != 0};
@@ -388,27 +452,34 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
 
-    TileLoader<float, BM, C::BK, true, SRC_F32> la;
-    TileLoader<float, BN, C::BK, true, SRC_F32> lb;
+    TileLoader<float, BM, BK, true, SRC_F32> la;
+    TileLoader<float, BN, BK, true, SRC_F32> lb;
+    auto stage_c = [&](int k0, int buf) {
+        if (threadIdx.x < BK) Cs[buf][threadIdx.x] = (k0 + (int)threadIdx.x < u.r) ? (float)cs[k0 + threadIdx.x] : 0.f;
+    };
     la.load(A, m0, 0);
     lb.load(B, n0, 0);
-    for (int k0 = 0; k0 < u.r; k0 += C::BK) {
-        la.template store<C::LDA>(As);
-        lb.template store<C::LDB>(Bs);
-        if (threadIdx.x < C::BK) Cs[threadIdx.x] = (k0 + (int)threadIdx.x < u.r) ? (float)cs[k0 + threadIdx.x] : 0.f;
-        __syncthreads();
-        if (k0 + C::BK < u.r) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
+    la.template store<C::LDA>(As);
+    lb.template store<C::LDB>(Bs);
+    stage_c(0, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < u.r; k0 += BK) {
+        const bool more = k0 + BK < u.r;
+        if (more) { la.load(A, m0, k0 + BK); lb.load(B, n0, k0 + BK); }
+        const float* as = As + buf * C::A_STAGE;
+        const float* bs = Bs + buf * C::B_STAGE;
 #pragma unroll
-        for (int kk = 0; kk < C::BK; kk += 4) {
+        for (int kk = 0; kk < BK; kk += 4) {
             float a[C::FM], a2[C::FM], b[C::FN];
-            const float ck = Cs[kk + lk];
+            const float ck = Cs[buf][kk + lk];
 #pragma unroll
             for (int i = 0; i < C::FM; ++i) {
-                a[i] = As[(kk + lk) * C::LDA + wm * C::WTM + i * 16 + lr];
+                a[i] = as[(kk + lk) * C::LDA + wm * C::WTM + i * 16 + lr];
                 a2[i] = a[i] * ck;
             }
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) b[j] = Bs[(kk + lk) * C::LDB + wn * C::WTN + j * 16 + lr];
+            for (int j = 0; j < C::FN; ++j) b[j] = bs[(kk + lk) * C::LDB + wn * C::WTN + j * 16 + lr];
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -417,7 +488,13 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
                     acc2[i][j] = Mfma<float>::mma(a2[i], b[j], acc2[i][j]);
                 }
         }
+        if (more) {
+            la.template store<C::LDA>(As + (buf ^ 1) * C::A_STAGE);
+            lb.template store<C::LDB>(Bs + (buf ^ 1) * C::B_STAGE);
+            stage_c(k0 + BK, buf ^ 1);
+        }
         __syncthreads();
+        buf ^= 1;
     }
 
     float* Mp = u.M + bz * mn;
@@ -530,21 +607,54 @@ struct ChainCtx {
 //          of every diagonal block kept in Td; a failed pivot sets `fail_bit`, a diagonal
 //          ratio above `tau` (tau > 0) sets `tau_bit`
 // invert:  Tf = L^-1;   apply: Pout = Pin Tf^T
+// W = sum over the K-splits of the partial Grams, in split order (lower triangle).
+template <typename T>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const T* part, T* W, int64_t r, int64_t splits,
+                                                          const int* st, int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    part += bz * splits * r * r;
+    W += bz * r * r;
+    const int64_t total = r * r;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        T s = 0;
+        for (int64_t q = 0; q < splits; ++q) s += part[q * total + idx];
+        W[idx] = s;
+    }
+}
+
 template <typename T>
 static int gram(const ChainCtx& c, const T* P, int mask, int val) {
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
+    const int64_t splits = p.gsplit, kc = (m + splits - 1) / splits;
     GemmArgs g{};
     g.a = Operand{P, nullptr, r, (int)r, (int)m, vr};   // A(i,k) = P[k][i]
     g.b = Operand{P, nullptr, r, (int)r, (int)m, vr};   // B(k,j) = P[k][j]
     g.sa0 = g.sb0 = m * r * (int64_t)sizeof(T);
-    g.c = c.ws + p.W; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
-    g.M = g.N = (int)r; g.K = (int)m;
+    g.M = g.N = (int)r;
     g.alpha = 1; g.beta = 0;
     g.st = c.st; g.st_mask = mask; g.st_val = val; g.lower = 1;
+    if (splits <= 1) {
+        g.c = c.ws + p.W; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
+        g.K = (int)m;
+        DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
+        return 0;
+    }
+    g.K = (int)kc;
+    g.zdiv = (int)splits;
+    g.ksplit_total = (int)m;
+    g.ga0 = g.gb0 = kc * r * (int64_t)sizeof(T);
+    g.c = c.ws + p.gpart; g.ldc = r;
+    g.sc = splits * r * r * (int64_t)sizeof(T);
+    g.gc = r * r * (int64_t)sizeof(T);
     DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
+    dim3 grid(grid_1d(r * r, 512), (unsigned)p.b);
+    hipLaunchKernelGGL((gram_reduce_kernel<T>), grid, dim3(256), 0, c.s, (const T*)(c.ws + p.gpart), (T*)(c.ws + p.W),
+                       r, splits, c.st, mask, val);
+    DION_TRY(hipGetLastError());
     return 0;
 }
 
@@ -717,6 +827,131 @@ static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int v
     return apply<T>(c, Pin, Pout, mask, val);
 }
 
+// Re-orthonormalization of a nearly orthonormal P1 (the second CholeskyQR pass) without a
+// sequential factorization.  With W = P1^T P1 = I + E and chol(W) = I + F, F lower triangular,
+// F + F^T + F F^T = E, i.e. F = Phi(E - F F^T) where Phi keeps the strictly lower part and half
+// the diagonal.  Starting from F = Phi(E), each fixed-point step shrinks the error by ~2 max|E|.
+// Then (I + F)^-1 = I - S with S = F - F^2 + F^3 - ..., evaluated as S <- F - F S, and
+// P = P1 (I + F)^-T = P1 - P1 S^T.  Matrices whose max|E| exceeds the pass's limit take the
+// blocked Cholesky path instead (state bit ST_CHOL2, decided on the device).
+template <typename T>
+__global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, unsigned long long* emax, int64_t r,
+                                                           const int* st, int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    W += bz * r * r;
+    F += bz * r * r;
+    const int64_t total = r * r;
+    double mx = 0.0;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t i = idx / r, k = idx % r;
+        T v = T(0);
+        if (k <= i) {
+            const T e = W[idx] - (i == k ? T(1) : T(0));
+            const double a = fabs((double)e);
+            mx = (a > mx || a != a) ? (a != a ? INFINITY : a) : mx;
+            v = (i == k) ? T(0.5) * e : e;
+        }
+        F[idx] = v;
+    }
+    __shared__ double red[256];
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    // non-negative doubles order like their bit patterns: max via an integer atomic (order-free)
+    if (threadIdx.x == 0) atomicMax(emax + bz, (unsigned long long)__double_as_longlong(red[0]));
+}
+
+__global__ void fill_u64_kernel(unsigned long long* p, int64_t n, unsigned long long v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ void near_id_decide_kernel(const unsigned long long* emax, int* st, int64_t b, int st_mask, int st_val,
+                                      double tau, int bit) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= b || (st[i] & st_mask) != st_val) return;
+    const double e = __longlong_as_double((long long)emax[i]);
+    st[i] = (e <= tau) ? (st[i] & ~bit) : (st[i] | bit);
+}
+
+template <typename T>
+static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, int nit, int nn, double tau,
+                        int fail_bit) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r, b = p.b;
+    constexpr int S = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    T* W = (T*)(c.ws + p.W);
+    T* bufs[3] = {(T*)(c.ws + p.L), (T*)(c.ws + p.Tf), W};
+    unsigned long long* emax = (unsigned long long*)(c.ws + p.emax);
+    int e;
+    if ((e = gram<T>(c, Pin, mask, val))) return e;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, emax, b, 0ull);
+    DION_TRY(hipGetLastError());
+    {
+        dim3 grid(grid_1d(r * r, 16), (unsigned)b);   // few blocks per matrix: one atomic each
+        hipLaunchKernelGGL((near_id_init_kernel<T>), grid, dim3(256), 0, c.s, (const T*)W, bufs[0], emax, r, c.st,
+                           mask, val);
+        DION_TRY(hipGetLastError());
+    }
+    hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const unsigned long long*)emax,
+                       c.st, b, mask, val, tau, (int)ST_CHOL2);
+    DION_TRY(hipGetLastError());
+    const int smask = mask | ST_CHOL2, sval = val;             // near-identity matrices
+    const int64_t rr = r * r * (int64_t)sizeof(T);
+    int fi = 0;                                                // buffer holding F
+    for (int it = 0; it < nit; ++it) {                         // F <- Phi(W - I - F F^T)
+        const int fo = fi ^ 1;
+        GemmArgs g{};
+        g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
+        g.b = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = F[j][k]
+        g.sa0 = g.sb0 = g.sc = rr;
+        g.c = bufs[fo]; g.ldc = r; g.csrc = W; g.phi = 1;
+        g.M = g.N = (int)r; g.K = (int)r;
+        g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 1;
+        g.st = c.st; g.st_mask = smask; g.st_val = sval;
+        DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+        fi = fo;
+    }
+    int si = fi;                                               // buffer holding S (S0 = F)
+    int free_[2], nf = 0;
+    for (int q = 0; q < 3; ++q) if (q != fi) free_[nf++] = q;
+    for (int it = 0; it < nn; ++it) {                          // S <- F - F S
+        const int so = free_[it & 1];
+        GemmArgs g{};
+        g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
+        g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[k][j]
+        g.sa0 = g.sb0 = g.sc = rr;
+        g.c = bufs[so]; g.ldc = r; g.csrc = bufs[fi];
+        g.M = g.N = (int)r; g.K = (int)r;
+        g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 4;
+        g.st = c.st; g.st_mask = smask; g.st_val = sval;
+        DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(g, b, c.s)));
+        si = so;
+    }
+    {                                                          // Pout = Pin - Pin S^T
+        GemmArgs g{};
+        g.a = Operand{Pin, nullptr, r, (int)m, (int)r, vr};        // A(i,k) = Pin[i][k]
+        g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[j][k]
+        g.sa0 = m * r * (int64_t)sizeof(T);
+        g.sb0 = rr;
+        g.c = Pout; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T); g.csrc = Pin;
+        g.M = (int)m; g.N = (int)r; g.K = (int)r;
+        g.alpha = -1; g.beta = 1; g.kskip = 1;
+        g.st = c.st; g.st_mask = smask; g.st_val = sval;
+        DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+    }
+    // the others: a full Cholesky pass (W is untouched for them)
+    const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
+    if ((e = factor<T>(c, cmask, cval, 0.0, fail_bit, 0, 0))) return e;
+    if ((e = invert<T>(c, cmask, cval))) return e;
+    return apply<T>(c, Pin, Pout, cmask, cval);
+}
+
 // P0 = (M + G) Q  and  R = (M + G)^T P for one chain.
 template <typename T, int ASRC>
 static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, const float* Q, T* P, int mask, int val) {
@@ -773,7 +1008,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
                         : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, mask, val))) return e;
         DION_TRY(mark(1));
         if ((e = cholqr_pass<T>(c, P, tmp, mask, val, force32 ? 0.0 : kTau32, fail, ST_PATH64))) return e;
-        if ((e = cholqr_pass<T>(c, tmp, P, mask, val, 0.0, fail, 0))) return e;
+        if ((e = reortho_pass<T>(c, tmp, P, mask, val, 0, 0, kNearId32, fail))) return e;
         DION_TRY(mark(2));
         return g_bf16 ? btp_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, P, R, mask, val)
                       : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, mask, val);
@@ -793,9 +1028,10 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     if ((e = invert<T>(c, A64 | F, A64))) return e;
     if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
     // pass 2
-    if ((e = cholqr_pass<T>(c, Pb, P, A64 | F, A64, 0.0, F, 0))) return e;
+    if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearIdIters64, kNearIdTerms64, kNearId64, F))) return e;
     // pass 3, only after a shifted first pass
-    if ((e = cholqr_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, 0.0, F, 0))) return e;
+    if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearIdIters64, kNearIdTerms64, kNearId64, F)))
+        return e;
     {
         dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
         hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st, A64 | SH | F,
@@ -819,8 +1055,15 @@ static hipError_t launch_update(const Plan& p, const char* ws, float* M, const v
     u.one_minus_mu = 1.0f - mu;
     u.lr_s = (float)((double)lr * sqrt((double)p.m / (double)p.n));
     u.vec = (p.r % 4) == 0;
-    dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
-    hipLaunchKernelGGL((update_kernel<64, 64, GB, XB>), grid, dim3(256), 0, s, u);
+    constexpr int UM = DION_UPD_BM, UN = DION_UPD_BN, UK = DION_UPD_BK;
+    const int64_t big = ((p.m + UM - 1) / UM) * ((p.n + UN - 1) / UN) * p.b;
+    if ((UM != 64 || UN != 64) && p.m >= UM && p.n >= UN && big >= kBigTileMinTiles) {
+        dim3 grid((unsigned)((p.n + UN - 1) / UN), (unsigned)((p.m + UM - 1) / UM), (unsigned)p.b);
+        hipLaunchKernelGGL((update_kernel<UM, UN, UK, GB, XB>), grid, dim3(256), 0, s, u);
+    } else {
+        dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
+        hipLaunchKernelGGL((update_kernel<64, 64, UK, GB, XB>), grid, dim3(256), 0, s, u);
+    }
     return hipGetLastError();
 }
 
@@ -928,9 +1171,10 @@ static hipError_t stream_set(StreamSet** out) {
     return hipSuccess;
 }
 
-static int auto_chunks(const Plan& p) {
-    // two chunks give the overlap; more would shrink the GEMM grids
-    return p.b >= 2 && p.r > 0 ? 2 : 1;
+static int auto_chunks(const Plan&) {
+    // Concurrent chunks start in lockstep, so their latency-bound phases overlap each other
+    // rather than the GEMMs; measured no gain on the 24 x 1024^2 stack.  Off by default.
+    return 1;
 }
 
 int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps, int x_bf16,

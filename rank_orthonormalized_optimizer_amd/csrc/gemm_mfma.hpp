@@ -64,42 +64,33 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// One element at element offset `off`.  For the SUM kinds the two addends are
-// widened to T first, so in double the sum is exact and in float it is rounded once.
-template <typename T, int SRC>
-__device__ __forceinline__ T load1(const void* p0, const void* p1, int64_t off) {
-    if constexpr (SRC == SRC_F32) return (T)((const float*)p0)[off];
-    else if constexpr (SRC == SRC_F64) return (T)((const double*)p0)[off];
-    else if constexpr (SRC == SRC_BF16) return (T)bf16_bits_to_float(((const uint16_t*)p0)[off]);
-    else if constexpr (SRC == SRC_SUM_F32) return (T)((const float*)p0)[off] + (T)((const float*)p1)[off];
-    else return (T)((const float*)p0)[off] + (T)bf16_bits_to_float(((const uint16_t*)p1)[off]);
+// Storage of an operand source: the raw element types read from p0 and p1.
+template <int SRC> struct SrcStorage;
+template <> struct SrcStorage<SRC_F32> { using S0 = float; using S1 = float; static constexpr bool two = false; };
+template <> struct SrcStorage<SRC_F64> { using S0 = double; using S1 = double; static constexpr bool two = false; };
+template <> struct SrcStorage<SRC_BF16> { using S0 = uint16_t; using S1 = uint16_t; static constexpr bool two = false; };
+template <> struct SrcStorage<SRC_SUM_F32> { using S0 = float; using S1 = float; static constexpr bool two = true; };
+template <> struct SrcStorage<SRC_SUM_BF16> { using S0 = float; using S1 = uint16_t; static constexpr bool two = true; };
+
+template <typename T, typename S> __device__ __forceinline__ T widen(S v) { return (T)v; }
+template <> __device__ __forceinline__ float widen<float, uint16_t>(uint16_t v) { return bf16_bits_to_float(v); }
+template <> __device__ __forceinline__ double widen<double, uint16_t>(uint16_t v) {
+    return (double)bf16_bits_to_float(v);
 }
 
-// Four consecutive elements; requires 4-element alignment of `off` and the base.
-template <typename T, int SRC>
-__device__ __forceinline__ void load4(const void* p0, const void* p1, int64_t off, T (&o)[4]) {
-    if constexpr (SRC == SRC_F32) {
-        float4 v = *(const float4*)((const float*)p0 + off);
-        o[0] = (T)v.x; o[1] = (T)v.y; o[2] = (T)v.z; o[3] = (T)v.w;
-    } else if constexpr (SRC == SRC_F64) {
-        double2 a = *(const double2*)((const double*)p0 + off);
-        double2 b = *(const double2*)((const double*)p0 + off + 2);
-        o[0] = (T)a.x; o[1] = (T)a.y; o[2] = (T)b.x; o[3] = (T)b.y;
-    } else if constexpr (SRC == SRC_BF16) {
-        uint2 v = *(const uint2*)((const uint16_t*)p0 + off);
-        o[0] = (T)bf16_bits_to_float(v.x & 0xffffu); o[1] = (T)bf16_bits_to_float(v.x >> 16);
-        o[2] = (T)bf16_bits_to_float(v.y & 0xffffu); o[3] = (T)bf16_bits_to_float(v.y >> 16);
-    } else if constexpr (SRC == SRC_SUM_F32) {
-        float4 a = *(const float4*)((const float*)p0 + off);
-        float4 b = *(const float4*)((const float*)p1 + off);
-        o[0] = (T)a.x + (T)b.x; o[1] = (T)a.y + (T)b.y; o[2] = (T)a.z + (T)b.z; o[3] = (T)a.w + (T)b.w;
+// Four consecutive raw elements; requires 4-element alignment of `off` and of the base.
+template <typename S>
+__device__ __forceinline__ void load4_raw(const void* p, int64_t off, S (&o)[4]) {
+    if constexpr (sizeof(S) == 4) {
+        const float4 v = *(const float4*)((const S*)p + off);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else if constexpr (sizeof(S) == 8) {
+        const double2 a = *(const double2*)((const S*)p + off);
+        const double2 b = *(const double2*)((const S*)p + off + 2);
+        o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
     } else {
-        float4 a = *(const float4*)((const float*)p0 + off);
-        uint2 b = *(const uint2*)((const uint16_t*)p1 + off);
-        o[0] = (T)a.x + (T)bf16_bits_to_float(b.x & 0xffffu);
-        o[1] = (T)a.y + (T)bf16_bits_to_float(b.x >> 16);
-        o[2] = (T)a.z + (T)bf16_bits_to_float(b.y & 0xffffu);
-        o[3] = (T)a.w + (T)bf16_bits_to_float(b.y >> 16);
+        const uint2 v = *(const uint2*)((const S*)p + off);
+        o[0] = (S)(v.x & 0xffffu); o[1] = (S)(v.x >> 16); o[2] = (S)(v.y & 0xffffu); o[3] = (S)(v.y >> 16);
     }
 }
 
@@ -113,13 +104,20 @@ struct Operand {
     bool vec;   // 4-element vector loads are legal (base, ld and stride aligned)
 };
 
-// Register-staged loader of one BX x BK operand tile.
+// Register-staged loader of one BX x BK operand tile.  load() only issues the global
+// loads of the raw storage values; store() widens them to T (adding the two addends of
+// the SUM sources, exactly in double and with one rounding in float) and writes LDS.  So the
+// loads stay in flight across the MFMAs placed between the two calls.
 template <typename T, int BX, int BK, bool KC, int SRC>
 struct TileLoader {
+    using St = SrcStorage<SRC>;
+    using S0 = typename St::S0;
+    using S1 = typename St::S1;
     static constexpr int GROUPS = BX * BK / 4;
     static_assert(GROUPS % 256 == 0, "tile must give every thread whole 4-element groups");
     static constexpr int PER = GROUPS / 256;
-    T r[PER][4];
+    S0 r0[PER][4];
+    S1 r1[St::two ? PER : 1][4];
 
     __device__ __forceinline__ void load(const Operand& op, int x0, int k0) {
 #pragma unroll
@@ -131,16 +129,23 @@ struct TileLoader {
             const int64_t off = KC ? (int64_t)x * op.ld + k : (int64_t)k * op.ld + x;
             const bool full = KC ? (x < op.xext && k + 3 < op.kext) : (k < op.kext && x + 3 < op.xext);
             if (op.vec && full) {
-                load4<T, SRC>(op.p0, op.p1, off, r[g]);
+                load4_raw<S0>(op.p0, off, r0[g]);
+                if constexpr (St::two) load4_raw<S1>(op.p1, off, r1[g]);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int xx = KC ? x : x + v;
                     const int kk = KC ? k + v : k;
-                    r[g][v] = (xx < op.xext && kk < op.kext) ? load1<T, SRC>(op.p0, op.p1, off + v) : T(0);
+                    const bool in = xx < op.xext && kk < op.kext;
+                    r0[g][v] = in ? ((const S0*)op.p0)[off + v] : S0(0);
+                    if constexpr (St::two) r1[g][v] = in ? ((const S1*)op.p1)[off + v] : S1(0);
                 }
             }
         }
+    }
+    __device__ __forceinline__ T value(int g, int v) const {
+        if constexpr (St::two) return widen<T, S0>(r0[g][v]) + widen<T, S1>(r1[g][v]);
+        else return widen<T, S0>(r0[g][v]);
     }
     // LDS tile layout: s[k * LDX + x]
     template <int LDX>
@@ -151,23 +156,25 @@ struct TileLoader {
             if constexpr (KC) {
                 const int x = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[(k + v) * LDX + x] = r[g][v];
+                for (int v = 0; v < 4; ++v) s[(k + v) * LDX + x] = value(g, v);
             } else {
                 const int k = idx / (BX / 4), x = (idx % (BX / 4)) * 4;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[k * LDX + x + v] = r[g][v];
+                for (int v = 0; v < 4; ++v) s[k * LDX + x + v] = value(g, v);
             }
         }
     }
 };
 
-// Tile geometry shared by the kernels.
-template <typename T, int BM_, int BN_>
+// Tile geometry shared by the kernels: BM x BN output tile, K slabs of BK, LDS tiles
+// [k][x] padded by PAD elements per k-row, two LDS stages (double buffering).
+template <typename T, int BM_, int BN_, int BK_ = 16>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 16, PAD = 16;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, PAD = 16;
     static constexpr int LDA = BM + PAD, LDB = BN + PAD;
     static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave sub-tile
     static constexpr int FM = WTM / 16, FN = WTN / 16; // MFMA blocks per wave
+    static constexpr int A_STAGE = BK * LDA, B_STAGE = BK * LDB;
     using acc_t = typename Mfma<T>::acc_t;
 };
 
@@ -187,6 +194,38 @@ __device__ __forceinline__ void mma_slab(const T* As, const T* Bs, typename C::a
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
+    }
+}
+
+// Double-buffered main loop over the K range [kbeg, kend): global loads of slab s+1 are in
+// flight while slab s is multiplied from LDS; one barrier per slab.  `slab_hook(k0, buf)` runs
+// right before each slab's MFMAs (used to stage per-slab side data).
+template <typename T, class C, bool AKC, int ASRC, bool BKC, int BSRC, class Hook>
+__device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int kbeg, int kend,
+                                         T* As, T* Bs, typename C::acc_t (&acc)[C::FM][C::FN], Hook&& hook) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    TileLoader<T, C::BM, C::BK, AKC, ASRC> la;
+    TileLoader<T, C::BN, C::BK, BKC, BSRC> lb;
+    if (kbeg >= kend) return;
+    la.load(A, m0, kbeg);
+    lb.load(B, n0, kbeg);
+    la.template store<C::LDA>(As);
+    lb.template store<C::LDB>(Bs);
+    hook(kbeg, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
+        const bool more = k0 + C::BK < kend;
+        if (more) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
+        mma_slab<T, C>(As + buf * C::A_STAGE, Bs + buf * C::B_STAGE, acc, wm, wn, lane);
+        if (more) {
+            la.template store<C::LDA>(As + (buf ^ 1) * C::A_STAGE);
+            lb.template store<C::LDB>(Bs + (buf ^ 1) * C::B_STAGE);
+            hook(k0 + C::BK, buf ^ 1);
+        }
+        __syncthreads();
+        buf ^= 1;
     }
 }
 
