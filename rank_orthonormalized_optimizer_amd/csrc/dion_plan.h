@@ -57,7 +57,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     {   // split the Gram's long K (= m) until the grid has ~1024 tiles, keeping >= 128 rows per split
         const int64_t nt = (r + 63) / 64;
         const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
-        int64_t s = (1024 + tiles - 1) / tiles;
+        int64_t s = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
         if (s > 16) s = 16;
         if (s > m / 128) s = m / 128;
         while (s > 1 && (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20)) --s;

@@ -45,6 +45,8 @@ def test_workspace_size():
     assert a >= 24 * (1024 * 256 * 12 * 2)
     assert dion.workspace_size(1024, 1024, 24, 128) < a
     assert dion.workspace_size(0, 5, 1, 0) == 0
+    assert dion.workspace_size(64, 96, 2, 0) > 0      # rank 0 is valid (M <- M + G only)
+    assert dion.workspace_size(64, 96, 0, 8) >= 0     # empty stack
     assert dion.workspace_size(4, 5, 1, 5) == 0      # rank > min(m, n)
     assert dion.workspace_size(4, 5, -1, 1) == 0
     assert dion.workspace_size(1 << 45, 1 << 45, 1, 1) == 0
