@@ -473,13 +473,14 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
         for (int kk = 0; kk < BK; kk += 4) {
             float a[C::FM], a2[C::FM], b[C::FN];
             const float ck = Cs[buf][kk + lk];
+            const int sw = lds_swizzle<BK>(kk);   // both operands are KC tiles
 #pragma unroll
             for (int i = 0; i < C::FM; ++i) {
-                a[i] = as[(kk + lk) * C::LDA + wm * C::WTM + i * 16 + lr];
+                a[i] = as[(kk + lk) * C::LDA + ((wm * C::WTM + i * 16 + lr) ^ sw)];
                 a2[i] = a[i] * ck;
             }
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) b[j] = bs[(kk + lk) * C::LDB + wn * C::WTN + j * 16 + lr];
+            for (int j = 0; j < C::FN; ++j) b[j] = bs[(kk + lk) * C::LDB + ((wn * C::WTN + j * 16 + lr) ^ sw)];
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll

@@ -104,6 +104,16 @@ struct Operand {
     bool vec;   // 4-element vector loads are legal (base, ld and stride aligned)
 };
 
+// XOR swizzle of the x index of KC operands in LDS.  A KC tile arrives as four consecutive k
+// per thread, so one wave's store of element v writes 256 / BK consecutive x in each of the
+// BK / 4 k-groups, and with the rows a multiple of 64 banks apart every k-group would land on
+// the same banks.  XORing x with (256 / BK) * (k / 4 mod BK / 4) moves each k-group to its own
+// bank window, while a fragment read (16 consecutive x, 16-aligned, of the four k-rows that
+// share k / 4, hence one swizzle value) still touches 16 distinct x per row.  The swizzle stays
+// below 64, so x keeps its 64-block: tile extents along x must be multiples of 64.
+template <int BK>
+__device__ __forceinline__ int lds_swizzle(int k) { return (256 / BK) * ((k >> 2) & (BK / 4 - 1)); }
+
 // Register-staged loader of one BX x BK operand tile.  load() only issues the global
 // loads of the raw storage values; store() widens them to T (adding the two addends of
 // the SUM sources, exactly in double and with one rounding in float) and writes LDS.  So the
@@ -115,6 +125,7 @@ struct TileLoader {
     using S1 = typename St::S1;
     static constexpr int GROUPS = BX * BK / 4;
     static_assert(GROUPS % 256 == 0, "tile must give every thread whole 4-element groups");
+    static_assert(!KC || (BX % 64 == 0 && BK >= 4 && BK <= 64), "swizzled KC tiles need BX % 64 == 0");
     static constexpr int PER = GROUPS / 256;
     S0 r0[PER][4];
     S1 r1[St::two ? PER : 1][4];
@@ -147,7 +158,7 @@ struct TileLoader {
         if constexpr (St::two) return widen<T, S0>(r0[g][v]) + widen<T, S1>(r1[g][v]);
         else return widen<T, S0>(r0[g][v]);
     }
-    // LDS tile layout: s[k * LDX + x]
+    // LDS tile layout: s[k * LDX + (x ^ lds_swizzle<BK>(k))] (the swizzle only for KC operands)
     template <int LDX>
     __device__ __forceinline__ void store(T* s) const {
 #pragma unroll
@@ -155,8 +166,9 @@ struct TileLoader {
             const int idx = threadIdx.x + g * 256;
             if constexpr (KC) {
                 const int x = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
+                const int xs = x ^ lds_swizzle<BK>(k);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[(k + v) * LDX + x] = value(g, v);
+                for (int v = 0; v < 4; ++v) s[(k + v) * LDX + xs] = value(g, v);
             } else {
                 const int k = idx / (BX / 4), x = (idx % (BX / 4)) * 4;
 #pragma unroll
@@ -179,17 +191,18 @@ struct TileCfg {
 };
 
 // acc[i][j] += A_frag[i] * B_frag[j] over one BK slab of LDS.
-template <typename T, class C>
+template <typename T, class C, bool AKC, bool BKC>
 __device__ __forceinline__ void mma_slab(const T* As, const T* Bs, typename C::acc_t (&acc)[C::FM][C::FN],
                                          int wm, int wn, int lane) {
     const int lr = lane & 15, lk = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < C::BK; kk += 4) {
         T a[C::FM], b[C::FN];
+        const int sa = AKC ? lds_swizzle<C::BK>(kk) : 0, sb = BKC ? lds_swizzle<C::BK>(kk) : 0;
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = As[(kk + lk) * C::LDA + wm * C::WTM + i * 16 + lr];
+        for (int i = 0; i < C::FM; ++i) a[i] = As[(kk + lk) * C::LDA + ((wm * C::WTM + i * 16 + lr) ^ sa)];
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = Bs[(kk + lk) * C::LDB + wn * C::WTN + j * 16 + lr];
+        for (int j = 0; j < C::FN; ++j) b[j] = Bs[(kk + lk) * C::LDB + ((wn * C::WTN + j * 16 + lr) ^ sb)];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -218,7 +231,7 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
     for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
         const bool more = k0 + C::BK < kend;
         if (more) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
-        mma_slab<T, C>(As + buf * C::A_STAGE, Bs + buf * C::B_STAGE, acc, wm, wn, lane);
+        mma_slab<T, C, AKC, BKC>(As + buf * C::A_STAGE, Bs + buf * C::B_STAGE, acc, wm, wn, lane);
         if (more) {
             la.template store<C::LDA>(As + (buf ^ 1) * C::A_STAGE);
             lb.template store<C::LDB>(Bs + (buf ^ 1) * C::B_STAGE);
