@@ -46,6 +46,37 @@ def algorithmic_flops(wl) -> float:
     return tot
 
 
+def kernel_source_hash(root: str) -> str:
+    """sha256 over the kernel and ABI sources the shared library is built from."""
+    import glob
+    import hashlib
+    files = sorted(f for f in glob.glob(os.path.join(root, "rank_orthonormalized_optimizer_amd", "csrc", "*"))
+                   if f.endswith((".hip", ".hpp", ".h", ".cpp")))
+    files.append(os.path.join(root, "include", "dion.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, phase: str):
+    """HBM bytes per launch of the phase's kernel, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary in profiles/traffic.json (already scaled by the copy-kernel calibration), or None
+    when there is none for this kernel or it was taken on other kernel sources."""
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic.json")) as fh:
+            ent = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not ent or ent.get("source_sha256") != kernel_source_hash(root):
+        return None
+    ph = ent.get("phases", {}).get(phase)
+    return None if ph is None else ph["bytes_per_launch"]
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -246,7 +277,7 @@ def main() -> int:
                      "achieved": achieved, "peak": PEAK_TFLOPS[dt_], "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TFLOPS[dt_],
                      "flops_per_launch": flops / launches, "avg_launch_ms": phase_ms[dom] / launches,
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name, dom), "traffic_unit": "bytes/launch"},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

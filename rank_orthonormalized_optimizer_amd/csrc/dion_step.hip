@@ -57,7 +57,7 @@ struct GemmArgs {
     const int* st;             // per-matrix state word; matrix runs iff (st & mask) == val
     int st_mask, st_val;
     int lower;                 // skip tiles strictly above the diagonal
-    int zdiv;                  // blockIdx.z = matrix * zdiv + group (0 or 1: no groups)
+    int zdiv;                  // tile z index = matrix * zdiv + group (0 or 1: no groups)
     int64_t ga0, gb0, gc;      // byte offsets between groups for a.p0, b.p0, c
     int kskip;                 // K range of a tile: 0 all; 1 k < n0 + BN (B = lower^T);
                                // 2 k >= n0 (B lower); 3 k < m0 + BM (A lower); 4 both 2 and 3
@@ -72,9 +72,10 @@ template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int 
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     using C = TileCfg<T, BM, BN, BK>;
     const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
-    const int bz = blockIdx.z / zdiv, grp = blockIdx.z % zdiv;
+    const TileId tid = xcd_tile_id();
+    const int bz = tid.z / zdiv, grp = tid.z % zdiv;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int m0 = tid.y * BM, n0 = tid.x * BN;
     if (g.lower && n0 >= m0 + BM) return;
     int kbeg = 0, kend = g.K;
     if (g.kskip == 1) kend = min(g.K, n0 + BN);
@@ -433,8 +434,9 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
     // Two accumulators share every LDS fragment: acc1 = P R^T and acc2 = P diag(c) R^T, the
     // second from the A fragment scaled by the column scale of its k index.
     using C = TileCfg<float, BM, BN, BK>;
-    const int bz = blockIdx.z;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const TileId tid = xcd_tile_id();
+    const int bz = tid.z;
+    const int m0 = tid.y * BM, n0 = tid.x * BN;
     __shared__ float As[2 * C::A_STAGE];
     __shared__ float Bs[2 * C::B_STAGE];
     __shared__ float Cs[2][BK];

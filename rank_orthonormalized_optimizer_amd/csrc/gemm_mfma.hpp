@@ -104,6 +104,23 @@ struct Operand {
     bool vec;   // 4-element vector loads are legal (base, ld and stride aligned)
 };
 
+// Tile numbering that keeps neighbouring tiles on one XCD.  The dispatcher hands workgroups
+// to the 8 XCDs round-robin by linear id, and each XCD has its own L2, so the tiles that share
+// an operand panel (the column tiles of one row panel, all tiles of one matrix) would otherwise
+// be spread over all eight L2s and fetch the panel eight times.  The linear id L (x fastest)
+// is renumbered so that XCD x processes the contiguous range of tile ids of its share, in
+// order; a bijection on [0, T) for any T.
+struct TileId { int x, y, z; };
+__device__ __forceinline__ TileId xcd_tile_id() {
+    constexpr int64_t NX = 8;
+    const int64_t gx = gridDim.x, gy = gridDim.y;
+    const int64_t T = gx * gy * (int64_t)gridDim.z;
+    const int64_t L = blockIdx.x + gx * (blockIdx.y + gy * (int64_t)blockIdx.z);
+    const int64_t q = T / NX, rem = T % NX, x = L % NX, slot = L / NX;
+    const int64_t t = (x < rem) ? x * (q + 1) + slot : rem * (q + 1) + (x - rem) * q + slot;
+    return TileId{(int)(t % gx), (int)((t / gx) % gy), (int)(t / (gx * gy))};
+}
+
 // XOR swizzle of the x index of KC operands in LDS.  A KC tile arrives as four consecutive k
 // per thread, so one wave's store of element v writes 256 / BK consecutive x in each of the
 // BK / 4 k-groups, and with the rows a multiple of 64 banks apart every k-group would land on
