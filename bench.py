@@ -134,6 +134,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--grads", type=int, default=3, help="distinct resident gradients cycled through")
     ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
+    ap.add_argument("--no-hint", action="store_true",
+                    help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
     ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -176,13 +178,18 @@ def main() -> int:
                            ws=workspace_for(g.m, g.n, g.batch, g.rank, dev)))
     opts = (0 if args.no_sticky else dion.OPT_STICKY_F64) | ((args.chunks & 15) << 8)
     stream = torch.cuda.current_stream(dev)
+    for s in stacks:   # what DionStack does: skip launching the fp32 chain once a stack is all-fp64
+        s["hint"] = None if (args.no_sticky or args.no_hint) else dion.StickyF64Hint(s["flags"])
 
     def one_step(k, events=None):
         for si, s in enumerate(stacks):
             g = s["g"]
+            o = opts if s["hint"] is None else s["hint"].options(opts)
             dion.step_(s["X"], s["G"][k % len(s["G"])], s["M"], s["Q"], g.rank, wl.mu, wl.lr, wl.eps,
-                       workspace=s["ws"], flags=s["flags"], options=opts, stream=stream,
+                       workspace=s["ws"], flags=s["flags"], options=o, stream=stream,
                        events=None if events is None else events[si])
+            if s["hint"] is not None:
+                s["hint"].after_step(stream)
 
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -265,7 +272,8 @@ def main() -> int:
         "config": {"workload": wl.name,
                    "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],
                    "mu": wl.mu, "lr": wl.lr, "eps": wl.eps, "grad": wl.grad,
-                   "sticky_fp64": not args.no_sticky, "chunks": args.chunks or "auto"},
+                   "sticky_fp64": not args.no_sticky,
+                   "host_fp64_hint": not (args.no_sticky or args.no_hint), "chunks": args.chunks or "auto"},
         "effective_param_GBps": eff_gbs,
         "pct_hbm_roofline": 100.0 * eff_gbs / HBM_PEAK_GBS,
         "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,

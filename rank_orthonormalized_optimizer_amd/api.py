@@ -66,6 +66,47 @@ def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | N
         raise _lib.DionError(st)
 
 
+class StickyF64Hint:
+    """Host-side knowledge, gathered without a host sync, that a whole stack is on the fp64 chain.
+
+    Under OPT_STICKY_F64 a matrix whose FLAG_F64 is set skips the fp32 attempt and keeps the
+    flag, so once every flag is set the fp32 chain has no matrix left and OPT_FORCE_F64 gives
+    the same kernels' work and bitwise the same results while not launching the (empty) fp32
+    chain at all.  After each step the flags are copied to pinned host memory; the copy is
+    looked at on a later step, once its event has completed.  Call ``reset()`` after changing
+    the flags tensor by hand.
+    """
+
+    def __init__(self, flags: torch.Tensor):
+        self.flags = flags
+        self.host = torch.zeros(tuple(flags.shape), dtype=torch.int32, pin_memory=True)
+        self.event = None
+        self.all_f64 = False
+
+    def reset(self) -> None:
+        self.event = None
+        self.all_f64 = False
+
+    def options(self, base: int) -> int:
+        if self.all_f64 and (base & _lib.OPT_STICKY_F64) and not (base & _lib.OPT_FORCE_F32):
+            return base | _lib.OPT_FORCE_F64
+        return base
+
+    def after_step(self, stream) -> None:
+        if self.all_f64:
+            return
+        if self.event is not None:
+            if not self.event.query():
+                return                       # the last copy is still in flight: look next step
+            self.all_f64 = bool(((self.host & _lib.FLAG_F64) != 0).all())
+            if self.all_f64:
+                return
+        with torch.cuda.stream(stream):
+            self.host.copy_(self.flags, non_blocking=True)
+            self.event = torch.cuda.Event()
+            self.event.record(stream)
+
+
 class DionStack:
     """Optimizer state (M, Q, flags, workspace) of one stack of same-shape matrices.
 
@@ -90,10 +131,15 @@ class DionStack:
         self.Q = q.to(torch.float32).to(dev).contiguous()
         self.flags = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.workspace = workspace_for(m, n, batch, self.rank, dev)
+        self.hint = StickyF64Hint(self.flags) if sticky else None
 
     def step(self, X: torch.Tensor, G: torch.Tensor) -> None:
+        opts = self.hint.options(self.options) if self.hint is not None else self.options
+        stream = torch.cuda.current_stream(self.flags.device)
         step_(X, G, self.M, self.Q, self.rank, self.mu, self.lr, self.eps, workspace=self.workspace,
-              flags=self.flags, options=self.options)
+              flags=self.flags, options=opts, stream=stream)
+        if self.hint is not None:
+            self.hint.after_step(stream)
 
     @property
     def P(self) -> torch.Tensor:

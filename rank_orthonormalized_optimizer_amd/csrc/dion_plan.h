@@ -18,7 +18,11 @@ enum : int {
     ST_SHIFT = 2,    // the fp64 chain needs the shifted first pass (and a third pass)
     ST_FAIL = 4,     // a factorization broke down with no further fallback
     ST_CHOL2 = 8,    // this re-orthonormalization pass uses the Cholesky path (P^T P far from I)
+    ST_SERIES = 16,  // this re-orthonormalization pass needs the higher-order near-identity series
 };
+
+// Partial sums of squares per matrix written by the near-identity test (fixed-order reduction).
+constexpr int kNearIdParts = 16;
 
 struct Plan {
     int64_t m, n, b, r;
@@ -71,7 +75,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.cs = take(B * r * 8);                // 1 / (||r_j|| + eps), fp64
     q.st = take(B * 4);                    // state words
     q.kap = take(B * 2 * 8);               // running min / max Cholesky diagonal
-    q.emax = take(B * 8);                  // max |P^T P - I| of a re-orthonormalization pass
+    q.emax = take(B * kNearIdParts * 8);   // partial sums of |P^T P - I|^2 of a re-orthonormalization pass
     q.W = take(B * r * r * 8);             // Gram matrix (fp32 or fp64)
     q.L = take(B * r * r * 8);             // Cholesky factor, in place
     q.Td = take(B * q.nblk * kNB * kNB * 8);   // inverses of the diagonal blocks
@@ -83,7 +87,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.gpart = take(q.gsplit > 1 ? B * q.gsplit * r * r * 8 : 0);   // Gram partials
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
-    q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = 8;
+    q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = kNearIdParts * 8;
     q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
     q.sgpart = q.gsplit > 1 ? (size_t)(q.gsplit * r * r * 8) : 0;

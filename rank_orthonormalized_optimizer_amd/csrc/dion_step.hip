@@ -37,10 +37,12 @@ namespace dion {
 // Diagonal-ratio thresholds of the first Cholesky pass (see the header comment).
 constexpr double kTau32 = 64.0;
 constexpr double kTau64 = 1.0e7;
-// Re-orthonormalization passes: largest max|P^T P - I| handled by the near-identity series, and
-// the series lengths.  fp32: F = Phi(E), S = F (error ~ E^2 <= 1e-8, below fp32 rounding).
-// fp64: two fixed-point steps (error ~ E^2 (2E)^2 <= 4e-12) and S up to F^3 (error E^4 <= 1e-12).
+// Re-orthonormalization passes, by eps = ||P^T P - I||_F.  fp32: F = Phi(E), S = F up to
+// eps = 1e-4 (error ~ eps^2 <= 1e-8, below fp32 rounding).  fp64: the same first-order form up to
+// eps = 3e-7 (error ~ eps^2 <= 1e-13); up to 1e-3 two fixed-point steps (error eps^2 (2 eps)^2
+// <= 4e-12) and S up to F^3 (truncation eps^4 <= 1e-12); beyond, the Cholesky pass.
 constexpr double kNearId32 = 1.0e-4;
+constexpr double kNearIdFast64 = 3.0e-7;
 constexpr double kNearId64 = 1.0e-3;
 constexpr int kNearIdIters64 = 2, kNearIdTerms64 = 2;
 
@@ -833,120 +835,137 @@ static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int v
 // Re-orthonormalization of a nearly orthonormal P1 (the second CholeskyQR pass) without a
 // sequential factorization.  With W = P1^T P1 = I + E and chol(W) = I + F, F lower triangular,
 // F + F^T + F F^T = E, i.e. F = Phi(E - F F^T) where Phi keeps the strictly lower part and half
-// the diagonal.  Starting from F = Phi(E), each fixed-point step shrinks the error by ~2 max|E|.
-// Then (I + F)^-1 = I - S with S = F - F^2 + F^3 - ..., evaluated as S <- F - F S, and
-// P = P1 (I + F)^-T = P1 - P1 S^T.  Matrices whose max|E| exceeds the pass's limit take the
-// blocked Cholesky path instead (state bit ST_CHOL2, decided on the device).
+// the diagonal.  Then (I + F)^-1 = I - S with S = F - F^2 + F^3 - ..., and
+// P = P1 (I + F)^-T = P1 - P1 S^T.  With eps = ||E||_F (>= ||E||_2, >= ||F||_2 up to O(eps^2)):
+//   eps <= tau_fast:            F = Phi(E), S = F; error O(eps^2)
+//   tau_fast < eps <= tau_chol: nit fixed-point steps F <- Phi(E - F F^T) (error eps^2 (2 eps)^nit)
+//                               and S <- F - F S nn times (truncation eps^(nn + 2))  [ST_SERIES]
+//   eps > tau_chol (or not finite): the blocked Cholesky pass                        [ST_CHOL2]
+// all decided per matrix on the device.
 template <typename T>
-__global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, unsigned long long* emax, int64_t r,
+__global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, double* part, int64_t r,
                                                            const int* st, int st_mask, int st_val) {
     const int bz = blockIdx.y;
     if ((st[bz] & st_mask) != st_val) return;
     W += bz * r * r;
     F += bz * r * r;
     const int64_t total = r * r;
-    double mx = 0.0;
+    double ss = 0.0;   // sum of squares of E over the full symmetric matrix
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
         const int64_t i = idx / r, k = idx % r;
         T v = T(0);
         if (k <= i) {
             const T e = W[idx] - (i == k ? T(1) : T(0));
-            const double a = fabs((double)e);
-            mx = (a > mx || a != a) ? (a != a ? INFINITY : a) : mx;
+            const double d = (double)e;
+            ss += (i == k ? 1.0 : 2.0) * d * d;
             v = (i == k) ? T(0.5) * e : e;
         }
         F[idx] = v;
     }
     __shared__ double red[256];
-    red[threadIdx.x] = mx;
+    red[threadIdx.x] = ss;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    // non-negative doubles order like their bit patterns: max via an integer atomic (order-free)
-    if (threadIdx.x == 0) atomicMax(emax + bz, (unsigned long long)__double_as_longlong(red[0]));
+    if (threadIdx.x == 0) part[(int64_t)bz * kNearIdParts + blockIdx.x] = red[0];
 }
 
-__global__ void fill_u64_kernel(unsigned long long* p, int64_t n, unsigned long long v) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
-__global__ void near_id_decide_kernel(const unsigned long long* emax, int* st, int64_t b, int st_mask, int st_val,
-                                      double tau, int bit) {
+__global__ void near_id_decide_kernel(const double* part, int nparts, int* st, int64_t b, int st_mask, int st_val,
+                                      double tau_fast, double tau_chol) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= b || (st[i] & st_mask) != st_val) return;
-    const double e = __longlong_as_double((long long)emax[i]);
-    st[i] = (e <= tau) ? (st[i] & ~bit) : (st[i] | bit);
+    double ss = 0.0;
+    for (int q = 0; q < nparts; ++q) ss += part[i * kNearIdParts + q];
+    const double e = sqrt(ss);
+    int s = st[i] & ~(ST_CHOL2 | ST_SERIES);
+    if (!(e <= tau_chol)) s |= ST_CHOL2;            // also NaN / Inf
+    else if (e > tau_fast) s |= ST_SERIES;
+    st[i] = s;
+}
+
+// Pout = Pin - Pin S^T for the matrices selected by (mask, val).
+template <typename T>
+static int near_id_apply(const ChainCtx& c, const T* Pin, T* Pout, const T* S, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r;
+    constexpr int SR = SrcOf<T>::v;
+    const bool vr = (r % 4) == 0;
+    GemmArgs g{};
+    g.a = Operand{Pin, nullptr, r, (int)m, (int)r, vr};   // A(i,k) = Pin[i][k]
+    g.b = Operand{S, nullptr, r, (int)r, (int)r, vr};     // B(k,j) = S[j][k]
+    g.sa0 = m * r * (int64_t)sizeof(T);
+    g.sb0 = r * r * (int64_t)sizeof(T);
+    g.c = Pout; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T); g.csrc = Pin;
+    g.M = (int)m; g.N = (int)r; g.K = (int)r;
+    g.alpha = -1; g.beta = 1; g.kskip = 1;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    DION_TRY((launch_gemm<T, 64, 64, true, SR, true, SR>(g, p.b, c.s)));
+    return 0;
 }
 
 template <typename T>
-static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, int nit, int nn, double tau,
-                        int fail_bit) {
+static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, int nit, int nn, double tau_fast,
+                        double tau_chol, int fail_bit) {
     const Plan& p = *c.p;
-    const int64_t m = p.m, r = p.r, b = p.b;
+    const int64_t r = p.r, b = p.b;
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
+    const bool series = nit + nn > 0;
+    if (!series) tau_fast = tau_chol;
     T* W = (T*)(c.ws + p.W);
     T* bufs[3] = {(T*)(c.ws + p.L), (T*)(c.ws + p.Tf), W};
-    unsigned long long* emax = (unsigned long long*)(c.ws + p.emax);
+    double* part = (double*)(c.ws + p.emax);
     int e;
     if ((e = gram<T>(c, Pin, mask, val))) return e;
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, emax, b, 0ull);
-    DION_TRY(hipGetLastError());
+    const unsigned nparts = grid_1d(r * r, kNearIdParts);
     {
-        dim3 grid(grid_1d(r * r, 16), (unsigned)b);   // few blocks per matrix: one atomic each
-        hipLaunchKernelGGL((near_id_init_kernel<T>), grid, dim3(256), 0, c.s, (const T*)W, bufs[0], emax, r, c.st,
+        dim3 grid(nparts, (unsigned)b);
+        hipLaunchKernelGGL((near_id_init_kernel<T>), grid, dim3(256), 0, c.s, (const T*)W, bufs[0], part, r, c.st,
                            mask, val);
         DION_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const unsigned long long*)emax,
-                       c.st, b, mask, val, tau, (int)ST_CHOL2);
+    hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part, (int)nparts,
+                       c.st, b, mask, val, tau_fast, tau_chol);
     DION_TRY(hipGetLastError());
-    const int smask = mask | ST_CHOL2, sval = val;             // near-identity matrices
-    const int64_t rr = r * r * (int64_t)sizeof(T);
-    int fi = 0;                                                // buffer holding F
-    for (int it = 0; it < nit; ++it) {                         // F <- Phi(W - I - F F^T)
-        const int fo = fi ^ 1;
-        GemmArgs g{};
-        g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
-        g.b = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = F[j][k]
-        g.sa0 = g.sb0 = g.sc = rr;
-        g.c = bufs[fo]; g.ldc = r; g.csrc = W; g.phi = 1;
-        g.M = g.N = (int)r; g.K = (int)r;
-        g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 1;
-        g.st = c.st; g.st_mask = smask; g.st_val = sval;
-        DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
-        fi = fo;
-    }
-    int si = fi;                                               // buffer holding S (S0 = F)
-    int free_[2], nf = 0;
-    for (int q = 0; q < 3; ++q) if (q != fi) free_[nf++] = q;
-    for (int it = 0; it < nn; ++it) {                          // S <- F - F S
-        const int so = free_[it & 1];
-        GemmArgs g{};
-        g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
-        g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[k][j]
-        g.sa0 = g.sb0 = g.sc = rr;
-        g.c = bufs[so]; g.ldc = r; g.csrc = bufs[fi];
-        g.M = g.N = (int)r; g.K = (int)r;
-        g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 4;
-        g.st = c.st; g.st_mask = smask; g.st_val = sval;
-        DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(g, b, c.s)));
-        si = so;
-    }
-    {                                                          // Pout = Pin - Pin S^T
-        GemmArgs g{};
-        g.a = Operand{Pin, nullptr, r, (int)m, (int)r, vr};        // A(i,k) = Pin[i][k]
-        g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[j][k]
-        g.sa0 = m * r * (int64_t)sizeof(T);
-        g.sb0 = rr;
-        g.c = Pout; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T); g.csrc = Pin;
-        g.M = (int)m; g.N = (int)r; g.K = (int)r;
-        g.alpha = -1; g.beta = 1; g.kskip = 1;
-        g.st = c.st; g.st_mask = smask; g.st_val = sval;
-        DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+    const int nmask = mask | ST_CHOL2 | ST_SERIES;
+    // first-order matrices: S = F = Phi(E)
+    if ((e = near_id_apply<T>(c, Pin, Pout, bufs[0], nmask, val))) return e;
+    if (series) {
+        const int smask = nmask, sval = val | ST_SERIES;
+        const int64_t rr = r * r * (int64_t)sizeof(T);
+        int fi = 0;                                                // buffer holding F
+        for (int it = 0; it < nit; ++it) {                         // F <- Phi(W - I - F F^T)
+            const int fo = fi ^ 1;
+            GemmArgs g{};
+            g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
+            g.b = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = F[j][k]
+            g.sa0 = g.sb0 = g.sc = rr;
+            g.c = bufs[fo]; g.ldc = r; g.csrc = W; g.phi = 1;
+            g.M = g.N = (int)r; g.K = (int)r;
+            g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 1;
+            g.st = c.st; g.st_mask = smask; g.st_val = sval;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+            fi = fo;
+        }
+        int si = fi;                                               // buffer holding S (S0 = F)
+        int free_[2], nf = 0;
+        for (int q = 0; q < 3; ++q) if (q != fi) free_[nf++] = q;
+        for (int it = 0; it < nn; ++it) {                          // S <- F - F S
+            const int so = free_[it & 1];
+            GemmArgs g{};
+            g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
+            g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[k][j]
+            g.sa0 = g.sb0 = g.sc = rr;
+            g.c = bufs[so]; g.ldc = r; g.csrc = bufs[fi];
+            g.M = g.N = (int)r; g.K = (int)r;
+            g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 4;
+            g.st = c.st; g.st_mask = smask; g.st_val = sval;
+            DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(g, b, c.s)));
+            si = so;
+        }
+        if ((e = near_id_apply<T>(c, Pin, Pout, bufs[si], smask, sval))) return e;
     }
     // the others: a full Cholesky pass (W is untouched for them)
     const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
@@ -1011,7 +1030,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
                         : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, mask, val))) return e;
         DION_TRY(mark(1));
         if ((e = cholqr_pass<T>(c, P, tmp, mask, val, force32 ? 0.0 : kTau32, fail, ST_PATH64))) return e;
-        if ((e = reortho_pass<T>(c, tmp, P, mask, val, 0, 0, kNearId32, fail))) return e;
+        if ((e = reortho_pass<T>(c, tmp, P, mask, val, 0, 0, kNearId32, kNearId32, fail))) return e;
         DION_TRY(mark(2));
         return g_bf16 ? btp_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, P, R, mask, val)
                       : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, mask, val);
@@ -1031,9 +1050,11 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     if ((e = invert<T>(c, A64 | F, A64))) return e;
     if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
     // pass 2
-    if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearIdIters64, kNearIdTerms64, kNearId64, F))) return e;
+    if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearIdIters64, kNearIdTerms64, kNearIdFast64, kNearId64, F)))
+        return e;
     // pass 3, only after a shifted first pass
-    if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearIdIters64, kNearIdTerms64, kNearId64, F)))
+    if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearIdIters64, kNearIdTerms64, kNearIdFast64, kNearId64,
+                             F)))
         return e;
     {
         dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);

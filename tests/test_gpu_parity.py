@@ -109,3 +109,61 @@ def test_chunking_is_bitwise_invariant(cuda):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("decades", [3.0, 5.0])
+def test_near_identity_regimes(cuda, decades):
+    """The fp64 second pass in each of its regimes, picked on the device by ||P^T P - I||_F after
+    the first pass.  At step 1 (fp64 CholeskyQR of P0 on the host): with 3 decades of spectrum
+    both matrices end below 3e-7 (first-order form); with 5 decades one ends at 8e-5 (fixed-point
+    and Neumann series) and the other at 2e-3 (blocked Cholesky)."""
+    import dataclasses
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = dataclasses.replace(W.SMALL[5], grad_args={"decades": decades}, name=f"regimes-{decades:g}")
+    # the regimes above, recomputed here so the test states what it covers
+    X, M, Q = W.make_state(wl, 0)
+    G = W.make_grad(wl, 0, 1)
+    eps = []
+    for i in range(wl.groups[0].batch):
+        P0 = G[i].astype(np.float64) @ Q[i].astype(np.float64)
+        L = np.linalg.cholesky(P0.T @ P0)
+        P1 = np.linalg.solve(L, P0.T).T
+        eps.append(np.linalg.norm(P1.T @ P1 - np.eye(P1.shape[1])))
+    print("[regimes] eps after first pass", eps, flush=True)
+    if decades == 3.0:
+        assert max(eps) < 3e-7
+    else:
+        assert min(eps) < 1e-3 < max(eps) and min(eps) > 3e-7
+    rep = run_teacher_forced(wl, cuda, options=dion.OPT_FORCE_F64, steps=2)
+    check(rep, tol_for(wl))
+
+
+def test_sticky_hint_is_bitwise_neutral(cuda):
+    """Skipping the fp32 chain once every flag is fp64 (StickyF64Hint) changes no bit."""
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.SMALL[2]
+    g = wl.groups[0]
+    X, M, Q = W.make_state(wl, 0)
+    runs = []
+    for use_hint in (False, True):
+        Xd, Md, Qd = to_torch(X, cuda), to_torch(M, cuda), to_torch(Q, cuda)
+        flags = torch.zeros(g.batch, dtype=torch.int32, device=cuda)
+        hint = dion.StickyF64Hint(flags) if use_hint else None
+        stream = torch.cuda.current_stream(cuda)
+        seq = []
+        for t in range(1, 6):
+            Gd = to_torch(W.make_grad(wl, 0, 1 + (t - 1) % 3), cuda)
+            opts = dion.OPT_STICKY_F64 if hint is None else hint.options(dion.OPT_STICKY_F64)
+            dion.step_(Xd, Gd, Md, Qd, g.rank, wl.mu, wl.lr, wl.eps, flags=flags, options=opts, stream=stream)
+            if hint is not None:
+                hint.after_step(stream)
+            torch.cuda.synchronize()
+            seq.append((to_numpy(Xd), to_numpy(Md), to_numpy(Qd), to_numpy(flags), opts))
+        runs.append(seq)
+        if hint is not None:
+            assert hint.all_f64, "the hint never saw an all-fp64 stack"
+    assert any(o[4] & dion.OPT_FORCE_F64 for o in runs[1]), "the hint never engaged"
+    for a, b in zip(runs[0], runs[1]):
+        for x, y in zip(a[:4], b[:4]):
+            assert np.array_equal(x, y)
