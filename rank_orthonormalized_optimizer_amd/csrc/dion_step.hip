@@ -31,6 +31,7 @@
 #include "dion.h"
 #include "dion_plan.h"
 #include "gemm_mfma.hpp"
+#include "bf16x6.hpp"
 
 namespace dion {
 
@@ -112,6 +113,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     T* Cp = (T*)((char*)g.c + bz * g.sc + grp * g.gc);
     const T* Sp = g.csrc ? (const T*)((const char*)g.csrc + bz * g.sc + grp * g.gc) : Cp;
     const T alpha = (T)g.alpha, beta = (T)g.beta;
+    const bool need_src = g.phi || beta != T(0);
+    // all source loads of the tile before the first store (see the update kernel's epilogue)
+    T sv[C::FM][C::FN][4];
+    if (need_src) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = m0 + wm * C::WTM + i * 16 + Mfma<T>::row(lane, v);
+                    const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
+                    sv[i][j][v] = (row < g.M && col < g.N) ? Sp[(int64_t)row * g.ldc + col] : T(0);
+                }
+    }
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -121,15 +137,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                 const int row = m0 + wm * C::WTM + i * 16 + Mfma<T>::row(lane, v);
                 const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
                 if (row < g.M && col < g.N) {
-                    const int64_t off = (int64_t)row * g.ldc + col;
                     T val = alpha * acc[i][j][v];
                     if (g.phi) {
-                        val += Sp[off] - (row == col ? T(1) : T(0));
+                        val += sv[i][j][v] - (row == col ? T(1) : T(0));
                         val = row > col ? val : (row == col ? T(0.5) * val : T(0));
                     } else if (beta != T(0)) {
-                        val += beta * Sp[off];
+                        val += beta * sv[i][j][v];
                     }
-                    Cp[off] = val;
+                    Cp[(int64_t)row * g.ldc + col] = val;
                 }
             }
 }
@@ -166,16 +181,11 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, int64_t batch, hipStream_t
 #ifndef DION_BIG_MIN_TILES
 #define DION_BIG_MIN_TILES 256
 #endif
-#ifndef DION_UPD_BM
-#define DION_UPD_BM 64
-#endif
-#ifndef DION_UPD_BN
-#define DION_UPD_BN 64
-#endif
-#ifndef DION_UPD_BK
-#define DION_UPD_BK 16
-#endif
 constexpr int kBigTileMinTiles = DION_BIG_MIN_TILES;
+#ifndef DION_UPD_BIG_MIN_TILES
+#define DION_UPD_BIG_MIN_TILES 256
+#endif
+constexpr int kUpdBigMinTiles = DION_UPD_BIG_MIN_TILES;
 
 template <typename T, int BM, int BN, bool AKC, int ASRC, bool BKC, int BSRC>
 static hipError_t launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t s) {
@@ -393,140 +403,192 @@ __global__ __launch_bounds__(256) void colscale_kernel(const double* part, doubl
     cs[bz * r + col] = 1.0 / (sqrt(s) + eps);
 }
 
-// Q <- R * c (fp32), and for fp64-chain matrices R32 <- R64 rounded.
+// Q <- R * c (fp32), for fp64-chain matrices R32 <- R64 rounded, and the bf16 split planes of
+// R32 and Q (k padded to kp with zeros) for the weight pass.
 __global__ __launch_bounds__(256) void next_q_kernel(const double* R64, float* R32, const double* cs, float* Q,
-                                                     int64_t n, int64_t r, const int* st) {
+                                                     uint16_t* Rp, uint16_t* Qp, int64_t n, int64_t r, int64_t kp,
+                                                     const int* st) {
     const int bz = blockIdx.y;
     const bool p64 = (st[bz] & ST_PATH64) != 0;
-    const int64_t total = n * r;
+    const int64_t nr = n * r, total = n * kp;
+    uint16_t* rp = Rp + bz * 3 * total;
+    uint16_t* qp = Qp + bz * 3 * total;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int64_t k = idx % r;
-        const double c = cs[bz * r + k];
-        double v;
-        if (p64) {
-            v = R64[bz * total + idx];
-            R32[bz * total + idx] = (float)v;
-        } else {
-            v = (double)R32[bz * total + idx];
+        const int64_t i = idx / kp, k = idx % kp;
+        float rv = 0.f, qv = 0.f;
+        if (k < r) {
+            const int64_t o = bz * nr + i * r + k;
+            const double c = cs[bz * r + k];
+            double v;
+            if (p64) {
+                v = R64[o];
+                rv = (float)v;
+                R32[o] = rv;
+            } else {
+                rv = R32[o];
+                v = (double)rv;
+            }
+            qv = (float)(v * c);
+            Q[o] = qv;
         }
-        Q[bz * total + idx] = (float)(v * c);
+        split3(rv, rp[idx], rp[total + idx], rp[2 * total + idx]);
+        split3(qv, qp[idx], qp[total + idx], qp[2 * total + idx]);
     }
 }
 
-__global__ __launch_bounds__(256) void round_p_kernel(const double* P64, float* P32, int64_t total, const int* st) {
+// P32 <- P64 rounded for fp64-chain matrices, and the bf16 split planes of P32 for all.
+__global__ __launch_bounds__(256) void split_p_kernel(const double* P64, float* P32, uint16_t* Pp, int64_t m,
+                                                      int64_t r, int64_t kp, const int* st) {
     const int bz = blockIdx.y;
-    if (!(st[bz] & ST_PATH64)) return;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256)
-        P32[bz * total + idx] = (float)P64[bz * total + idx];
+    const bool p64 = (st[bz] & ST_PATH64) != 0;
+    const int64_t mr = m * r, total = m * kp;
+    uint16_t* pp = Pp + bz * 3 * total;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        const int64_t i = idx / kp, k = idx % kp;
+        float v = 0.f;
+        if (k < r) {
+            const int64_t o = bz * mr + i * r + k;
+            if (p64) {
+                v = (float)P64[o];
+                P32[o] = v;
+            } else {
+                v = P32[o];
+            }
+        }
+        split3(v, pp[idx], pp[total + idx], pp[2 * total + idx]);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// momentum / weight pass:  M <- (M + G) - (1 - mu) P R^T,  X <- X - lr s P diag(c) R^T
+// momentum / weight pass:  M <- (M + G) - (1 - mu) P R^T,  X <- X - lr s P Q^T
 // ---------------------------------------------------------------------------
 struct UpdArgs {
-    const float* P; const float* R; const double* cs;
+    const uint16_t* Pp; const uint16_t* Rp; const uint16_t* Qp;   // split planes [b][3][rows][kp]
     float* M; const void* G; void* X;
-    int m, n, r;
+    int m, n, kp;
     float one_minus_mu, lr_s;
-    int vec;   // r % 4 == 0
 };
 
-template <int BM, int BN, int BK, bool G_BF16, bool X_BF16>
-__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
-    // Two accumulators share every LDS fragment: acc1 = P R^T and acc2 = P diag(c) R^T, the
-    // second from the A fragment scaled by the column scale of its k index.
-    using C = TileCfg<float, BM, BN, BK>;
+// One BM x BN tile of M and X per workgroup of WGM x WGN waves: both rank-kp products on the
+// bf16 matrix cores in the six-term split form (fp32 accuracy), sharing the P fragments, then
+// one pass over the tile of M, G and X.  Nine part tiles (P, R, Q x h, m, l) per 32-k slab,
+// double-buffered in LDS; each thread stages one 16-byte chunk of each.
+template <int BM, int BN, int WGM, int WGN, bool G_BF16, bool X_BF16>
+__global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
+    constexpr int NT = WGM * WGN * 64, BK = kSplitK;
+    constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
+    static_assert(BM * 4 == NT && BN * 4 == NT, "one staged chunk per thread and part tile");
+    static_assert(FM * WGM * 16 == BM && FN * WGN * 16 == BN, "whole MFMA blocks per wave");
     const TileId tid = xcd_tile_id();
-    const int bz = tid.z;
-    const int m0 = tid.y * BM, n0 = tid.x * BN;
-    __shared__ float As[2 * C::A_STAGE];
-    __shared__ float Bs[2 * C::B_STAGE];
-    __shared__ float Cs[2][BK];
-    const int64_t mr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r, mn = (int64_t)u.m * u.n;
-    Operand A{u.P + bz * mr, nullptr, u.r, u.m, u.r, u.vec != 0};
-    Operand B{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec != 0};
-    const double* cs = u.cs + (int64_t)bz * u.r;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 15, lk = lane >> 4;
-    typename C::acc_t acc1[C::FM][C::FN], acc2[C::FM][C::FN];
+    const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
+    __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][3][BM * BK];   // P h m l
+    __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][6][BN * BK];   // R h m l | Q h m l
+    const int64_t ps = (int64_t)u.m * u.kp, ns = (int64_t)u.n * u.kp;
+    const uint16_t* srcP = u.Pp + (int64_t)bz * 3 * ps;
+    const uint16_t* srcR = u.Rp + (int64_t)bz * 3 * ns;
+    const uint16_t* srcQ = u.Qp + (int64_t)bz * 3 * ns;
+    const int t = threadIdx.x, lx = t >> 2, lc = t & 3;        // staging: row lx, 16-byte chunk lc
+    const bool okA = m0 + lx < u.m, okB = n0 + lx < u.n;
+    const int64_t gA = (int64_t)(okA ? m0 + lx : 0) * u.kp + 8 * lc;
+    const int64_t gB = (int64_t)(okB ? n0 + lx : 0) * u.kp + 8 * lc;
+    const int so = part_off(lx, lc);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    u32x4 stg[9];
+    auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
-
-    TileLoader<float, BM, BK, true, SRC_F32> la;
-    TileLoader<float, BN, BK, true, SRC_F32> lb;
-    auto stage_c = [&](int k0, int buf) {
-        if (threadIdx.x < BK) Cs[buf][threadIdx.x] = (k0 + (int)threadIdx.x < u.r) ? (float)cs[k0 + threadIdx.x] : 0.f;
+        for (int q = 0; q < 3; ++q) {
+            stg[q] = okA ? *(const u32x4*)(srcP + q * ps + gA + k0) : z;
+            stg[3 + q] = okB ? *(const u32x4*)(srcR + q * ns + gB + k0) : z;
+            stg[6 + q] = okB ? *(const u32x4*)(srcQ + q * ns + gB + k0) : z;
+        }
     };
-    la.load(A, m0, 0);
-    lb.load(B, n0, 0);
-    la.template store<C::LDA>(As);
-    lb.template store<C::LDB>(Bs);
-    stage_c(0, 0);
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *(u32x4*)&ldsA[buf][q][so] = stg[q];
+#pragma unroll
+        for (int q = 0; q < 6; ++q) *(u32x4*)&ldsB[buf][q][so] = stg[3 + q];
+    };
+
+    const int lane = t & 63, wave = t >> 6, wm = wave / WGN, wn = wave % WGN;
+    const int fr = lane & 15, fc = lane >> 4;
+    int ao[FM], bo[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ao[i] = part_off(wm * FM * 16 + i * 16 + fr, fc);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bo[j] = part_off(wn * FN * 16 + j * 16 + fr, fc);
+    f32x4 acc1[FM][FN], acc2[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
+
+    gload(0);
+    lstore(0);
     __syncthreads();
     int buf = 0;
-    for (int k0 = 0; k0 < u.r; k0 += BK) {
-        const bool more = k0 + BK < u.r;
-        if (more) { la.load(A, m0, k0 + BK); lb.load(B, n0, k0 + BK); }
-        const float* as = As + buf * C::A_STAGE;
-        const float* bs = Bs + buf * C::B_STAGE;
+    for (int k0 = 0; k0 < u.kp; k0 += BK) {
+        const bool more = k0 + BK < u.kp;
+        if (more) gload(k0 + BK);
+        u32x4 a[FM][3], b[FN][3], c[FN][3];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            float a[C::FM], a2[C::FM], b[C::FN];
-            const float ck = Cs[buf][kk + lk];
-            const int sw = lds_swizzle<BK>(kk);   // both operands are KC tiles
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i) {
-                a[i] = as[(kk + lk) * C::LDA + ((wm * C::WTM + i * 16 + lr) ^ sw)];
-                a2[i] = a[i] * ck;
+            for (int q = 0; q < 3; ++q) a[i][q] = *(const u32x4*)&ldsA[buf][q][ao[i]];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                b[j][q] = *(const u32x4*)&ldsB[buf][q][bo[j]];
+                c[j][q] = *(const u32x4*)&ldsB[buf][3 + q][bo[j]];
             }
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) b[j] = bs[(kk + lk) * C::LDB + ((wn * C::WTN + j * 16 + lr) ^ sw)];
+        for (int term = 0; term < 6; ++term)
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::FN; ++j) {
-                    acc1[i][j] = Mfma<float>::mma(a[i], b[j], acc1[i][j]);
-                    acc2[i][j] = Mfma<float>::mma(a2[i], b[j], acc2[i][j]);
+                for (int j = 0; j < FN; ++j) {
+                    acc1[i][j] = mma_bf16(a[i][kTermA[term]], b[j][kTermB[term]], acc1[i][j]);
+                    acc2[i][j] = mma_bf16(a[i][kTermA[term]], c[j][kTermB[term]], acc2[i][j]);
                 }
-        }
-        if (more) {
-            la.template store<C::LDA>(As + (buf ^ 1) * C::A_STAGE);
-            lb.template store<C::LDB>(Bs + (buf ^ 1) * C::B_STAGE);
-            stage_c(k0 + BK, buf ^ 1);
-        }
+        if (more) lstore(buf ^ 1);
         __syncthreads();
         buf ^= 1;
     }
 
+    // Epilogue: every load of the tile is issued before the first store (a store may alias a
+    // later load, so interleaving them would serialize one memory round trip per element).
+    const int64_t mn = (int64_t)u.m * u.n;
     float* Mp = u.M + bz * mn;
+    float mv[FM][FN][4], gv[FM][FN][4], xv[FM][FN][4];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm * C::WTM + i * 16 + Mfma<float>::row(lane, v);
-                const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
-                if (row < u.m && col < u.n) {
-                    const int64_t off = bz * mn + (int64_t)row * u.n + col;
-                    float g;
-                    if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
-                    else g = ((const float*)u.G)[off];
-                    const float bv = Mp[off - bz * mn] + g;
-                    Mp[off - bz * mn] = bv - u.one_minus_mu * acc1[i][j][v];
-                    if constexpr (X_BF16) {
-                        uint16_t* X = (uint16_t*)u.X;
-                        const float xv = bf16_bits_to_float(X[off]);
-                        X[off] = float_to_bf16_bits(xv - u.lr_s * acc2[i][j][v]);
-                    } else {
-                        float* X = (float*)u.X;
-                        X[off] = X[off] - u.lr_s * acc2[i][j][v];
-                    }
-                }
+                const int row = m0 + wm * FM * 16 + i * 16 + 4 * fc + v;
+                const int col = n0 + wn * FN * 16 + j * 16 + fr;
+                const int64_t l = (row < u.m && col < u.n) ? (int64_t)row * u.n + col : 0, off = bz * mn + l;
+                mv[i][j][v] = Mp[l];
+                if constexpr (G_BF16) gv[i][j][v] = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
+                else gv[i][j][v] = ((const float*)u.G)[off];
+                if constexpr (X_BF16) xv[i][j][v] = bf16_bits_to_float(((const uint16_t*)u.X)[off]);
+                else xv[i][j][v] = ((const float*)u.X)[off];
+            }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm * FM * 16 + i * 16 + 4 * fc + v;
+                const int col = n0 + wn * FN * 16 + j * 16 + fr;
+                if (row >= u.m || col >= u.n) continue;
+                const int64_t l = (int64_t)row * u.n + col, off = bz * mn + l;
+                Mp[l] = (mv[i][j][v] + gv[i][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                const float x = xv[i][j][v] - u.lr_s * acc2[i][j][v];
+                if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(x);
+                else ((float*)u.X)[off] = x;
             }
 }
 
@@ -1071,22 +1133,21 @@ template <bool GB, bool XB>
 static hipError_t launch_update(const Plan& p, const char* ws, float* M, const void* G, void* X, float mu,
                                 float lr, hipStream_t s) {
     UpdArgs u{};
-    u.P = (const float*)(ws + p.P32);
-    u.R = (const float*)(ws + p.R32);
-    u.cs = (const double*)(ws + p.cs);
+    u.Pp = (const uint16_t*)(ws + p.Pp);
+    u.Rp = (const uint16_t*)(ws + p.Rp);
+    u.Qp = (const uint16_t*)(ws + p.Qp);
     u.M = M; u.G = G; u.X = X;
-    u.m = (int)p.m; u.n = (int)p.n; u.r = (int)p.r;
+    u.m = (int)p.m; u.n = (int)p.n; u.kp = (int)p.kp;
     u.one_minus_mu = 1.0f - mu;
     u.lr_s = (float)((double)lr * sqrt((double)p.m / (double)p.n));
-    u.vec = (p.r % 4) == 0;
-    constexpr int UM = DION_UPD_BM, UN = DION_UPD_BN, UK = DION_UPD_BK;
-    const int64_t big = ((p.m + UM - 1) / UM) * ((p.n + UN - 1) / UN) * p.b;
-    if ((UM != 64 || UN != 64) && p.m >= UM && p.n >= UN && big >= kBigTileMinTiles) {
-        dim3 grid((unsigned)((p.n + UN - 1) / UN), (unsigned)((p.m + UM - 1) / UM), (unsigned)p.b);
-        hipLaunchKernelGGL((update_kernel<UM, UN, UK, GB, XB>), grid, dim3(256), 0, s, u);
+    // 128 x 128 tiles (half the operand traffic per output) while they still fill the chip
+    const int64_t big = ((p.n + 127) / 128) * ((p.m + 127) / 128) * p.b;
+    if (big >= kUpdBigMinTiles) {
+        dim3 grid((unsigned)((p.n + 127) / 128), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
+        hipLaunchKernelGGL((update_kernel<128, 128, 2, 4, GB, XB>), grid, dim3(512), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
-        hipLaunchKernelGGL((update_kernel<64, 64, UK, GB, XB>), grid, dim3(256), 0, s, u);
+        hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB>), grid, dim3(256), 0, s, u);
     }
     return hipGetLastError();
 }
@@ -1140,13 +1201,14 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
         hipLaunchKernelGGL(colscale_kernel, g2, dim3(256), 0, s, (const double*)(ws + p.part), (double*)(ws + p.cs),
                            p.r, (int)p.nchunk, (double)eps);
         DION_TRY(hipGetLastError());
-        dim3 g3(grid_1d(p.n * p.r, 1024), (unsigned)p.b);
+        dim3 g3(grid_1d(p.n * p.kp, 1024), (unsigned)p.b);
         hipLaunchKernelGGL(next_q_kernel, g3, dim3(256), 0, s, (const double*)(ws + p.R64), (float*)(ws + p.R32),
-                           (const double*)(ws + p.cs), Q, p.n, p.r, c.st);
+                           (const double*)(ws + p.cs), Q, (uint16_t*)(ws + p.Rp), (uint16_t*)(ws + p.Qp), p.n, p.r,
+                           p.kp, c.st);
         DION_TRY(hipGetLastError());
-        dim3 g4(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
-        hipLaunchKernelGGL(round_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
-                           p.m * p.r, c.st);
+        dim3 g4(grid_1d(p.m * p.kp, 1024), (unsigned)p.b);
+        hipLaunchKernelGGL(split_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
+                           (uint16_t*)(ws + p.Pp), p.m, p.r, p.kp, c.st);
         DION_TRY(hipGetLastError());
     }
     DION_TRY(mark(DION_PHASE_UPDATE));

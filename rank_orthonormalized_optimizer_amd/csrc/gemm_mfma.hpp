@@ -109,7 +109,10 @@ struct Operand {
 // an operand panel (the column tiles of one row panel, all tiles of one matrix) would otherwise
 // be spread over all eight L2s and fetch the panel eight times.  The linear id L (x fastest)
 // is renumbered so that XCD x processes the contiguous range of tile ids of its share, in
-// order; a bijection on [0, T) for any T.
+// order; a bijection on [0, T) for any T.  Within a matrix, tile ids then run down bands of
+// kTileBand rows, column by column, so the tiles resident on an XCD at one time (about 64)
+// form a block about 8 x 8 whose row and column operand panels together fit in its L2.
+constexpr int kTileBand = 8;
 struct TileId { int x, y, z; };
 __device__ __forceinline__ TileId xcd_tile_id() {
     constexpr int64_t NX = 8;
@@ -118,7 +121,11 @@ __device__ __forceinline__ TileId xcd_tile_id() {
     const int64_t L = blockIdx.x + gx * (blockIdx.y + gy * (int64_t)blockIdx.z);
     const int64_t q = T / NX, rem = T % NX, x = L % NX, slot = L / NX;
     const int64_t t = (x < rem) ? x * (q + 1) + slot : rem * (q + 1) + (x - rem) * q + slot;
-    return TileId{(int)(t % gx), (int)((t / gx) % gy), (int)(t / (gx * gy))};
+    const int64_t per = gx * gy, z = t / per, w = t % per;
+    const int64_t band = w / (kTileBand * gx), y0 = band * kTileBand;
+    const int64_t rows = gy - y0 < kTileBand ? gy - y0 : kTileBand;
+    const int64_t u = w - band * kTileBand * gx;     // position inside the band
+    return TileId{(int)(u / rows), (int)(y0 + u % rows), (int)z};
 }
 
 // XOR swizzle of the x index of KC operands in LDS.  A KC tile arrives as four consecutive k

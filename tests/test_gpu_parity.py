@@ -167,3 +167,11 @@ def test_sticky_hint_is_bitwise_neutral(cuda):
     for a, b in zip(runs[0], runs[1]):
         for x, y in zip(a[:4], b[:4]):
             assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("base", [1, 3])
+def test_wide_update_tiles(cuda, base):
+    """A stack large enough for the 128 x 128 weight-pass tiles (16 x 520 x 1000: 640 tiles, both
+    edges ragged, r = 72 padded to 96 in the split planes), fp32 and bf16 weights."""
+    wl = W.SMALL[base].with_groups(W.Group(16, 520, 1000, 72), name=f"wide-tiles-{base}", steps=2)
+    check(run_teacher_forced(wl, cuda), tol_for(wl))
