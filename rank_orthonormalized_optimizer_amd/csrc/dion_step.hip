@@ -7,7 +7,8 @@
 // rivista.ai: low-rank orthonormalized update with error feedback, amortized
 // power iteration with QR and Cholesky).
 //
-// orth() is CholeskyQR2: W = P0^T P0, L = chol(W), P1 = P0 L^-T, repeated once.
+// orth() is CholeskyQR2: W = P0^T P0, L = chol(W), P1 = P0 L^-T, repeated once
+// (the second pass by the near-identity series when P1^T P1 is close to I).
 // In exact arithmetic it gives the same Q-factor (positive diagonal) as a
 // Householder QR.  Two precision chains share the kernels:
 //   fp32 chain  B rounded once to fp32, fp32 MFMA everywhere.  If a Cholesky
@@ -21,7 +22,9 @@
 // The hand-over is a per-matrix state word in device memory: every kernel of a
 // chain tests it and returns at once for matrices it does not own, so the host
 // never synchronizes.  The momentum/weight pass then runs once for all
-// matrices in fp32 from P and R rounded to fp32.
+// matrices from P, R and the new Q rounded to fp32, with its two rank-r
+// products on the bf16 matrix cores in the exact three-way split form
+// (fp32 accuracy; see bf16x6.hpp).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
