@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{0, 0, 0, 0};
 
-    mainloop<T, C, AKC, ASRC, BKC, BSRC>(A, B, m0, n0, kbeg, kend, As, Bs, acc, [](int, int) {});
+    mainloop<T, C, AKC, ASRC, BKC, BSRC>(A, B, m0, n0, kbeg, kend, As, Bs, acc);
 
     T* Cp = (T*)((char*)g.c + bz * g.sc + grp * g.gc);
     const T* Sp = g.csrc ? (const T*)((const char*)g.csrc + bz * g.sc + grp * g.gc) : Cp;
@@ -669,6 +669,13 @@ struct ChainCtx {
     char* ws;
     int* st;
     hipStream_t s;
+    hipEvent_t gate = nullptr;   // recorded once, after the chunk's first product (staggered chunks)
+    bool* gated = nullptr;
+    hipError_t open_gate() const {
+        if (!gate || *gated) return hipSuccess;
+        *gated = true;
+        return hipEventRecord(gate, s);
+    }
 };
 
 // CholeskyQR building blocks on P [b][m][r], for the matrices with (st & mask) == val.
@@ -1093,6 +1100,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
         DION_TRY(mark(0));
         if ((e = g_bf16 ? bq_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, Q, P, mask, val)
                         : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, mask, val))) return e;
+        DION_TRY(c.open_gate());
         DION_TRY(mark(1));
         if ((e = cholqr_pass<T>(c, P, tmp, mask, val, force32 ? 0.0 : kTau32, fail, ST_PATH64))) return e;
         if ((e = reortho_pass<T>(c, tmp, P, mask, val, 0, 0, kNearId32, kNearId32, fail))) return e;
@@ -1106,6 +1114,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     DION_TRY(mark(0));
     if ((e = g_bf16 ? bq_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, Q, P, A64, A64)
                     : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, A64, A64))) return e;
+    DION_TRY(c.open_gate());
     DION_TRY(mark(1));
     // pass 1: unshifted attempt; a failed pivot or a large diagonal ratio marks SHIFT,
     // and the marked matrices factor W + s I instead (W is kept by the factorization)
@@ -1158,7 +1167,7 @@ static hipError_t launch_update(const Plan& p, const char* ws, float* M, const v
 // The whole step for the matrices of one chunk, on stream s.
 static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps,
                      int x_bf16, int g_bf16, char* ws, int32_t* flags, uint32_t options, hipStream_t s,
-                     void* const* ev) {
+                     void* const* ev, hipEvent_t gate = nullptr) {
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (p.b == 0) return 0;
     const int64_t mn = p.m * p.n;
@@ -1172,13 +1181,15 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
             hipLaunchKernelGGL(zero_flags_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, flags, p.b);
             DION_TRY(hipGetLastError());
         }
+        if (gate) DION_TRY(hipEventRecord(gate, s));
         DION_TRY(mark(DION_NUM_PHASES));
         return 0;
     }
     const bool force64 = options & DION_OPT_FORCE_F64;
     const bool force32 = options & DION_OPT_FORCE_F32;
     const bool sticky = options & DION_OPT_STICKY_F64;
-    ChainCtx c{&p, ws, (int*)(ws + p.st), s};
+    bool gated = false;
+    ChainCtx c{&p, ws, (int*)(ws + p.st), s, gate, &gated};
     DION_TRY(mark(DION_PHASE_INIT));
     hipLaunchKernelGGL(init_state_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, c.st, (const int32_t*)flags, p.b,
                        (int)force64, (int)sticky);
@@ -1192,6 +1203,7 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
         return e;
     if (force32 && ev)
         for (int i = DION_PHASE_F64_PRODUCT; i <= DION_PHASE_F64_BACKPROJECT; ++i) DION_TRY(mark(i));
+    DION_TRY(c.open_gate());
     DION_TRY(mark(DION_PHASE_NORMS));
 
     // column norms -> c = 1 / (||r_j|| + eps); Q <- R c; fp64-chain P, R rounded to fp32
@@ -1232,13 +1244,16 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
 }
 
 // Streams and events of the internal fork/join, one set per device, created on first use
-// (default priority).  A step is split into chunks of whole matrices, each run on its own
-// stream, so that one chunk's latency-bound CholeskyQR overlaps another chunk's GEMMs.
+// (default priority).  A step can be split into chunks of whole matrices, each run on its own
+// stream.  The chunks are staggered: chunk c + 1 starts once chunk c has issued its first
+// product, so that chunk c's latency-bound CholeskyQR (few workgroups, many dependent
+// launches) runs beside chunk c + 1's compute-bound products, and chunk c's back-projection
+// and weight pass beside chunk c + 1's CholeskyQR.
 constexpr int kMaxChunks = 8;
 struct StreamSet {
     bool ready = false;
     hipStream_t s[kMaxChunks];
-    hipEvent_t fork, join[kMaxChunks];
+    hipEvent_t fork, join[kMaxChunks], gate[kMaxChunks];
 };
 static std::mutex g_stream_mu;
 static StreamSet g_streams[64];
@@ -1252,6 +1267,7 @@ static hipError_t stream_set(StreamSet** out) {
         for (int i = 0; i < kMaxChunks; ++i) {
             DION_TRY_HIP(hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking));
             DION_TRY_HIP(hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming));
+            DION_TRY_HIP(hipEventCreateWithFlags(&ss.gate[i], hipEventDisableTiming));
         }
         DION_TRY_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
         ss.ready = true;
@@ -1285,9 +1301,10 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu
         const int64_t c0 = p.b * c / nc, c1 = p.b * (c + 1) / nc;
         const Plan q = chunk_plan(p, c0, c1 - c0);
         DION_TRY(hipStreamWaitEvent(ss->s[c], ss->fork, 0));
+        if (c > 0) DION_TRY(hipStreamWaitEvent(ss->s[c], ss->gate[c - 1], 0));
         int e = run_chunk(q, (char*)X + c0 * mn * xs, (const char*)G + c0 * mn * gs, M + c0 * mn,
                           Q ? Q + c0 * p.n * p.r : nullptr, mu, lr, eps, x_bf16, g_bf16, ws, flags ? flags + c0 : nullptr,
-                          options, ss->s[c], c == 0 ? ev : nullptr);
+                          options, ss->s[c], c == 0 ? ev : nullptr, ss->gate[c]);
         if (e) return e;
         DION_TRY(hipEventRecord(ss->join[c], ss->s[c]));
         DION_TRY(hipStreamWaitEvent(s, ss->join[c], 0));

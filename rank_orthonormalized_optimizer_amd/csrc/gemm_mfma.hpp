@@ -234,35 +234,67 @@ __device__ __forceinline__ void mma_slab(const T* As, const T* Bs, typename C::a
     }
 }
 
-// Double-buffered main loop over the K range [kbeg, kend): global loads of slab s+1 are in
-// flight while slab s is multiplied from LDS; one barrier per slab.  `slab_hook(k0, buf)` runs
-// right before each slab's MFMAs (used to stage per-slab side data).
-template <typename T, class C, bool AKC, int ASRC, bool BKC, int BSRC, class Hook>
+// Main loop over the K range [kbeg, kend), slab k in LDS buffer k % 2 (one barrier per slab).
+// fp64: two register staging sets, the raw loads of slab k + 2 issued before slab k is
+// multiplied, so each has two slabs of MFMA work to arrive.  fp32 (four times the MFMA rate,
+// half the bytes) keeps one staging set: the second one costs it a wave of occupancy.
+template <typename T, class C, bool AKC, int ASRC, bool BKC, int BSRC>
 __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int m0, int n0, int kbeg, int kend,
-                                         T* As, T* Bs, typename C::acc_t (&acc)[C::FM][C::FN], Hook&& hook) {
+                                         T* As, T* Bs, typename C::acc_t (&acc)[C::FM][C::FN]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    TileLoader<T, C::BM, C::BK, AKC, ASRC> la;
-    TileLoader<T, C::BN, C::BK, BKC, BSRC> lb;
     if (kbeg >= kend) return;
-    la.load(A, m0, kbeg);
-    lb.load(B, n0, kbeg);
-    la.template store<C::LDA>(As);
-    lb.template store<C::LDB>(Bs);
-    hook(kbeg, 0);
-    __syncthreads();
-    int buf = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
-        const bool more = k0 + C::BK < kend;
-        if (more) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
-        mma_slab<T, C, AKC, BKC>(As + buf * C::A_STAGE, Bs + buf * C::B_STAGE, acc, wm, wn, lane);
-        if (more) {
-            la.template store<C::LDA>(As + (buf ^ 1) * C::A_STAGE);
-            lb.template store<C::LDB>(Bs + (buf ^ 1) * C::B_STAGE);
-            hook(k0 + C::BK, buf ^ 1);
-        }
+    T* A0 = As;
+    T* A1 = As + C::A_STAGE;
+    T* B0 = Bs;
+    T* B1 = Bs + C::B_STAGE;
+    if constexpr (sizeof(T) == 8) {
+        TileLoader<T, C::BM, C::BK, AKC, ASRC> la0, la1;
+        TileLoader<T, C::BN, C::BK, BKC, BSRC> lb0, lb1;
+        la0.load(A, m0, kbeg);
+        lb0.load(B, n0, kbeg);
+        if (kbeg + C::BK < kend) { la1.load(A, m0, kbeg + C::BK); lb1.load(B, n0, kbeg + C::BK); }
+        la0.template store<C::LDA>(A0);
+        lb0.template store<C::LDB>(B0);
         __syncthreads();
-        buf ^= 1;
+        for (int k0 = kbeg; k0 < kend; k0 += 2 * C::BK) {
+            const int k1 = k0 + C::BK, k2 = k0 + 2 * C::BK, k3 = k0 + 3 * C::BK;
+            if (k2 < kend) { la0.load(A, m0, k2); lb0.load(B, n0, k2); }
+            mma_slab<T, C, AKC, BKC>(A0, B0, acc, wm, wn, lane);
+            if (k1 < kend) {
+                la1.template store<C::LDA>(A1);
+                lb1.template store<C::LDB>(B1);
+            }
+            __syncthreads();
+            if (k1 >= kend) break;
+            if (k3 < kend) { la1.load(A, m0, k3); lb1.load(B, n0, k3); }
+            mma_slab<T, C, AKC, BKC>(A1, B1, acc, wm, wn, lane);
+            if (k2 < kend) {
+                la0.template store<C::LDA>(A0);
+                lb0.template store<C::LDB>(B0);
+            }
+            __syncthreads();
+        }
+    } else {
+        TileLoader<T, C::BM, C::BK, AKC, ASRC> la;
+        TileLoader<T, C::BN, C::BK, BKC, BSRC> lb;
+        la.load(A, m0, kbeg);
+        lb.load(B, n0, kbeg);
+        la.template store<C::LDA>(A0);
+        lb.template store<C::LDB>(B0);
+        __syncthreads();
+        int buf = 0;
+        for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
+            const bool more = k0 + C::BK < kend;
+            if (more) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
+            mma_slab<T, C, AKC, BKC>(buf ? A1 : A0, buf ? B1 : B0, acc, wm, wn, lane);
+            if (more) {
+                la.template store<C::LDA>(buf ? A0 : A1);
+                lb.template store<C::LDB>(buf ? B0 : B1);
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
     }
 }
 
