@@ -56,3 +56,242 @@ constexpr int kTermA[6] = {1, 0, 2, 0, 1, 0};
 constexpr int kTermB[6] = {1, 2, 0, 1, 0, 0};
 
 }  // namespace dion
+
+namespace dion {
+
+// ---------------------------------------------------------------------------
+// Operand tiles of BX rows (x) by one 32-k slab, staged into LDS as three swizzled bf16 part
+// tiles [x][32] (part_off).  Each of 256 staging threads (index t) owns a fixed share: load()
+// fetches its raw values, split() turns them into bf16 parts in registers, store() writes them.
+// ---------------------------------------------------------------------------
+enum Src6 : int {
+    S6_PLANES = 0,   // pre-split planes p0[3][rows][ld] (h, m, l), k contiguous, zero padded to ld
+    S6_KC = 1,       // fp32 p0[x * ld + k] (+ addend p1 at the same index), k contiguous
+    S6_XC = 2,       // fp32 p0[k * ld + x] (+ addend p1 at the same index), x contiguous
+};
+enum Add6 : int { A6_NONE = 0, A6_F32 = 1, A6_BF16 = 2 };
+
+struct Op6 {
+    const void* p0;
+    const void* p1;     // addend (B = M + G), or null
+    int64_t ld;         // pitch in elements between rows of the stored array
+    int64_t plane;      // elements per plane (S6_PLANES)
+    int xext, kext;     // valid extents along x and k (outside: zeros)
+    bool vec;           // S6_KC: 4-element vector loads are legal (ld, bases aligned)
+};
+
+// value of element (raw a, raw b) of a sum source: one fp32 addition (correctly rounded)
+template <int ADD> struct Add6T { using t = float; };
+template <> struct Add6T<A6_BF16> { using t = uint16_t; };
+template <int ADD>
+__device__ __forceinline__ float sum6(float a, typename Add6T<ADD>::t b) {
+    if constexpr (ADD == A6_NONE) return a;
+    else if constexpr (ADD == A6_BF16) return a + __uint_as_float((uint32_t)b << 16);
+    else return a + b;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// two values at once: packed (h, m, l) parts, low half = first value
+__device__ __forceinline__ void split3x2(float a0, float a1, uint32_t& h, uint32_t& m, uint32_t& l) {
+    const f32x2_t a = {a0, a1};
+    const bf16x2_t bh = __builtin_convertvector(a, bf16x2_t);
+    const f32x2_t r1 = a - __builtin_convertvector(bh, f32x2_t);
+    const bf16x2_t bm = __builtin_convertvector(r1, bf16x2_t);
+    const f32x2_t r2 = r1 - __builtin_convertvector(bm, f32x2_t);
+    const bf16x2_t bl = __builtin_convertvector(r2, bf16x2_t);
+    h = __builtin_bit_cast(uint32_t, bh);
+    m = __builtin_bit_cast(uint32_t, bm);
+    l = __builtin_bit_cast(uint32_t, bl);
+}
+
+// four consecutive k, split: parts p[0..2] as packed pairs
+struct Parts4 { u32x2 p[3]; };
+__device__ __forceinline__ Parts4 split4(const float (&v)[4]) {
+    Parts4 r;
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3x2(v[0], v[1], h0, m0, l0);
+    split3x2(v[2], v[3], h1, m1, l1);
+    r.p[0] = u32x2{h0, h1};
+    r.p[1] = u32x2{m0, m1};
+    r.p[2] = u32x2{l0, l1};
+    return r;
+}
+// write them at k (k % 4 == 0 within the slab) of row x of the three part tiles
+__device__ __forceinline__ void store4(uint16_t* lds, int part_stride, int x, int k, const Parts4& q) {
+    const int off = part_off(x, k >> 3) + (k & 7);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *(u32x2*)&lds[p * part_stride + off] = q.p[p];
+}
+
+template <int BX, int KIND, int ADD>
+struct Loader6;
+
+// pre-split planes: BX * 4 chunks of 16 bytes per part, BX / 64 per thread
+template <int BX, int ADD>
+struct Loader6<BX, S6_PLANES, ADD> {
+    static constexpr int PER = BX / 64;
+    u32x4 r[3][PER];
+    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int x = (t >> 2) + 64 * q, c = t & 3;
+            const bool ok = x0 + x < op.xext;
+            const int64_t o = (int64_t)(ok ? x0 + x : 0) * op.ld + k0 + 8 * c;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                r[p][q] = ok ? *(const u32x4*)((const uint16_t*)op.p0 + p * op.plane + o) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void split() {}
+    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int off = part_off((t >> 2) + 64 * q, t & 3);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) *(u32x4*)&lds[p * BX * kSplitK + off] = r[p][q];
+        }
+    }
+};
+
+// k-contiguous fp32 (+ addend): BX * 8 groups of four k, BX / 32 per thread (8 threads per row).
+// Interior tiles with vector-aligned rows take unchecked 4-element loads.
+template <int BX, int ADD>
+struct Loader6<BX, S6_KC, ADD> {
+    static constexpr int PER = BX / 32;
+    using AT = typename Add6T<ADD>::t;
+    float a[PER][4];
+    AT b[ADD == A6_NONE ? 1 : PER][4];
+    Parts4 sp[PER];
+    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
+        const int xr = t >> 3, kk = 4 * (t & 7);
+        const bool interior = op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
+        if (interior) {
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int64_t o = (int64_t)(x0 + xr + 32 * q) * op.ld + k0 + kk;
+                const float4 v = *(const float4*)((const float*)op.p0 + o);
+                a[q][0] = v.x; a[q][1] = v.y; a[q][2] = v.z; a[q][3] = v.w;
+                if constexpr (ADD == A6_F32) {
+                    const float4 w = *(const float4*)((const float*)op.p1 + o);
+                    b[q][0] = w.x; b[q][1] = w.y; b[q][2] = w.z; b[q][3] = w.w;
+                } else if constexpr (ADD == A6_BF16) {
+                    const uint2 w = *(const uint2*)((const uint16_t*)op.p1 + o);
+                    b[q][0] = (uint16_t)w.x; b[q][1] = (uint16_t)(w.x >> 16);
+                    b[q][2] = (uint16_t)w.y; b[q][3] = (uint16_t)(w.y >> 16);
+                }
+            }
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int x = x0 + xr + 32 * q, k = k0 + kk;
+            const int64_t o = (int64_t)(x < op.xext ? x : 0) * op.ld + k;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool in = x < op.xext && k + e < op.kext;
+                a[q][e] = in ? ((const float*)op.p0)[o + e] : 0.f;
+                if constexpr (ADD != A6_NONE) b[q][e] = in ? ((const AT*)op.p1)[o + e] : AT(0);
+            }
+        }
+    }
+    __device__ __forceinline__ void split() {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ADD == A6_NONE) v[e] = a[q][e];
+                else v[e] = sum6<ADD>(a[q][e], b[q][e]);
+            }
+            sp[q] = split4(v);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) store4(lds, BX * kSplitK, (t >> 3) + 32 * q, 4 * (t & 7), sp[q]);
+    }
+};
+
+// x-contiguous fp32 (+ addend): thread owns one x and BX / 8 consecutive k (coalesced along x).
+// The k rows a wave reads are the same for all its lanes, so their offsets are made scalar.
+template <int BX, int ADD>
+struct Loader6<BX, S6_XC, ADD> {
+    static constexpr int KPT = BX * kSplitK / 256;   // k values per thread
+    static_assert(KPT % 4 == 0 && 256 % BX == 0 && BX % 64 == 0, "whole groups of four k per thread");
+    using AT = typename Add6T<ADD>::t;
+    float a[KPT];
+    AT b[ADD == A6_NONE ? 1 : KPT];
+    Parts4 sp[KPT / 4];
+    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
+        const int x = x0 + t % BX;
+        const int kb = __builtin_amdgcn_readfirstlane(k0 + (t / BX) * KPT);   // uniform per wave
+        const bool interior = x0 + BX <= op.xext && kb + KPT <= op.kext;
+        const float* pa = (const float*)op.p0 + (int64_t)kb * op.ld;
+        const AT* pb = ADD != A6_NONE ? (const AT*)op.p1 + (int64_t)kb * op.ld : nullptr;
+        if (interior) {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                a[e] = pa[(int64_t)e * op.ld + x];
+                if constexpr (ADD != A6_NONE) b[e] = pb[(int64_t)e * op.ld + x];
+            }
+            return;
+        }
+        const bool xin = x < op.xext;
+        const int xs = xin ? x : 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const bool in = xin && kb + e < op.kext;
+            const int64_t o = (int64_t)(kb + e < op.kext ? e : 0) * op.ld + xs;
+            a[e] = in ? pa[o] : 0.f;
+            if constexpr (ADD != A6_NONE) b[e] = in ? pb[o] : AT(0);
+        }
+    }
+    __device__ __forceinline__ void split() {
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ADD == A6_NONE) v[e] = a[4 * g + e];
+                else v[e] = sum6<ADD>(a[4 * g + e], b[4 * g + e]);
+            }
+            sp[g] = split4(v);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+        const int x = t % BX, kb = (t / BX) * KPT;
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) store4(lds, BX * kSplitK, x, kb + 4 * g, sp[g]);
+    }
+};
+
+// acc[i][j] (wave sub-tile FM x FN blocks of 16 x 16) += A B over one 32-k slab from the part
+// tiles: B fragments of all three parts held, A fragments one part at a time, the six kept
+// products in increasing size.
+template <int BXA, int BXB, int FM, int FN>
+__device__ __forceinline__ void mma6_slab(const uint16_t* lA, const uint16_t* lB, f32x4 (&acc)[FM][FN], int ra,
+                                          int rb, int fr, int fc) {
+    u32x4 b[FN][3];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            b[j][p] = *(const u32x4*)&lB[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
+#pragma unroll
+    for (int pa = 2; pa >= 0; --pa) {
+        u32x4 a[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = *(const u32x4*)&lA[pa * BXA * kSplitK + part_off(ra + 16 * i + fr, fc)];
+#pragma unroll
+        for (int pb = 2 - pa; pb >= 0; --pb)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mma_bf16(a[i], b[j][pb], acc[i][j]);
+    }
+}
+
+}  // namespace dion

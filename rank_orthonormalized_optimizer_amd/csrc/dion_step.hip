@@ -1046,11 +1046,118 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
     return apply<T>(c, Pin, Pout, cmask, cval);
 }
 
+// ---------------------------------------------------------------------------
+// fp32-chain products on the bf16 matrix cores (six-term split, fp32 accuracy; bf16x6.hpp):
+// C[M x N] = A B per matrix, with A and B read as split-bf16 operand tiles.  128 x 128 tiles,
+// four multiplying waves of 64 x 64 (so each LDS fragment feeds four MFMA blocks) and four
+// staging waves, triple-buffered part tiles in 144 KB of LDS: one workgroup per CU.
+// ---------------------------------------------------------------------------
+#ifndef DION_PROD6
+#define DION_PROD6 1
+#endif
+struct Prod6Args {
+    Op6 a, b;
+    int64_t sa0, sa1, sb0;       // batch strides in bytes of a.p0, a.p1, b.p0
+    float* c;
+    int64_t ldc, sc;             // sc in elements
+    int M, N, K;
+    const int* st;
+    int st_mask, st_val;
+};
+
+template <int AK, int AADD, int BK6>
+__global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
+    // Eight waves: waves 0-3 multiply (a 64 x 64 sub-tile each), waves 4-7 stage the operands
+    // (load, split into bf16 parts, write LDS).  Each SIMD holds one wave of each kind, so the
+    // staging VALU work issues between the other wave's MFMAs; one barrier per slab.
+    constexpr int BT = 128, PT = BT * kSplitK;
+    const TileId tid = xcd_tile_id();
+    const int bz = tid.z;
+    if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
+    const int m0 = tid.y * BT, n0 = tid.x * BT;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3][6 * PT];   // A h m l | B h m l
+    const int wave = threadIdx.x >> 6;
+    const bool stager = wave >= 4;
+    const int st_t = threadIdx.x - 256;
+    Op6 A = g.a, B = g.b;
+    A.p0 = (const char*)A.p0 + bz * g.sa0;
+    if (A.p1) A.p1 = (const char*)A.p1 + bz * g.sa1;
+    B.p0 = (const char*)B.p0 + bz * g.sb0;
+    Loader6<BT, AK, AADD> la;
+    Loader6<BT, BK6, A6_NONE> lb;
+    const int lane = threadIdx.x & 63, wm = (wave >> 1) & 1, wn = wave & 1;
+    const int fr = lane & 15, fc = lane >> 4;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    // three LDS buffers: while slab s is multiplied from buffer s % 3, the staging waves
+    // write slab s + 2 (loaded one slab earlier) to buffer (s + 2) % 3 and load slab s + 3
+    auto stage = [&](int k, int b) {
+        la.split();
+        lb.split();
+        if (k + kSplitK < g.K) { la.load(A, m0, k + kSplitK, st_t); lb.load(B, n0, k + kSplitK, st_t); }
+        la.store(lds[b], st_t);
+        lb.store(lds[b] + 3 * PT, st_t);
+    };
+    if (stager) {
+        la.load(A, m0, 0, st_t);
+        lb.load(B, n0, 0, st_t);
+        stage(0, 0);
+        if (kSplitK < g.K) stage(kSplitK, 1);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < g.K; k0 += kSplitK) {
+        if (stager) {
+            if (k0 + 2 * kSplitK < g.K) stage(k0 + 2 * kSplitK, buf == 0 ? 2 : buf - 1);
+        } else {
+            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc, wm * 64, wn * 64, fr, fc);
+        }
+        __syncthreads();
+        buf = buf == 2 ? 0 : buf + 1;
+    }
+    if (stager) return;
+    float* C = g.c + bz * g.sc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm * 64 + 16 * i + 4 * fc + v, col = n0 + wn * 64 + 16 * j + fr;
+                if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = acc[i][j][v];
+            }
+}
+
+template <int AK, int AADD, int BK6>
+static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+    dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128), (unsigned)batch);
+    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6>), grid, dim3(512), 0, s, g);
+    return hipGetLastError();
+}
+
 // P0 = (M + G) Q  and  R = (M + G)^T P for one chain.
 template <typename T, int ASRC>
 static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, const float* Q, T* P, int mask, int val) {
     const Plan& p = *c.p;
     const int64_t m = p.m, n = p.n, r = p.r;
+    if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
+        Prod6Args g{};
+        g.a = Op6{M, G, n, 0, (int)m, (int)n, va};               // A(i,k) = B[i][k]  (k contiguous)
+        g.b = Op6{Q, nullptr, r, 0, (int)r, (int)n, false};      // B(k,j) = Q[k][j]  (j contiguous)
+        g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = n * r * 4;
+        g.c = (float*)P; g.ldc = r; g.sc = m * r;
+        g.M = (int)m; g.N = (int)r; g.K = (int)n;
+        g.st = c.st; g.st_mask = mask; g.st_val = val;
+        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC>(g, p.b, c.s)
+                                                   : launch_prod6<S6_KC, A6_F32, S6_XC>(g, p.b, c.s);
+        DION_TRY(he);
+        return 0;
+    }
     GemmArgs g{};
     const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
     g.a = Operand{M, G, n, (int)m, (int)n, va};                    // A(i,k) = B[i][k]
@@ -1068,6 +1175,19 @@ template <typename T, int ASRC>
 static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, const T* P, T* R, int mask, int val) {
     const Plan& p = *c.p;
     const int64_t m = p.m, n = p.n, r = p.r;
+    if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        Prod6Args g{};
+        g.a = Op6{M, G, n, 0, (int)n, (int)m, false};            // A(i,k) = B[k][i]  (i contiguous)
+        g.b = Op6{P, nullptr, r, 0, (int)r, (int)m, false};      // B(k,j) = P[k][j]  (j contiguous)
+        g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = m * r * 4;
+        g.c = (float*)R; g.ldc = r; g.sc = n * r;
+        g.M = (int)n; g.N = (int)r; g.K = (int)m;
+        g.st = c.st; g.st_mask = mask; g.st_val = val;
+        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC, A6_BF16, S6_XC>(g, p.b, c.s)
+                                                   : launch_prod6<S6_XC, A6_F32, S6_XC>(g, p.b, c.s);
+        DION_TRY(he);
+        return 0;
+    }
     GemmArgs g{};
     const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
     g.a = Operand{M, G, n, (int)n, (int)m, va};                    // A(i,k) = B[k][i]
