@@ -595,6 +595,170 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
             }
 }
 
+// The weight pass for large stacks: 128 x 128 tiles of M and X per workgroup of eight waves.
+// Waves 0-3 multiply (a 64 x 64 sub-tile each, both products), waves 4-7 copy the split planes
+// of P, R and Q into double-buffered LDS (144 KB, one workgroup per CU).  The epilogue runs on
+// the multiplying waves in four 16-row chunks, the next chunk's loads issued before the
+// current chunk's stores.
+template <bool G_BF16, bool X_BF16>
+__global__ __launch_bounds__(512) void update6_kernel(UpdArgs u) {
+    constexpr int BT = 128, PT = BT * kSplitK;
+    const TileId tid = xcd_tile_id();
+    const int bz = tid.z, m0 = tid.y * BT, n0 = tid.x * BT;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][9 * PT];   // P h m l | R h m l | Q h m l
+    const int wave = threadIdx.x >> 6;
+    const bool stager = wave >= 4;
+    const int st_t = threadIdx.x - 256;
+    const int64_t ps = (int64_t)u.m * u.kp, ns = (int64_t)u.n * u.kp;
+    const Op6 oP{u.Pp + (int64_t)bz * 3 * ps, nullptr, u.kp, ps, u.m, u.kp, true};
+    const Op6 oR{u.Rp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
+    const Op6 oQ{u.Qp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
+    Loader6<BT, S6_PLANES, A6_NONE> lp, lr, lq;
+    const int lane = threadIdx.x & 63, wm = (wave >> 1) & 1, wn = wave & 1;
+    const int fr = lane & 15, fc = lane >> 4;
+    f32x4 acc1[4][4], acc2[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
+    auto stage_load = [&](int k) {
+        lp.load(oP, m0, k, st_t);
+        lr.load(oR, n0, k, st_t);
+        lq.load(oQ, n0, k, st_t);
+    };
+    auto stage_store = [&](int b) {
+        lp.store(lds[b], st_t);
+        lr.store(lds[b] + 3 * PT, st_t);
+        lq.store(lds[b] + 6 * PT, st_t);
+    };
+    // the two roles run separate loops (disjoint register live ranges) with one barrier per slab
+    if (stager) {
+        stage_load(0);
+        stage_store(0);
+        if (kSplitK < u.kp) stage_load(kSplitK);
+        __syncthreads();
+        int buf = 0;
+        for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
+            if (k0 + kSplitK < u.kp) {
+                stage_store(buf ^ 1);
+                if (k0 + 2 * kSplitK < u.kp) stage_load(k0 + 2 * kSplitK);
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+    } else {
+        __syncthreads();
+        int buf = 0;
+        for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
+            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc1, wm * 64, wn * 64, fr, fc);
+            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 6 * PT, acc2, wm * 64, wn * 64, fr, fc);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+    // Epilogue: the two product tiles go through LDS (row-major, rows padded to 132 floats so the
+    // MFMA-layout writes spread over all banks); then all eight waves update M and X with
+    // four-element row-contiguous accesses, every load of a half-tile issued before its stores.
+    constexpr int LDC = BT + 4;
+    float* c1 = (float*)&lds[0][0];
+    float* c2 = c1 + BT * LDC;
+    static_assert(2 * BT * LDC * 4 <= (int)sizeof(lds), "product tiles fit in the operand buffers");
+    if (!stager) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = wm * 64 + 16 * i + 4 * fc + v, c = wn * 64 + 16 * j + fr;
+                    c1[r * LDC + c] = acc1[i][j][v];
+                    c2[r * LDC + c] = acc2[i][j][v];
+                }
+    }
+    __syncthreads();
+    const int64_t mn = (int64_t)u.m * u.n;
+    float* Mp = u.M + bz * mn;
+    const bool vec = (u.n % 4) == 0 && m0 + BT <= u.m && n0 + BT <= u.n;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // four-column groups g = t + 512 q of the half-tile's 64 rows x 32 groups
+        float4 mv[4], gv[4], xv[4];
+        int64_t loc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int g = t + 512 * q, r = 64 * h + (g >> 5), c = 4 * (g & 31);
+            loc[q] = (int64_t)(m0 + r) * u.n + n0 + c;
+            if (vec) {
+                mv[q] = *(const float4*)(Mp + loc[q]);
+                if constexpr (G_BF16) {
+                    const uint2 w = *(const uint2*)((const uint16_t*)u.G + bz * mn + loc[q]);
+                    gv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
+                                   bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
+                } else {
+                    gv[q] = *(const float4*)((const float*)u.G + bz * mn + loc[q]);
+                }
+                if constexpr (X_BF16) {
+                    const uint2 w = *(const uint2*)((const uint16_t*)u.X + bz * mn + loc[q]);
+                    xv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
+                                   bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
+                } else {
+                    xv[q] = *(const float4*)((const float*)u.X + bz * mn + loc[q]);
+                }
+            } else {
+                float tm[4], tg[4], tx[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool in = m0 + r < u.m && n0 + c + e < u.n;
+                    const int64_t l = in ? loc[q] + e : 0, off = bz * mn + l;
+                    tm[e] = Mp[l];
+                    if constexpr (G_BF16) tg[e] = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
+                    else tg[e] = ((const float*)u.G)[off];
+                    if constexpr (X_BF16) tx[e] = bf16_bits_to_float(((const uint16_t*)u.X)[off]);
+                    else tx[e] = ((const float*)u.X)[off];
+                }
+                mv[q] = float4{tm[0], tm[1], tm[2], tm[3]};
+                gv[q] = float4{tg[0], tg[1], tg[2], tg[3]};
+                xv[q] = float4{tx[0], tx[1], tx[2], tx[3]};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int g = t + 512 * q, r = 64 * h + (g >> 5), c = 4 * (g & 31);
+            const float4 p1 = *(const float4*)&c1[r * LDC + c];
+            const float4 p2 = *(const float4*)&c2[r * LDC + c];
+            const float m4[4] = {mv[q].x, mv[q].y, mv[q].z, mv[q].w}, g4[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+            const float x4[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+            const float a1[4] = {p1.x, p1.y, p1.z, p1.w}, a2[4] = {p2.x, p2.y, p2.z, p2.w};
+            float mo[4], xo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                mo[e] = (m4[e] + g4[e]) - u.one_minus_mu * a1[e];
+                xo[e] = x4[e] - u.lr_s * a2[e];
+            }
+            if (vec) {
+                *(float4*)(Mp + loc[q]) = float4{mo[0], mo[1], mo[2], mo[3]};
+                if constexpr (X_BF16) {
+                    const uint2 w = {(uint32_t)float_to_bf16_bits(xo[0]) | ((uint32_t)float_to_bf16_bits(xo[1]) << 16),
+                                     (uint32_t)float_to_bf16_bits(xo[2]) | ((uint32_t)float_to_bf16_bits(xo[3]) << 16)};
+                    *(uint2*)((uint16_t*)u.X + bz * mn + loc[q]) = w;
+                } else {
+                    *(float4*)((float*)u.X + bz * mn + loc[q]) = float4{xo[0], xo[1], xo[2], xo[3]};
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (m0 + r >= u.m || n0 + c + e >= u.n) continue;
+                    const int64_t l = loc[q] + e, off = bz * mn + l;
+                    Mp[l] = mo[e];
+                    if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(xo[e]);
+                    else ((float*)u.X)[off] = xo[e];
+                }
+            }
+        }
+    }
+}
+
 // rank 0: M <- M + G
 template <bool G_BF16>
 __global__ __launch_bounds__(256) void add_grad_kernel(float* M, const void* G, int64_t total) {
@@ -1276,7 +1440,7 @@ static hipError_t launch_update(const Plan& p, const char* ws, float* M, const v
     const int64_t big = ((p.n + 127) / 128) * ((p.m + 127) / 128) * p.b;
     if (big >= kUpdBigMinTiles) {
         dim3 grid((unsigned)((p.n + 127) / 128), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
-        hipLaunchKernelGGL((update_kernel<128, 128, 2, 4, GB, XB>), grid, dim3(512), 0, s, u);
+        hipLaunchKernelGGL((update6_kernel<GB, XB>), grid, dim3(512), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
         hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB>), grid, dim3(256), 0, s, u);
