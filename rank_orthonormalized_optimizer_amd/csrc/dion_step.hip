@@ -280,25 +280,28 @@ struct DiagSteps {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
-    // One fused right-looking sweep over the columns k of the block:
-    //   Cholesky   l_ik = a_ik / l_kk,  a_ij -= l_ik l_jk      (k < j <= i)
-    //   inverse    x_i  -= l_ik (x_k / l_kk)                   (rows of X = L^-1, columns c <= k)
-    // Thread t owns row i = t / 4 and, in registers, the 16 columns j = 4 s + t % 4 of that row of
-    // the working matrix and of X.  Per column, the raw column k (zero at rows <= k), the pivot and
-    // row k of X (zero right of the diagonal) travel through double-buffered LDS, so the updates
-    // need no predicates and one barrier per column suffices.
+struct DiagSmem {
+    T col[2][kNB];
+    T xrow[2][kNB];
+    T piv[2];
+    T dg[kNB];
+};
+
+// One fused right-looking sweep over the columns k of the diagonal block of matrix bz:
+//   Cholesky   l_ik = a_ik / l_kk,  a_ij -= l_ik l_jk      (k < j <= i)
+//   inverse    x_i  -= l_ik (x_k / l_kk)                   (rows of X = L^-1, columns c <= k)
+// Thread t owns row i = t / 4 and, in registers, the 16 columns j = 4 s + t % 4 of that row of
+// the working matrix and of X.  Per column, the raw column k (zero at rows <= k), the pivot and
+// row k of X (zero right of the diagonal) travel through double-buffered LDS, so the updates
+// need no predicates and one barrier per column suffices.  Returns false (fail bit set) on a
+// non-positive or non-finite pivot; the decision is the same in every thread.
+template <typename T>
+__device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
     constexpr int NB = kNB, NS = NB / 4;
     static_assert(NB * 4 == 256, "one row per four threads");
-    const int bz = blockIdx.x;
-    if ((p.st[bz] & p.st_mask) != p.st_val) return;
-    __shared__ T col[2][NB];
-    __shared__ T xrow[2][NB];
-    __shared__ T piv[2];
-    __shared__ T dg[NB];
     T* L = (T*)p.L + bz * p.sL;
     DiagCtx<T> c;
-    c.col = col; c.xrow = xrow; c.piv = piv; c.dg = dg;
+    c.col = sm.col; c.xrow = sm.xrow; c.piv = sm.piv; c.dg = sm.dg;
     c.nbj = p.nbj; c.tid = threadIdx.x;
     c.i = c.tid >> 2; c.part = c.tid & 3;
     c.row_ok = c.i < c.nbj;
@@ -314,13 +317,13 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
     const int tid = c.tid, i = c.i, part = c.part, nbj = c.nbj;
     if (!c.ok) {
         if (tid == 0) p.st[bz] |= p.fail_bit;
-        return;
+        return false;
     }
     __syncthreads();
     if (tid == 0) {
-        double mn = (double)dg[0], mx = (double)dg[0];
+        double mn = (double)sm.dg[0], mx = (double)sm.dg[0];
         for (int q = 1; q < nbj; ++q) {
-            const double d = (double)dg[q];
+            const double d = (double)sm.dg[q];
             mn = d < mn ? d : mn;
             mx = d > mx ? d : mx;
         }
@@ -330,13 +333,22 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
         if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
     }
     T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * NB * NB;
-    const T rinv = c.row_ok ? T(1) / dg[i] : T(0);
+    const T rinv = c.row_ok ? T(1) / sm.dg[i] : T(0);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int j = 4 * s + part;
         if (c.row_ok && j <= i) c.Lrow[j] = c.a[s];
         Td[i * NB + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
     }
+    return true;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
+    const int bz = blockIdx.x;
+    if ((p.st[bz] & p.st_mask) != p.st_val) return;
+    __shared__ DiagSmem<T> sm;
+    diag_block<T>(p, bz, sm);
 }
 
 // L = W (+ s I), s = c_shift * trace(W) when shifting.
@@ -983,6 +995,152 @@ __global__ __launch_bounds__(256) void copy_pred_kernel(const T* src, T* dst, in
         dst[bz * total + idx] = src[bz * total + idx];
 }
 
+// ---------------------------------------------------------------------------
+// Factor and inverse in one launch, one workgroup per matrix (ranks up to kFusedMaxBlocks
+// blocks): L = chol(W (+ s I)) by 64-column blocks (diagonal block with its inverse, panel
+// L21 <- L21 Td^T, trailing L22 <- L22 - L21 L21^T, each product a 64 x 64 MFMA tile of the
+// workgroup), then Tf = L^-1 by blocked forward substitution,
+//   Tf_jj = Td_j,   Tf_ij = -Td_i (sum_{j <= k < i} L_ik Tf_kj).
+// Same arithmetic as the multi-launch factor() + invert(), with one launch instead of about
+// 3 nblk + 2 log2(nblk) + 2, which matters most on the rarely taken fallback paths (their
+// launches are otherwise issued, and return at once, on every step).
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxBlocks = 8;
+struct CholInvArgs {
+    const void* W; void* L; void* Td; void* Tf; void* Y;
+    int64_t r, nblk;
+    int* st;
+    int st_mask, st_val;
+    double* kap;
+    double tau;
+    int fail_bit, tau_bit, shift;
+    double c_shift;
+};
+
+// C (M x N <= 64 x 64, ldc) = alpha A B + beta C with A(i,k) k-contiguous and B either
+// k-contiguous (BKC) or row-contiguous; all loads of C happen before its stores, and the
+// workgroup synchronizes at the end (C is read back by the next tile).
+template <typename T, bool BKC>
+__device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int K, T* Cp, int64_t ldc, T alpha,
+                          T beta, T* As, T* Bs) {
+    using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
+    constexpr int S = SrcOf<T>::v;
+    typename C::acc_t acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{0, 0, 0, 0};
+    mainloop<T, C, true, S, BKC, S>(A, B, 0, 0, 0, K, As, Bs, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+    T sv[C::FM][C::FN][4];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = wm * C::WTM + i * 16 + Mfma<T>::row(lane, v), col = wn * C::WTN + j * 16 + (lane & 15);
+                sv[i][j][v] = (beta != T(0) && row < M && col < N) ? Cp[(int64_t)row * ldc + col] : T(0);
+            }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = wm * C::WTM + i * 16 + Mfma<T>::row(lane, v), col = wn * C::WTN + j * 16 + (lane & 15);
+                if (row < M && col < N) Cp[(int64_t)row * ldc + col] = alpha * acc[i][j][v] + beta * sv[i][j][v];
+            }
+    __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void cholinv_kernel(CholInvArgs a) {
+    const int bz = blockIdx.x;
+    if ((a.st[bz] & a.st_mask) != a.st_val) return;
+    using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
+    __shared__ DiagSmem<T> sm;
+    __shared__ T As[2 * C::A_STAGE];
+    __shared__ T Bs[2 * C::B_STAGE];
+    __shared__ double red[256];
+    const int64_t r = a.r, rr = r * r, nblk = a.nblk;
+    const T* W = (const T*)a.W + bz * rr;
+    T* L = (T*)a.L + bz * rr;
+    T* Tf = (T*)a.Tf + bz * rr;
+    T* Y = (T*)a.Y + bz * rr;
+    T* Td = (T*)a.Td + bz * nblk * kNB * kNB;
+    const bool vr = (r % 4) == 0;
+    // L = W (+ s I), s = c_shift trace(W)
+    T sv = T(0);
+    if (a.shift) {
+        double tr = 0;
+        for (int64_t i = threadIdx.x; i < r; i += 256) tr += (double)W[i * r + i];
+        red[threadIdx.x] = tr;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+            __syncthreads();
+        }
+        sv = (T)(a.c_shift * red[0]);
+    }
+    for (int64_t idx = threadIdx.x; idx < rr; idx += 256) {
+        const int64_t i = idx / r, k = idx % r;
+        L[idx] = W[idx] + ((i == k) ? sv : T(0));
+    }
+    __syncthreads();
+    auto nb = [&](int64_t jb) { return (int)((r - jb * kNB) < kNB ? (r - jb * kNB) : kNB); };
+    for (int64_t jb = 0; jb < nblk; ++jb) {
+        PotrfArgs pa{};
+        pa.L = a.L; pa.ldl = r; pa.sL = rr;
+        pa.Td = a.Td; pa.sTd = nblk * kNB * kNB;
+        pa.j0 = (int)(jb * kNB); pa.nbj = nb(jb); pa.jblk = (int)jb;
+        pa.st = a.st; pa.kap = a.kap;
+        pa.first = jb == 0; pa.last = jb == nblk - 1;
+        pa.tau = a.tau; pa.fail_bit = a.fail_bit; pa.tau_bit = a.tau_bit;
+        if (!diag_block<T>(pa, bz, sm)) return;
+        __syncthreads();
+        const int nbj = nb(jb);
+        for (int64_t ib = jb + 1; ib < nblk; ++ib) {          // panel
+            T* tile = L + ib * kNB * r + jb * kNB;
+            const Operand A{tile, nullptr, r, nb(ib), nbj, vr};
+            const Operand B{Td + jb * kNB * kNB, nullptr, kNB, nbj, nbj, true};
+            tile_gemm<T, true>(A, B, nb(ib), nbj, nbj, tile, r, T(1), T(0), As, Bs);
+        }
+        for (int64_t kb = jb + 1; kb < nblk; ++kb)            // trailing, lower tiles
+            for (int64_t ib = kb; ib < nblk; ++ib) {
+                const Operand A{L + ib * kNB * r + jb * kNB, nullptr, r, nb(ib), nbj, vr};
+                const Operand B{L + kb * kNB * r + jb * kNB, nullptr, r, nb(kb), nbj, vr};
+                tile_gemm<T, true>(A, B, nb(ib), nb(kb), nbj, L + ib * kNB * r + kb * kNB, r, T(-1), T(1), As, Bs);
+            }
+    }
+    __syncthreads();                                          // the state word written by thread 0
+    if (a.tau_bit && (a.st[bz] & a.tau_bit)) return;          // refactored shifted: no inverse needed
+    // Tf = L^-1: diagonal blocks from Td, zero above, then the blocks below by rows of blocks
+    for (int64_t idx = threadIdx.x; idx < rr; idx += 256) {
+        const int64_t i = idx / r, k = idx % r, bi = i / kNB, bk = k / kNB;
+        Tf[idx] = (bi == bk) ? Td[(bi * kNB + (i % kNB)) * kNB + (k % kNB)] : T(0);
+    }
+    __syncthreads();
+    for (int64_t ib = 1; ib < nblk; ++ib)
+        for (int64_t jb = 0; jb < ib; ++jb) {
+            const int K = (int)((ib - jb) * kNB);
+            // Y = sum_{jb <= k < ib} L[ib][k] Tf[k][jb]   (64 x nb(jb), ld 64)
+            const Operand A{L + ib * kNB * r + jb * kNB, nullptr, r, nb(ib), K, vr};
+            const Operand B{Tf + jb * kNB * r + jb * kNB, nullptr, r, nb(jb), K, vr};
+            tile_gemm<T, false>(A, B, nb(ib), nb(jb), K, Y, kNB, T(1), T(0), As, Bs);
+            // Tf[ib][jb] = -Td_ib Y
+            const Operand A2{Td + ib * kNB * kNB, nullptr, kNB, nb(ib), nb(ib), true};
+            const Operand B2{Y, nullptr, kNB, nb(jb), nb(ib), (rr % 4) == 0};
+            tile_gemm<T, false>(A2, B2, nb(ib), nb(jb), nb(ib), Tf + ib * kNB * r + jb * kNB, r, T(-1), T(0), As,
+                                Bs);
+        }
+}
+
+// factor + invert for the matrices with (st & mask) == val
+template <typename T>
+static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
+                         bool rare);
+
 template <typename T>
 static int invert(const ChainCtx& c, int mask, int val) {
     const Plan& p = *c.p;
@@ -1037,6 +1195,31 @@ static int invert(const ChainCtx& c, int mask, int val) {
     return 0;
 }
 
+// `rare`: a fallback path that usually has no matrix to work on, where one launch (instead of
+// about 15 that return at once) is what counts; the common paths keep the multi-launch
+// factorization, which spreads the panel and trailing products over many CUs.
+template <typename T>
+static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
+                         bool rare) {
+    const Plan& p = *c.p;
+    if (!rare || p.nblk > kFusedMaxBlocks) {
+        int e;
+        if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, shift))) return e;
+        // a matrix marked by tau_bit here is refactored (shifted) by a later call, which inverts
+        return invert<T>(c, tau_bit ? (mask | tau_bit) : mask, val);
+    }
+    CholInvArgs a{};
+    a.W = c.ws + p.W; a.L = c.ws + p.L; a.Td = c.ws + p.Td; a.Tf = c.ws + p.Tf; a.Y = c.ws + p.W;
+    a.r = p.r; a.nblk = p.nblk;
+    a.st = c.st; a.st_mask = mask; a.st_val = val;
+    a.kap = (double*)(c.ws + p.kap);
+    a.tau = tau; a.fail_bit = fail_bit; a.tau_bit = tau_bit; a.shift = shift;
+    const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
+    a.c_shift = 11.0 * ((double)p.m * p.r + (double)p.r * (p.r + 1)) * u;
+    hipLaunchKernelGGL((cholinv_kernel<T>), dim3((unsigned)p.b), dim3(256), 0, c.s, a);
+    return (int)hipGetLastError();
+}
+
 // Pout = Pin Tf^T = Pin L^-T  (Tf lower: output column tile n0 needs only k < n0 + BN)
 template <typename T>
 static int apply(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val) {
@@ -1063,8 +1246,7 @@ static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int v
                        int tau_bit) {
     int e;
     if ((e = gram<T>(c, Pin, mask, val))) return e;
-    if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, 0))) return e;
-    if ((e = invert<T>(c, mask, val))) return e;
+    if ((e = factor_invert<T>(c, mask, val, tau, fail_bit, tau_bit, 0, false))) return e;
     return apply<T>(c, Pin, Pout, mask, val);
 }
 
@@ -1205,8 +1387,7 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
     }
     // the others: a full Cholesky pass (W is untouched for them)
     const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
-    if ((e = factor<T>(c, cmask, cval, 0.0, fail_bit, 0, 0))) return e;
-    if ((e = invert<T>(c, cmask, cval))) return e;
+    if ((e = factor_invert<T>(c, cmask, cval, 0.0, fail_bit, 0, 0, true))) return e;
     return apply<T>(c, Pin, Pout, cmask, cval);
 }
 
@@ -1403,9 +1584,8 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     // pass 1: unshifted attempt; a failed pivot or a large diagonal ratio marks SHIFT,
     // and the marked matrices factor W + s I instead (W is kept by the factorization)
     if ((e = gram<T>(c, P, A64 | F, A64))) return e;
-    if ((e = factor<T>(c, A64 | SH | F, A64, kTau64, SH, SH, 0))) return e;
-    if ((e = factor<T>(c, A64 | SH | F, A64 | SH, 0.0, F, 0, 1))) return e;
-    if ((e = invert<T>(c, A64 | F, A64))) return e;
+    if ((e = factor_invert<T>(c, A64 | SH | F, A64, kTau64, SH, SH, 0, false))) return e;
+    if ((e = factor_invert<T>(c, A64 | SH | F, A64 | SH, 0.0, F, 0, 1, true))) return e;
     if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
     // pass 2
     if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearIdIters64, kNearIdTerms64, kNearIdFast64, kNearId64, F)))

@@ -175,3 +175,18 @@ def test_wide_update_tiles(cuda, base):
     edges ragged, r = 72 padded to 96 in the split planes), fp32 and bf16 weights."""
     wl = W.SMALL[base].with_groups(W.Group(16, 520, 1000, 72), name=f"wide-tiles-{base}", steps=2)
     check(run_teacher_forced(wl, cuda), tol_for(wl))
+
+
+@pytest.mark.parametrize("force64", [False, True])
+def test_shifted_first_pass(cuda, force64):
+    """8 decades of spectrum: the fp64 chain's plain Cholesky of P0^T P0 breaks down (host fp64
+    Cholesky fails too) and the shifted first pass plus two plain passes take over; shifted
+    CholeskyQR3 in fp64 on the host stays within 4e-9 of the oracle's P Q^T on these inputs."""
+    import dataclasses
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = dataclasses.replace(W.SMALL[5], grad_args={"decades": 8.0}, name="shifted-8")
+    rep = run_teacher_forced(wl, cuda, options=dion.OPT_FORCE_F64 if force64 else 0, steps=2)
+    for _, t, _, flags in rep:
+        if t == 1:
+            assert np.all(flags & dion.FLAG_SHIFTED), flags
+    check(rep, tol_for(wl))
