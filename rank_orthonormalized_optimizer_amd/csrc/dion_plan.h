@@ -61,14 +61,22 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.nblk = (r + kNB - 1) / kNB;
     q.nchunk = (n + kNormChunk - 1) / kNormChunk;
     q.kp = (r + 31) / 32 * 32;
-    {   // split the Gram's long K (= m) until the grid has ~1024 tiles, keeping >= 128 rows per split
+    {   // split the Gram's long K (= m) over the grid: with three 64 x 64 workgroups resident per
+        // CU (the register budget of the fp64 tile), pick the split count minimizing
+        // rounds x (slabs per split + 3 slabs of fill and drain), keeping >= 128 rows per split
+        // and the partials within 512 MB
         const int64_t nt = (r + 63) / 64;
         const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
-        int64_t s = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
-        if (s > 16) s = 16;
-        if (s > m / 128) s = m / 128;
-        while (s > 1 && (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20)) --s;
-        q.gsplit = s < 1 ? 1 : s;
+        const int64_t slots = 256 * 3, slabs = (m + 15) / 16;
+        int64_t best = 1;
+        double best_cost = 0.0;
+        for (int64_t s = 1; s <= 16; ++s) {
+            if (s > 1 && (s > m / 128 || (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20))) break;
+            const double rounds = (double)((s * tiles + slots - 1) / slots);
+            const double cost = rounds * (double)((slabs + s - 1) / s + 3);
+            if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
+        }
+        q.gsplit = tiles > 0 ? best : 1;
     }
     size_t off = 0;
     auto take = [&](double bytes) { size_t o = off; off = align256(off + (size_t)bytes); return o; };

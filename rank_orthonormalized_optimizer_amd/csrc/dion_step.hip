@@ -870,6 +870,7 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const T* part, T* W, i
     W += bz * r * r;
     const int64_t total = r * r;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+        if (idx % r > idx / r) continue;            // the consumers read the lower triangle only
         T s = 0;
         for (int64_t q = 0; q < splits; ++q) s += part[q * total + idx];
         W[idx] = s;
