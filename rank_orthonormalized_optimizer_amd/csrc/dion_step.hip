@@ -607,167 +607,90 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
             }
 }
 
-// The weight pass for large stacks: 128 x 128 tiles of M and X per workgroup of eight waves.
-// Waves 0-3 multiply (a 64 x 64 sub-tile each, both products), waves 4-7 copy the split planes
-// of P, R and Q into double-buffered LDS (144 KB, one workgroup per CU).  The epilogue runs on
-// the multiplying waves in four 16-row chunks, the next chunk's loads issued before the
-// current chunk's stores.
+// The weight pass for large stacks: 128 x 64 tiles of M and X, four waves of 64 x 32 that
+// both stage (a copy of the split planes) and multiply, and a single-buffered 48 KB LDS stage
+// (two barriers per slab).  Two workgroups fit on a CU, so one workgroup's memory-bound
+// epilogue (the loads of each half-tile issued before its stores) runs while the other keeps
+// the matrix cores busy.
 template <bool G_BF16, bool X_BF16>
-__global__ __launch_bounds__(512) void update6_kernel(UpdArgs u) {
-    constexpr int BT = 128, PT = BT * kSplitK;
+__global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
+    constexpr int BM = 128, BN = 64, PA = BM * kSplitK, PB = BN * kSplitK, FM = 4, FN = 2;
     const TileId tid = xcd_tile_id();
-    const int bz = tid.z, m0 = tid.y * BT, n0 = tid.x * BT;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][9 * PT];   // P h m l | R h m l | Q h m l
-    const int wave = threadIdx.x >> 6;
-    const bool stager = wave >= 4;
-    const int st_t = threadIdx.x - 256;
+    const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * PA + 6 * PB];   // P h m l | R h m l | Q h m l
     const int64_t ps = (int64_t)u.m * u.kp, ns = (int64_t)u.n * u.kp;
     const Op6 oP{u.Pp + (int64_t)bz * 3 * ps, nullptr, u.kp, ps, u.m, u.kp, true};
     const Op6 oR{u.Rp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
     const Op6 oQ{u.Qp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
-    Loader6<BT, S6_PLANES, A6_NONE> lp, lr, lq;
-    const int lane = threadIdx.x & 63, wm = (wave >> 1) & 1, wn = wave & 1;
+    Loader6<BM, S6_PLANES, A6_NONE> lp;
+    Loader6<BN, S6_PLANES, A6_NONE> lr, lq;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     const int fr = lane & 15, fc = lane >> 4;
-    f32x4 acc1[4][4], acc2[4][4];
+    f32x4 acc1[FM][FN], acc2[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
-    auto stage_load = [&](int k) {
-        lp.load(oP, m0, k, st_t);
-        lr.load(oR, n0, k, st_t);
-        lq.load(oQ, n0, k, st_t);
+        for (int j = 0; j < FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
+    auto load = [&](int k) {
+        lp.load(oP, m0, k, t);
+        lr.load(oR, n0, k, t);
+        lq.load(oQ, n0, k, t);
     };
-    auto stage_store = [&](int b) {
-        lp.store(lds[b], st_t);
-        lr.store(lds[b] + 3 * PT, st_t);
-        lq.store(lds[b] + 6 * PT, st_t);
+    auto store = [&]() {
+        lp.store(lds, t);
+        lr.store(lds + 3 * PA, t);
+        lq.store(lds + 3 * PA + 3 * PB, t);
     };
-    // the two roles run separate loops (disjoint register live ranges) with one barrier per slab
-    if (stager) {
-        stage_load(0);
-        stage_store(0);
-        if (kSplitK < u.kp) stage_load(kSplitK);
-        __syncthreads();
-        int buf = 0;
-        for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
-            if (k0 + kSplitK < u.kp) {
-                stage_store(buf ^ 1);
-                if (k0 + 2 * kSplitK < u.kp) stage_load(k0 + 2 * kSplitK);
-            }
-            __syncthreads();
-            buf ^= 1;
-        }
-    } else {
-        __syncthreads();
-        int buf = 0;
-        for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
-            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc1, wm * 64, wn * 64, fr, fc);
-            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 6 * PT, acc2, wm * 64, wn * 64, fr, fc);
-            __syncthreads();
-            buf ^= 1;
-        }
-    }
-    // Epilogue: the two product tiles go through LDS (row-major, rows padded to 132 floats so the
-    // MFMA-layout writes spread over all banks); then all eight waves update M and X with
-    // four-element row-contiguous accesses, every load of a half-tile issued before its stores.
-    constexpr int LDC = BT + 4;
-    float* c1 = (float*)&lds[0][0];
-    float* c2 = c1 + BT * LDC;
-    static_assert(2 * BT * LDC * 4 <= (int)sizeof(lds), "product tiles fit in the operand buffers");
-    if (!stager) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = wm * 64 + 16 * i + 4 * fc + v, c = wn * 64 + 16 * j + fr;
-                    c1[r * LDC + c] = acc1[i][j][v];
-                    c2[r * LDC + c] = acc2[i][j][v];
-                }
-    }
+    load(0);
+    store();
     __syncthreads();
+    for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
+        const bool more = k0 + kSplitK < u.kp;
+        if (more) load(k0 + kSplitK);
+        mma6_slab<BM, BN, FM, FN>(lds, lds + 3 * PA, acc1, wm * 64, wn * 32, fr, fc);
+        mma6_slab<BM, BN, FM, FN>(lds, lds + 3 * PA + 3 * PB, acc2, wm * 64, wn * 32, fr, fc);
+        __syncthreads();
+        if (more) {
+            store();
+            __syncthreads();
+        }
+    }
+    // epilogue in the MFMA layout, in two halves of rows: all loads of a half before its stores
     const int64_t mn = (int64_t)u.m * u.n;
     float* Mp = u.M + bz * mn;
-    const bool vec = (u.n % 4) == 0 && m0 + BT <= u.m && n0 + BT <= u.n;
-    const int t = threadIdx.x;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        // four-column groups g = t + 512 q of the half-tile's 64 rows x 32 groups
-        float4 mv[4], gv[4], xv[4];
-        int64_t loc[4];
+        float mv[2][FN][4], gv[2][FN][4], xv[2][FN][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int g = t + 512 * q, r = 64 * h + (g >> 5), c = 4 * (g & 31);
-            loc[q] = (int64_t)(m0 + r) * u.n + n0 + c;
-            if (vec) {
-                mv[q] = *(const float4*)(Mp + loc[q]);
-                if constexpr (G_BF16) {
-                    const uint2 w = *(const uint2*)((const uint16_t*)u.G + bz * mn + loc[q]);
-                    gv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
-                                   bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
-                } else {
-                    gv[q] = *(const float4*)((const float*)u.G + bz * mn + loc[q]);
-                }
-                if constexpr (X_BF16) {
-                    const uint2 w = *(const uint2*)((const uint16_t*)u.X + bz * mn + loc[q]);
-                    xv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
-                                   bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
-                } else {
-                    xv[q] = *(const float4*)((const float*)u.X + bz * mn + loc[q]);
-                }
-            } else {
-                float tm[4], tg[4], tx[4];
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool in = m0 + r < u.m && n0 + c + e < u.n;
-                    const int64_t l = in ? loc[q] + e : 0, off = bz * mn + l;
-                    tm[e] = Mp[l];
-                    if constexpr (G_BF16) tg[e] = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
-                    else tg[e] = ((const float*)u.G)[off];
-                    if constexpr (X_BF16) tx[e] = bf16_bits_to_float(((const uint16_t*)u.X)[off]);
-                    else tx[e] = ((const float*)u.X)[off];
-                }
-                mv[q] = float4{tm[0], tm[1], tm[2], tm[3]};
-                gv[q] = float4{tg[0], tg[1], tg[2], tg[3]};
-                xv[q] = float4{tx[0], tx[1], tx[2], tx[3]};
-            }
-        }
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int g = t + 512 * q, r = 64 * h + (g >> 5), c = 4 * (g & 31);
-            const float4 p1 = *(const float4*)&c1[r * LDC + c];
-            const float4 p2 = *(const float4*)&c2[r * LDC + c];
-            const float m4[4] = {mv[q].x, mv[q].y, mv[q].z, mv[q].w}, g4[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
-            const float x4[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-            const float a1[4] = {p1.x, p1.y, p1.z, p1.w}, a2[4] = {p2.x, p2.y, p2.z, p2.w};
-            float mo[4], xo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                mo[e] = (m4[e] + g4[e]) - u.one_minus_mu * a1[e];
-                xo[e] = x4[e] - u.lr_s * a2[e];
-            }
-            if (vec) {
-                *(float4*)(Mp + loc[q]) = float4{mo[0], mo[1], mo[2], mo[3]};
-                if constexpr (X_BF16) {
-                    const uint2 w = {(uint32_t)float_to_bf16_bits(xo[0]) | ((uint32_t)float_to_bf16_bits(xo[1]) << 16),
-                                     (uint32_t)float_to_bf16_bits(xo[2]) | ((uint32_t)float_to_bf16_bits(xo[3]) << 16)};
-                    *(uint2*)((uint16_t*)u.X + bz * mn + loc[q]) = w;
-                } else {
-                    *(float4*)((float*)u.X + bz * mn + loc[q]) = float4{xo[0], xo[1], xo[2], xo[3]};
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 2 * h + ii;
+                    const int row = m0 + wm * 64 + 16 * i + 4 * fc + v, col = n0 + wn * 32 + 16 * j + fr;
+                    const int64_t l = (row < u.m && col < u.n) ? (int64_t)row * u.n + col : 0, off = bz * mn + l;
+                    mv[ii][j][v] = Mp[l];
+                    if constexpr (G_BF16) gv[ii][j][v] = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
+                    else gv[ii][j][v] = ((const float*)u.G)[off];
+                    if constexpr (X_BF16) xv[ii][j][v] = bf16_bits_to_float(((const uint16_t*)u.X)[off]);
+                    else xv[ii][j][v] = ((const float*)u.X)[off];
                 }
-            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (m0 + r >= u.m || n0 + c + e >= u.n) continue;
-                    const int64_t l = loc[q] + e, off = bz * mn + l;
-                    Mp[l] = mo[e];
-                    if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(xo[e]);
-                    else ((float*)u.X)[off] = xo[e];
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 2 * h + ii;
+                    const int row = m0 + wm * 64 + 16 * i + 4 * fc + v, col = n0 + wn * 32 + 16 * j + fr;
+                    if (row >= u.m || col >= u.n) continue;
+                    const int64_t l = (int64_t)row * u.n + col, off = bz * mn + l;
+                    Mp[l] = (mv[ii][j][v] + gv[ii][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                    const float x = xv[ii][j][v] - u.lr_s * acc2[i][j][v];
+                    if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(x);
+                    else ((float*)u.X)[off] = x;
                 }
-            }
-        }
     }
 }
 
@@ -1617,11 +1540,11 @@ static hipError_t launch_update(const Plan& p, const char* ws, float* M, const v
     u.m = (int)p.m; u.n = (int)p.n; u.kp = (int)p.kp;
     u.one_minus_mu = 1.0f - mu;
     u.lr_s = (float)((double)lr * sqrt((double)p.m / (double)p.n));
-    // 128 x 128 tiles (half the operand traffic per output) while they still fill the chip
-    const int64_t big = ((p.n + 127) / 128) * ((p.m + 127) / 128) * p.b;
+    // 128 x 64 tiles while they still fill the chip, else 64 x 64
+    const int64_t big = ((p.n + 63) / 64) * ((p.m + 127) / 128) * p.b;
     if (big >= kUpdBigMinTiles) {
-        dim3 grid((unsigned)((p.n + 127) / 128), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
-        hipLaunchKernelGGL((update6_kernel<GB, XB>), grid, dim3(512), 0, s, u);
+        dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
+        hipLaunchKernelGGL((update3_kernel<GB, XB>), grid, dim3(256), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
         hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB>), grid, dim3(256), 0, s, u);
