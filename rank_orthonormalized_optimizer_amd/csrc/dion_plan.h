@@ -10,7 +10,7 @@ namespace dion {
 // column blocks of this width; the last one may be narrower).
 constexpr int kNB = 64;
 // Row chunk of the column-norm partial sums.
-constexpr int kNormChunk = 256;
+constexpr int kNormChunk = 64;
 
 // Per-matrix state word kept in the workspace during a call.
 enum : int {

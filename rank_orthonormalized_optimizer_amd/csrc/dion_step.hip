@@ -418,59 +418,84 @@ __global__ __launch_bounds__(256) void colscale_kernel(const double* part, doubl
     cs[bz * r + col] = 1.0 / (sqrt(s) + eps);
 }
 
+// Four consecutive k of one row of an r-column array (fp64 chain: rounded from R64 / P64 and
+// written back to the fp32 copy; fp32 chain: read from it), zero at k >= r.  `vec`: r % 4 == 0,
+// so a group lies inside the row and 32-byte aligned.
+__device__ __forceinline__ void row4(const double* p64src, float* p32, int64_t o, int64_t k, int64_t r, bool p64,
+                                     bool vec, double (&v)[4]) {
+    if (vec && k < r) {
+        if (p64) {
+            const double4 d = *(const double4*)(p64src + o);
+            v[0] = d.x; v[1] = d.y; v[2] = d.z; v[3] = d.w;
+            *(float4*)(p32 + o) = float4{(float)d.x, (float)d.y, (float)d.z, (float)d.w};
+        } else {
+            const float4 f = *(const float4*)(p32 + o);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = 0.0;
+        if (k + e < r) {
+            if (p64) { v[e] = p64src[o + e]; p32[o + e] = (float)v[e]; }
+            else v[e] = p32[o + e];
+        }
+    }
+}
+
 // Q <- R * c (fp32), for fp64-chain matrices R32 <- R64 rounded, and the bf16 split planes of
-// R32 and Q (k padded to kp with zeros) for the weight pass.
+// R32 and Q (k padded to kp with zeros) for the weight pass; four k per thread.
 __global__ __launch_bounds__(256) void next_q_kernel(const double* R64, float* R32, const double* cs, float* Q,
                                                      uint16_t* Rp, uint16_t* Qp, int64_t n, int64_t r, int64_t kp,
                                                      const int* st) {
     const int bz = blockIdx.y;
-    const bool p64 = (st[bz] & ST_PATH64) != 0;
-    const int64_t nr = n * r, total = n * kp;
+    const bool p64 = (st[bz] & ST_PATH64) != 0, vec = (r % 4) == 0;
+    const int64_t nr = n * r, total = n * kp, groups = total / 4, gpr = kp / 4;
     uint16_t* rp = Rp + bz * 3 * total;
     uint16_t* qp = Qp + bz * 3 * total;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int64_t i = idx / kp, k = idx % kp;
-        float rv = 0.f, qv = 0.f;
-        if (k < r) {
-            const int64_t o = bz * nr + i * r + k;
-            const double c = cs[bz * r + k];
-            double v;
-            if (p64) {
-                v = R64[o];
-                rv = (float)v;
-                R32[o] = rv;
-            } else {
-                rv = R32[o];
-                v = (double)rv;
-            }
-            qv = (float)(v * c);
-            Q[o] = qv;
+    const double* c = cs + bz * r;
+    for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
+        const int64_t i = gi / gpr, k = 4 * (gi % gpr), o = bz * nr + i * r + k;
+        double v[4];
+        row4(R64, R32, o, k, r, p64, vec, v);
+        float rv[4], qv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rv[e] = (float)v[e];
+            qv[e] = k + e < r ? (float)(v[e] * c[k + e]) : 0.f;
         }
-        split3(rv, rp[idx], rp[total + idx], rp[2 * total + idx]);
-        split3(qv, qp[idx], qp[total + idx], qp[2 * total + idx]);
+        if (vec && k < r) *(float4*)(Q + o) = float4{qv[0], qv[1], qv[2], qv[3]};
+        else
+#pragma unroll
+            for (int e = 0; e < 4; ++e) if (k + e < r) Q[o + e] = qv[e];
+        const Parts4 pr = split4(rv), pq = split4(qv);
+        const int64_t pidx = i * kp + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            *(u32x2*)(rp + q * total + pidx) = pr.p[q];
+            *(u32x2*)(qp + q * total + pidx) = pq.p[q];
+        }
     }
 }
 
-// P32 <- P64 rounded for fp64-chain matrices, and the bf16 split planes of P32 for all.
+// P32 <- P64 rounded for fp64-chain matrices, and the bf16 split planes of P32 for all; four
+// k per thread.
 __global__ __launch_bounds__(256) void split_p_kernel(const double* P64, float* P32, uint16_t* Pp, int64_t m,
                                                       int64_t r, int64_t kp, const int* st) {
     const int bz = blockIdx.y;
-    const bool p64 = (st[bz] & ST_PATH64) != 0;
-    const int64_t mr = m * r, total = m * kp;
+    const bool p64 = (st[bz] & ST_PATH64) != 0, vec = (r % 4) == 0;
+    const int64_t mr = m * r, total = m * kp, groups = total / 4, gpr = kp / 4;
     uint16_t* pp = Pp + bz * 3 * total;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int64_t i = idx / kp, k = idx % kp;
-        float v = 0.f;
-        if (k < r) {
-            const int64_t o = bz * mr + i * r + k;
-            if (p64) {
-                v = (float)P64[o];
-                P32[o] = v;
-            } else {
-                v = P32[o];
-            }
-        }
-        split3(v, pp[idx], pp[total + idx], pp[2 * total + idx]);
+    for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
+        const int64_t i = gi / gpr, k = 4 * (gi % gpr), o = bz * mr + i * r + k;
+        double v[4];
+        row4(P64, P32, o, k, r, p64, vec, v);
+        const float f[4] = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        const Parts4 pr = split4(f);
+        const int64_t pidx = i * kp + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *(u32x2*)(pp + q * total + pidx) = pr.p[q];
     }
 }
 
@@ -1604,12 +1629,12 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
         hipLaunchKernelGGL(colscale_kernel, g2, dim3(256), 0, s, (const double*)(ws + p.part), (double*)(ws + p.cs),
                            p.r, (int)p.nchunk, (double)eps);
         DION_TRY(hipGetLastError());
-        dim3 g3(grid_1d(p.n * p.kp, 1024), (unsigned)p.b);
+        dim3 g3(grid_1d(p.n * p.kp / 4, 1024), (unsigned)p.b);
         hipLaunchKernelGGL(next_q_kernel, g3, dim3(256), 0, s, (const double*)(ws + p.R64), (float*)(ws + p.R32),
                            (const double*)(ws + p.cs), Q, (uint16_t*)(ws + p.Rp), (uint16_t*)(ws + p.Qp), p.n, p.r,
                            p.kp, c.st);
         DION_TRY(hipGetLastError());
-        dim3 g4(grid_1d(p.m * p.kp, 1024), (unsigned)p.b);
+        dim3 g4(grid_1d(p.m * p.kp / 4, 1024), (unsigned)p.b);
         hipLaunchKernelGGL(split_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
                            (uint16_t*)(ws + p.Pp), p.m, p.r, p.kp, c.st);
         DION_TRY(hipGetLastError());
