@@ -154,6 +154,7 @@ struct Loader6<BX, S6_PLANES, ADD> {
             for (int p = 0; p < 3; ++p) *(u32x4*)&lds[p * BX * kSplitK + off] = r[p][q];
         }
     }
+    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const { store(lds, t); }
 };
 
 // k-contiguous fp32 (+ addend): BX * 8 groups of four k, BX / 32 per thread (8 threads per row).
@@ -213,6 +214,19 @@ struct Loader6<BX, S6_KC, ADD> {
 #pragma unroll
         for (int q = 0; q < PER; ++q) store4(lds, BX * kSplitK, (t >> 3) + 32 * q, 4 * (t & 7), sp[q]);
     }
+    // split and store group by group (no register copy of the whole split slab)
+    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ADD == A6_NONE) v[e] = a[q][e];
+                else v[e] = sum6<ADD>(a[q][e], b[q][e]);
+            }
+            store4(lds, BX * kSplitK, (t >> 3) + 32 * q, 4 * (t & 7), split4(v));
+        }
+    }
 };
 
 // x-contiguous fp32 (+ addend): thread owns one x and BX / 8 consecutive k (coalesced along x).
@@ -266,6 +280,19 @@ struct Loader6<BX, S6_XC, ADD> {
 #pragma unroll
         for (int g = 0; g < KPT / 4; ++g) store4(lds, BX * kSplitK, x, kb + 4 * g, sp[g]);
     }
+    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
+        const int x = t % BX, kb = (t / BX) * KPT;
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ADD == A6_NONE) v[e] = a[4 * g + e];
+                else v[e] = sum6<ADD>(a[4 * g + e], b[4 * g + e]);
+            }
+            store4(lds, BX * kSplitK, x, kb + 4 * g, split4(v));
+        }
+    }
 };
 
 // acc[i][j] (wave sub-tile FM x FN blocks of 16 x 16) += A B over one 32-k slab from the part
@@ -291,6 +318,38 @@ __device__ __forceinline__ void mma6_slab(const uint16_t* lA, const uint16_t* lB
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = mma_bf16(a[i], b[j][pb], acc[i][j]);
+    }
+}
+
+// Two products sharing A (acc1 += A B1, acc2 += A B2) over one slab: A fragments of all three
+// parts are read once, then per column block the B1 and B2 fragments of all three parts; the six
+// kept products of each pair in the same increasing order as mma6_slab.
+template <int BXA, int BXB, int FM, int FN>
+__device__ __forceinline__ void mma6_slab2(const uint16_t* lA, const uint16_t* lB1, const uint16_t* lB2,
+                                           f32x4 (&acc1)[FM][FN], f32x4 (&acc2)[FM][FN], int ra, int rb, int fr,
+                                           int fc) {
+    u32x4 a[3][FM];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[p][i] = *(const u32x4*)&lA[p * BXA * kSplitK + part_off(ra + 16 * i + fr, fc)];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        u32x4 b1[3], b2[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            b1[p] = *(const u32x4*)&lB1[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
+            b2[p] = *(const u32x4*)&lB2[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
+        }
+#pragma unroll
+        for (int pa = 2; pa >= 0; --pa)
+#pragma unroll
+            for (int pb = 2 - pa; pb >= 0; --pb)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    acc1[i][j] = mma_bf16(a[pa][i], b1[pb], acc1[i][j]);
+                    acc2[i][j] = mma_bf16(a[pa][i], b2[pb], acc2[i][j]);
+                }
     }
 }
 

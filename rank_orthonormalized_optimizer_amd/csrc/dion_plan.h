@@ -22,7 +22,7 @@ enum : int {
 };
 
 // Partial sums of squares per matrix written by the near-identity test (fixed-order reduction).
-constexpr int kNearIdParts = 16;
+constexpr int kNearIdParts = 256;
 
 struct Plan {
     int64_t m, n, b, r;

@@ -29,7 +29,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "dion.h"
 #include "dion_plan.h"
@@ -74,8 +76,11 @@ struct GemmArgs {
                                // diagonal halved, upper part zero (square outputs only)
 };
 
+// fp64 tiles are held to 128 registers a lane so that four workgroups share a CU (their LDS
+// is 40 KB each): the fp64 MFMA has a long issue time, and more resident waves keep it fed
+// across the per-slab barriers.
 template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmArgs g) {
     using C = TileCfg<T, BM, BN, BK>;
     const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
     const TileId tid = xcd_tile_id();
@@ -209,8 +214,11 @@ static hipError_t launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t s) {
 // and invert the factor (both kept in LDS)
 // ---------------------------------------------------------------------------
 struct PotrfArgs {
-    void* L; int64_t ldl, sL;   // factor in place (elements)
-    void* Td; int64_t sTd;      // [nblk][kNB][kNB] inverses of the diagonal blocks
+    void* L; int64_t ldl, sL;   // factor (elements); the block is read from S (same layout), which may be L
+    const void* S;
+    void* Td; int64_t sTd;      // inverses of the diagonal blocks: block jblk at Td + jblk * blkTd, pitch ldTd
+    int64_t ldTd, blkTd;
+    int tdfull;                 // write the whole kNB x kNB block (zeros outside nbj x nbj), else nbj x nbj only
     int j0, nbj, jblk;
     int* st; int st_mask, st_val;
     double* kap;                // [batch][2] running min / max of diag(L)
@@ -306,11 +314,13 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
     c.i = c.tid >> 2; c.part = c.tid & 3;
     c.row_ok = c.i < c.nbj;
     c.ok = true;
-    c.Lrow = L + (int64_t)(p.j0 + (c.row_ok ? c.i : 0)) * p.ldl + p.j0;
+    const int64_t roff = (int64_t)(p.j0 + (c.row_ok ? c.i : 0)) * p.ldl + p.j0;
+    c.Lrow = L + roff;
+    const T* Srow = (const T*)p.S + bz * p.sL + roff;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int j = 4 * s + c.part;
-        c.a[s] = (c.row_ok && j <= c.i) ? c.Lrow[j] : T(0);
+        c.a[s] = (c.row_ok && j <= c.i) ? Srow[j] : T(0);
         c.x[s] = (j == c.i) ? T(1) : T(0);
     }
     DiagSteps<T, 0>::run(c);
@@ -332,13 +342,13 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         kp[0] = mn; kp[1] = mx;
         if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
     }
-    T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * NB * NB;
+    T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * p.blkTd;
     const T rinv = c.row_ok ? T(1) / sm.dg[i] : T(0);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int j = 4 * s + part;
         if (c.row_ok && j <= i) c.Lrow[j] = c.a[s];
-        Td[i * NB + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
+        if (p.tdfull || (c.row_ok && j < nbj)) Td[i * p.ldTd + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
     }
     return true;
 }
@@ -672,8 +682,7 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
         const bool more = k0 + kSplitK < u.kp;
         if (more) load(k0 + kSplitK);
-        mma6_slab<BM, BN, FM, FN>(lds, lds + 3 * PA, acc1, wm * 64, wn * 32, fr, fc);
-        mma6_slab<BM, BN, FM, FN>(lds, lds + 3 * PA + 3 * PB, acc2, wm * 64, wn * 32, fr, fc);
+        mma6_slab2<BM, BN, FM, FN>(lds, lds + 3 * PA, lds + 3 * PA + 3 * PB, acc1, acc2, wm * 64, wn * 32, fr, fc);
         __syncthreads();
         if (more) {
             store();
@@ -805,9 +814,10 @@ struct ChainCtx {
 // CholeskyQR building blocks on P [b][m][r], for the matrices with (st & mask) == val.
 // gram:    W = P^T P (lower tiles)
 // factor:  L = chol(W (+ s I)) by blocks of kNB columns (right-looking), with the inverse
-//          of every diagonal block kept in Td; a failed pivot sets `fail_bit`, a diagonal
-//          ratio above `tau` (tau > 0) sets `tau_bit`
-// invert:  Tf = L^-1;   apply: Pout = Pin Tf^T
+//          of every diagonal block written to the matching diagonal block of Tf; a failed
+//          pivot sets `fail_bit`, a diagonal ratio above `tau` (tau > 0) sets `tau_bit`
+// invert:  Tf = L^-1 (its lower off-diagonal blocks);   apply: Pout = Pin Tf^T
+// The blocks of Tf above the diagonal are never written: every consumer skips them.
 // W = sum over the K-splits of the partial Grams, in split order (lower triangle).
 template <typename T>
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const T* part, T* W, int64_t r, int64_t splits,
@@ -825,8 +835,10 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const T* part, T* W, i
     }
 }
 
+// W = P^T P; a split Gram leaves its partials in gpart and, unless `reduce` is false (the
+// caller then sums them itself), adds them into W.
 template <typename T>
-static int gram(const ChainCtx& c, const T* P, int mask, int val) {
+static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = true) {
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     constexpr int S = SrcOf<T>::v;
@@ -853,6 +865,7 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val) {
     g.sc = splits * r * r * (int64_t)sizeof(T);
     g.gc = r * r * (int64_t)sizeof(T);
     DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
+    if (!reduce) return 0;
     dim3 grid(grid_1d(r * r, 512), (unsigned)p.b);
     hipLaunchKernelGGL((gram_reduce_kernel<T>), grid, dim3(256), 0, c.s, (const T*)(c.ws + p.gpart), (T*)(c.ws + p.W),
                        r, splits, c.st, mask, val);
@@ -866,11 +879,14 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
     const int64_t m = p.m, r = p.r, b = p.b;
     T* W = (T*)(c.ws + p.W);
     T* L = (T*)(c.ws + p.L);
-    T* Td = (T*)(c.ws + p.Td);
+    T* Tf = (T*)(c.ws + p.Tf);
     double* kap = (double*)(c.ws + p.kap);
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
-    {
+    const int64_t rr = r * r * (int64_t)sizeof(T);
+    // Unshifted, the first block column reads W and writes L (W stays intact for a shifted
+    // retry); shifted, L = W + s I is formed first.
+    if (shift) {
         const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
         const double c_shift = 11.0 * ((double)m * r + (double)r * (r + 1)) * u;
         dim3 grid(grid_1d(r * r, 1024), (unsigned)b);
@@ -881,9 +897,11 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         const int j0 = (int)(jb * kNB);
         const int nbj = (int)((r - j0) < kNB ? (r - j0) : kNB);
         const int rest = (int)(r - j0 - nbj);
+        const T* src = (jb == 0 && !shift) ? W : L;
         PotrfArgs pa{};
-        pa.L = L; pa.ldl = r; pa.sL = r * r;
-        pa.Td = Td; pa.sTd = p.nblk * kNB * kNB;
+        pa.L = L; pa.ldl = r; pa.sL = r * r; pa.S = src;
+        // the inverted diagonal blocks go straight into the diagonal of Tf = L^-1
+        pa.Td = Tf; pa.sTd = r * r; pa.ldTd = r; pa.blkTd = kNB * (r + 1); pa.tdfull = 0;
         pa.j0 = j0; pa.nbj = nbj; pa.jblk = (int)jb;
         pa.st = c.st; pa.st_mask = mask; pa.st_val = val;
         pa.kap = kap; pa.first = jb == 0; pa.last = jb == p.nblk - 1;
@@ -891,48 +909,32 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         hipLaunchKernelGGL((potrf_diag_kernel<T>), dim3((unsigned)b), dim3(256), 0, c.s, pa);
         DION_TRY(hipGetLastError());
         if (rest > 0) {
-            T* below = L + (int64_t)(j0 + nbj) * r + j0;
-            // panel: L21 <- L21 Td^T (in place; one column tile covers all nbj columns)
+            const int64_t ob = (int64_t)(j0 + nbj) * r + j0, ot = (int64_t)(j0 + nbj) * (r + 1);
+            T* below = L + ob;
+            // panel: L21 <- S21 Td^T (one column tile covers all nbj columns, so in place is safe)
             GemmArgs g{};
-            g.a = Operand{below, nullptr, r, rest, nbj, vr};
-            g.b = Operand{Td + jb * kNB * kNB, nullptr, kNB, nbj, nbj, true};
-            g.sa0 = r * r * (int64_t)sizeof(T);
-            g.sb0 = p.nblk * kNB * kNB * (int64_t)sizeof(T);
-            g.c = below; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
+            g.a = Operand{src + ob, nullptr, r, rest, nbj, vr};
+            g.b = Operand{Tf + (int64_t)j0 * (r + 1), nullptr, r, nbj, nbj, vr};
+            g.sa0 = rr;
+            g.sb0 = rr;
+            g.c = below; g.ldc = r; g.sc = rr;
             g.M = rest; g.N = nbj; g.K = nbj;
             g.alpha = 1; g.beta = 0;
             g.st = c.st; g.st_mask = mask; g.st_val = val;
             DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
             // trailing: L22 <- L22 - L21 L21^T (lower tiles only)
             GemmArgs h = g;
+            h.a = Operand{below, nullptr, r, rest, nbj, vr};
             h.b = Operand{below, nullptr, r, rest, nbj, vr};
-            h.sb0 = r * r * (int64_t)sizeof(T);
-            h.c = L + (int64_t)(j0 + nbj) * r + (j0 + nbj);
+            h.sb0 = rr;
+            h.c = L + ot;
+            if (src != L) h.csrc = src + ot;
             h.M = rest; h.N = rest; h.K = nbj;
             h.alpha = -1; h.beta = 1; h.lower = 1;
             DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(h, b, c.s)));
         }
     }
     return 0;
-}
-
-// Tf = L^-1 (lower, [b][r][r]) from the factor L and the inverted diagonal blocks Td, by
-// recursive doubling over the blocks: for neighbouring block ranges U (above) and V (below)
-// whose inverses are known, T_VU = -T_VV (L_VU T_UU).  log2(nblk) levels of two batched GEMMs;
-// the product L_VU T_UU is parked in W (free once the factor is accepted).
-template <typename T>
-__global__ __launch_bounds__(256) void init_tinv_kernel(const T* Td, T* Tf, int64_t r, int64_t nblk, const int* st,
-                                                        int st_mask, int st_val) {
-    const int bz = blockIdx.y;
-    if ((st[bz] & st_mask) != st_val) return;
-    Tf += bz * r * r;
-    Td += bz * nblk * kNB * kNB;
-    const int64_t total = r * r;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int64_t i = idx / r, k = idx % r;
-        const int64_t bi = i / kNB, bk = k / kNB;
-        Tf[idx] = (bi == bk) ? Td[(bi * kNB + (i % kNB)) * kNB + (k % kNB)] : T(0);
-    }
 }
 
 template <typename T>
@@ -1040,8 +1042,8 @@ __global__ __launch_bounds__(256) void cholinv_kernel(CholInvArgs a) {
     auto nb = [&](int64_t jb) { return (int)((r - jb * kNB) < kNB ? (r - jb * kNB) : kNB); };
     for (int64_t jb = 0; jb < nblk; ++jb) {
         PotrfArgs pa{};
-        pa.L = a.L; pa.ldl = r; pa.sL = rr;
-        pa.Td = a.Td; pa.sTd = nblk * kNB * kNB;
+        pa.L = a.L; pa.ldl = r; pa.sL = rr; pa.S = a.L;
+        pa.Td = a.Td; pa.sTd = nblk * kNB * kNB; pa.ldTd = kNB; pa.blkTd = kNB * kNB; pa.tdfull = 1;
         pa.j0 = (int)(jb * kNB); pa.nbj = nb(jb); pa.jblk = (int)jb;
         pa.st = a.st; pa.kap = a.kap;
         pa.first = jb == 0; pa.last = jb == nblk - 1;
@@ -1090,6 +1092,10 @@ template <typename T>
 static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
                          bool rare);
 
+// Tf = L^-1 (lower, [b][r][r]) from the factor L and the inverted diagonal blocks already in
+// Tf, by recursive doubling over the blocks: for neighbouring block ranges U (above) and V
+// (below) whose inverses are known, T_VU = -T_VV (L_VU T_UU).  log2(nblk) levels of two batched
+// GEMMs; the product L_VU T_UU is parked in W (free once the factor is accepted).
 template <typename T>
 static int invert(const ChainCtx& c, int mask, int val) {
     const Plan& p = *c.p;
@@ -1099,12 +1105,6 @@ static int invert(const ChainCtx& c, int mask, int val) {
     T* Y = (T*)(c.ws + p.W);
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
-    {
-        dim3 grid(grid_1d(r * r, 1024), (unsigned)b);
-        hipLaunchKernelGGL((init_tinv_kernel<T>), grid, dim3(256), 0, c.s, (const T*)(c.ws + p.Td), Tf, r, p.nblk,
-                           c.st, mask, val);
-        DION_TRY(hipGetLastError());
-    }
     const int64_t rr = r * r * (int64_t)sizeof(T);
     for (int64_t s = 1; s < p.nblk; s *= 2) {
         const int64_t span = 2 * s * kNB;               // rows/cols of one group
@@ -1209,20 +1209,35 @@ static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int v
 //                               and S <- F - F S nn times (truncation eps^(nn + 2))  [ST_SERIES]
 //   eps > tau_chol (or not finite): the blocked Cholesky pass                        [ST_CHOL2]
 // all decided per matrix on the device.
+// Setup of a re-orthonormalization pass (grid: parts x matrices): W = the sum of the split-K
+// Gram partials in split order (when the Gram was split; lower triangle), F = Phi(E) with
+// E = W - I, and per workgroup the sum of squares of E over its share.  (A last-arriving
+// workgroup could decide in place, but its device-scope fence writes back the L2 of every XCD;
+// a separate launch is cheaper.)
 template <typename T>
-__global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, double* part, int64_t r,
-                                                           const int* st, int st_mask, int st_val) {
+__global__ __launch_bounds__(256) void near_id_setup_kernel(const T* gpart, int64_t splits, T* W, T* F,
+                                                            double* part, int64_t r, const int* st, int st_mask,
+                                                            int st_val) {
     const int bz = blockIdx.y;
     if ((st[bz] & st_mask) != st_val) return;
-    W += bz * r * r;
-    F += bz * r * r;
     const int64_t total = r * r;
+    W += bz * total;
+    F += bz * total;
+    if (gpart) gpart += bz * splits * total;
     double ss = 0.0;   // sum of squares of E over the full symmetric matrix
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
         const int64_t i = idx / r, k = idx % r;
         T v = T(0);
         if (k <= i) {
-            const T e = W[idx] - (i == k ? T(1) : T(0));
+            T w;
+            if (gpart) {
+                w = 0;
+                for (int64_t q = 0; q < splits; ++q) w += gpart[q * total + idx];
+                W[idx] = w;
+            } else {
+                w = W[idx];
+            }
+            const T e = w - (i == k ? T(1) : T(0));
             const double d = (double)e;
             ss += (i == k ? 1.0 : 2.0) * d * d;
             v = (i == k) ? T(0.5) * e : e;
@@ -1230,6 +1245,7 @@ __global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, dou
         F[idx] = v;
     }
     __shared__ double red[256];
+    __shared__ int last;
     red[threadIdx.x] = ss;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -1239,6 +1255,7 @@ __global__ __launch_bounds__(256) void near_id_init_kernel(const T* W, T* F, dou
     if (threadIdx.x == 0) part[(int64_t)bz * kNearIdParts + blockIdx.x] = red[0];
 }
 
+// Regime bits of each selected matrix from ||E||_F, the partial sums added in part order.
 __global__ void near_id_decide_kernel(const double* part, int nparts, int* st, int64_t b, int st_mask, int st_val,
                                       double tau_fast, double tau_chol) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1246,10 +1263,10 @@ __global__ void near_id_decide_kernel(const double* part, int nparts, int* st, i
     double ss = 0.0;
     for (int q = 0; q < nparts; ++q) ss += part[i * kNearIdParts + q];
     const double e = sqrt(ss);
-    int s = st[i] & ~(ST_CHOL2 | ST_SERIES);
-    if (!(e <= tau_chol)) s |= ST_CHOL2;            // also NaN / Inf
-    else if (e > tau_fast) s |= ST_SERIES;
-    st[i] = s;
+    int sv = st[i] & ~(ST_CHOL2 | ST_SERIES);
+    if (!(e <= tau_chol)) sv |= ST_CHOL2;            // also NaN / Inf
+    else if (e > tau_fast) sv |= ST_SERIES;
+    st[i] = sv;
 }
 
 // Pout = Pin - Pin S^T for the matrices selected by (mask, val).
@@ -1285,17 +1302,21 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
     T* bufs[3] = {(T*)(c.ws + p.L), (T*)(c.ws + p.Tf), W};
     double* part = (double*)(c.ws + p.emax);
     int e;
-    if ((e = gram<T>(c, Pin, mask, val))) return e;
-    const unsigned nparts = grid_1d(r * r, kNearIdParts);
+    if ((e = gram<T>(c, Pin, mask, val, false))) return e;
     {
+        // about 2048 workgroups over the stack (the split partials are summed here), at most
+        // kNearIdParts per matrix
+        const int64_t per = std::min<int64_t>(kNearIdParts, std::max<int64_t>(16, (2048 + b - 1) / b));
+        const unsigned nparts = grid_1d(r * r, per);
         dim3 grid(nparts, (unsigned)b);
-        hipLaunchKernelGGL((near_id_init_kernel<T>), grid, dim3(256), 0, c.s, (const T*)W, bufs[0], part, r, c.st,
-                           mask, val);
+        const T* gp = p.gsplit > 1 ? (const T*)(c.ws + p.gpart) : nullptr;
+        hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, p.gsplit, W, bufs[0], part, r,
+                           (const int*)c.st, mask, val);
+        DION_TRY(hipGetLastError());
+        hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part,
+                           (int)nparts, c.st, b, mask, val, tau_fast, tau_chol);
         DION_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part, (int)nparts,
-                       c.st, b, mask, val, tau_fast, tau_chol);
-    DION_TRY(hipGetLastError());
     const int nmask = mask | ST_CHOL2 | ST_SERIES;
     // first-order matrices: S = F = Phi(E)
     if ((e = near_id_apply<T>(c, Pin, Pout, bufs[0], nmask, val))) return e;
@@ -1359,12 +1380,35 @@ struct Prod6Args {
     int st_mask, st_val;
 };
 
+// Staging side of prod6_kernel: three register sets of raw operand values and three LDS buffers,
+// both indexed by slab % 3, so a slab's global loads are issued three slabs before it is split
+// (enough bytes in flight per CU to cover the memory latency at the matrix-core rate).
+template <int AK, int AADD, int BK6>
+struct Stage6 {
+    static constexpr int BT = 128, PT = BT * kSplitK, D = 3;
+    Loader6<BT, AK, AADD> la[D];
+    Loader6<BT, BK6, A6_NONE> lb[D];
+    template <int J>
+    __device__ __forceinline__ void load(const Op6& A, const Op6& B, int m0, int n0, int k, int K, int t) {
+        if (k < K) { la[J].load(A, m0, k, t); lb[J].load(B, n0, k, t); }
+    }
+    // slab at k (held in set J) -> LDS buffer J; set J then loads the slab D slabs later
+    template <int J>
+    __device__ __forceinline__ void stage(const Op6& A, const Op6& B, int m0, int n0, int k, int K, uint16_t* lds,
+                                          int t) {
+        la[J].split_store(lds, t);
+        lb[J].split_store(lds + 3 * PT, t);
+        load<J>(A, B, m0, n0, k + D * kSplitK, K, t);
+    }
+};
+
 template <int AK, int AADD, int BK6>
 __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     // Eight waves: waves 0-3 multiply (a 64 x 64 sub-tile each), waves 4-7 stage the operands
     // (load, split into bf16 parts, write LDS).  Each SIMD holds one wave of each kind, so the
     // staging VALU work issues between the other wave's MFMAs; one barrier per slab.
-    constexpr int BT = 128, PT = BT * kSplitK;
+    using St = Stage6<AK, AADD, BK6>;
+    constexpr int BT = St::BT, PT = St::PT;
     const TileId tid = xcd_tile_id();
     const int bz = tid.z;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
@@ -1377,8 +1421,30 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     A.p0 = (const char*)A.p0 + bz * g.sa0;
     if (A.p1) A.p1 = (const char*)A.p1 + bz * g.sa1;
     B.p0 = (const char*)B.p0 + bz * g.sb0;
-    Loader6<BT, AK, AADD> la;
-    Loader6<BT, BK6, A6_NONE> lb;
+    const int K = g.K;
+    // slab s is multiplied from LDS buffer s % 3 while the staging waves write slab s + 2 to
+    // buffer (s + 2) % 3 and issue the loads of slab s + 5.  The two roles run separate loops
+    // with the same barriers, so their registers (raw slabs, accumulators) never overlap.
+    if (stager) {
+        St sg;
+        sg.template load<0>(A, B, m0, n0, 0, K, st_t);
+        sg.template load<1>(A, B, m0, n0, kSplitK, K, st_t);
+        sg.template load<2>(A, B, m0, n0, 2 * kSplitK, K, st_t);
+        sg.template stage<0>(A, B, m0, n0, 0, K, lds[0], st_t);
+        if (kSplitK < K) sg.template stage<1>(A, B, m0, n0, kSplitK, K, lds[1], st_t);
+        __syncthreads();
+        for (int k0 = 0; k0 < K; k0 += 3 * kSplitK) {
+            if (k0 + 2 * kSplitK < K) sg.template stage<2>(A, B, m0, n0, k0 + 2 * kSplitK, K, lds[2], st_t);
+            __syncthreads();
+            if (k0 + kSplitK >= K) break;
+            if (k0 + 3 * kSplitK < K) sg.template stage<0>(A, B, m0, n0, k0 + 3 * kSplitK, K, lds[0], st_t);
+            __syncthreads();
+            if (k0 + 2 * kSplitK >= K) break;
+            if (k0 + 4 * kSplitK < K) sg.template stage<1>(A, B, m0, n0, k0 + 4 * kSplitK, K, lds[1], st_t);
+            __syncthreads();
+        }
+        return;
+    }
     const int lane = threadIdx.x & 63, wm = (wave >> 1) & 1, wn = wave & 1;
     const int fr = lane & 15, fc = lane >> 4;
     f32x4 acc[4][4];
@@ -1386,33 +1452,13 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-    // three LDS buffers: while slab s is multiplied from buffer s % 3, the staging waves
-    // write slab s + 2 (loaded one slab earlier) to buffer (s + 2) % 3 and load slab s + 3
-    auto stage = [&](int k, int b) {
-        la.split();
-        lb.split();
-        if (k + kSplitK < g.K) { la.load(A, m0, k + kSplitK, st_t); lb.load(B, n0, k + kSplitK, st_t); }
-        la.store(lds[b], st_t);
-        lb.store(lds[b] + 3 * PT, st_t);
-    };
-    if (stager) {
-        la.load(A, m0, 0, st_t);
-        lb.load(B, n0, 0, st_t);
-        stage(0, 0);
-        if (kSplitK < g.K) stage(kSplitK, 1);
-    }
     __syncthreads();
     int buf = 0;
-    for (int k0 = 0; k0 < g.K; k0 += kSplitK) {
-        if (stager) {
-            if (k0 + 2 * kSplitK < g.K) stage(k0 + 2 * kSplitK, buf == 0 ? 2 : buf - 1);
-        } else {
-            mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc, wm * 64, wn * 64, fr, fc);
-        }
+    for (int k0 = 0; k0 < K; k0 += kSplitK) {
+        mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc, wm * 64, wn * 64, fr, fc);
         __syncthreads();
         buf = buf == 2 ? 0 : buf + 1;
     }
-    if (stager) return;
     float* C = g.c + bz * g.sc;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
