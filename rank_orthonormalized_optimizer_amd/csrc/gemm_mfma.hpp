@@ -8,10 +8,13 @@
 // (BM/2) x (BN/2) sub-tile built from 16 x 16 MFMA blocks
 // (v_mfma_f64_16x16x4_f64 for double, v_mfma_f32_16x16x4_f32 for float).
 //
-// Operands are staged through LDS as [k][x] tiles (x = row of A or column of
-// B), padded so the four 16-lane groups of a fragment read hit disjoint banks.
+// Operands are staged through LDS in their memory order: k-contiguous operands as
+// [x][k] tiles, x-contiguous ones as [k][x] tiles (x = row of A or column of B),
+// so every staging store is a contiguous 4-element vector.  Within a slab of BK,
+// lane group g = lane / 16 of the MFMA feeds k = (BK / 4) g + s at step s, so a
+// fragment of an [x][k] tile is BK / 4 consecutive k: two 16-byte LDS reads.
 // Global loads are 4-element vectors along whichever index is contiguous in
-// memory, prefetched into registers one k-tile ahead of the MFMA work.
+// memory, prefetched into registers ahead of the MFMA work.
 //
 // MFMA operand/result lane mapping (16 x 16 x 4, one block):
 //   A: lane l holds A[l % 16][l / 16]      B: lane l holds B[l / 16][l % 16]
@@ -128,16 +131,6 @@ __device__ __forceinline__ TileId xcd_tile_id() {
     return TileId{(int)(u / rows), (int)(y0 + u % rows), (int)z};
 }
 
-// XOR swizzle of the x index of KC operands in LDS.  A KC tile arrives as four consecutive k
-// per thread, so one wave's store of element v writes 256 / BK consecutive x in each of the
-// BK / 4 k-groups, and with the rows a multiple of 64 banks apart every k-group would land on
-// the same banks.  XORing x with (256 / BK) * (k / 4 mod BK / 4) moves each k-group to its own
-// bank window, while a fragment read (16 consecutive x, 16-aligned, of the four k-rows that
-// share k / 4, hence one swizzle value) still touches 16 distinct x per row.  The swizzle stays
-// below 64, so x keeps its 64-block: tile extents along x must be multiples of 64.
-template <int BK>
-__device__ __forceinline__ int lds_swizzle(int k) { return (256 / BK) * ((k >> 2) & (BK / 4 - 1)); }
-
 // Register-staged loader of one BX x BK operand tile.  load() only issues the global
 // loads of the raw storage values; store() widens them to T (adding the two addends of
 // the SUM sources, exactly in double and with one rounding in float) and writes LDS.  So the
@@ -149,7 +142,7 @@ struct TileLoader {
     using S1 = typename St::S1;
     static constexpr int GROUPS = BX * BK / 4;
     static_assert(GROUPS % 256 == 0, "tile must give every thread whole 4-element groups");
-    static_assert(!KC || (BX % 64 == 0 && BK >= 4 && BK <= 64), "swizzled KC tiles need BX % 64 == 0");
+    static_assert(!KC || BK % 4 == 0, "KC tiles are stored four k at a time");
     static constexpr int PER = GROUPS / 256;
     S0 r0[PER][4];
     S1 r1[St::two ? PER : 1][4];
@@ -182,56 +175,76 @@ struct TileLoader {
         if constexpr (St::two) return widen<T, S0>(r0[g][v]) + widen<T, S1>(r1[g][v]);
         else return widen<T, S0>(r0[g][v]);
     }
-    // LDS tile layout: s[k * LDX + (x ^ lds_swizzle<BK>(k))] (the swizzle only for KC operands)
-    template <int LDX>
+    // LDS tile layout: s[x * LD + k] for KC operands, s[k * LD + x] otherwise (LD the pitch)
+    template <int LD>
     __device__ __forceinline__ void store(T* s) const {
 #pragma unroll
         for (int g = 0; g < PER; ++g) {
             const int idx = threadIdx.x + g * 256;
             if constexpr (KC) {
                 const int x = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
-                const int xs = x ^ lds_swizzle<BK>(k);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[(k + v) * LDX + xs] = value(g, v);
+                for (int v = 0; v < 4; ++v) s[x * LD + k + v] = value(g, v);
             } else {
                 const int k = idx / (BX / 4), x = (idx % (BX / 4)) * 4;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[k * LDX + x + v] = value(g, v);
+                for (int v = 0; v < 4; ++v) s[k * LD + x + v] = value(g, v);
             }
         }
     }
 };
 
-// Tile geometry shared by the kernels: BM x BN output tile, K slabs of BK, LDS tiles
-// [k][x] padded by PAD elements per k-row, two LDS stages (double buffering).
+// Tile geometry shared by the kernels: BM x BN output tile, K slabs of BK, LDS tiles [k][x]
+// padded by PAD elements per k-row or [x][k] padded by 16 bytes per x-row (which spreads the
+// rows of a fragment read over the banks), two LDS stages (double buffering).
 template <typename T, int BM_, int BN_, int BK_ = 16>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, PAD = 16;
-    static constexpr int LDA = BM + PAD, LDB = BN + PAD;
+    static constexpr int LDA = BM + PAD, LDB = BN + PAD;     // [k][x] pitches
+    static constexpr int LDK = BK + 16 / (int)sizeof(T);     // [x][k] pitch
     static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave sub-tile
     static constexpr int FM = WTM / 16, FN = WTN / 16; // MFMA blocks per wave
-    static constexpr int A_STAGE = BK * LDA, B_STAGE = BK * LDB;
+    static constexpr int KS = BK / 4;                  // MFMA steps per slab
+    static constexpr int A_STAGE = BK * LDA > BM * LDK ? BK * LDA : BM * LDK;
+    static constexpr int B_STAGE = BK * LDB > BN * LDK ? BK * LDB : BN * LDK;
     using acc_t = typename Mfma<T>::acc_t;
 };
+
+// The KS values of one fragment at row x of a tile: k = KS g + s, s = 0 .. KS - 1.
+template <typename T, class C, bool KC, int LDX>
+__device__ __forceinline__ void frag_k(const T* s, int x, int g, T (&v)[C::KS]) {
+    if constexpr (KC) {
+        typedef T t4 __attribute__((ext_vector_type(16 / sizeof(T))));
+        constexpr int W = 16 / sizeof(T);
+        const T* p = s + x * C::LDK + C::KS * g;
+#pragma unroll
+        for (int q = 0; q < C::KS / W; ++q) {
+            const t4 u = *(const t4*)(p + W * q);
+#pragma unroll
+            for (int e = 0; e < W; ++e) v[W * q + e] = u[e];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < C::KS; ++q) v[q] = s[(C::KS * g + q) * LDX + x];
+    }
+}
 
 // acc[i][j] += A_frag[i] * B_frag[j] over one BK slab of LDS.
 template <typename T, class C, bool AKC, bool BKC>
 __device__ __forceinline__ void mma_slab(const T* As, const T* Bs, typename C::acc_t (&acc)[C::FM][C::FN],
                                          int wm, int wn, int lane) {
     const int lr = lane & 15, lk = lane >> 4;
+    T a[C::FM][C::KS], b[C::FN][C::KS];
 #pragma unroll
-    for (int kk = 0; kk < C::BK; kk += 4) {
-        T a[C::FM], b[C::FN];
-        const int sa = AKC ? lds_swizzle<C::BK>(kk) : 0, sb = BKC ? lds_swizzle<C::BK>(kk) : 0;
+    for (int i = 0; i < C::FM; ++i) frag_k<T, C, AKC, C::LDA>(As, wm * C::WTM + i * 16 + lr, lk, a[i]);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = As[(kk + lk) * C::LDA + ((wm * C::WTM + i * 16 + lr) ^ sa)];
+    for (int j = 0; j < C::FN; ++j) frag_k<T, C, BKC, C::LDB>(Bs, wn * C::WTN + j * 16 + lr, lk, b[j]);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = Bs[(kk + lk) * C::LDB + ((wn * C::WTN + j * 16 + lr) ^ sb)];
+    for (int q = 0; q < C::KS; ++q)
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
-    }
+            for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<T>::mma(a[i][q], b[j][q], acc[i][j]);
 }
 
 // Main loop over the K range [kbeg, kend), slab k in LDS buffer k % 2 (one barrier per slab).
@@ -254,24 +267,24 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
         la0.load(A, m0, kbeg);
         lb0.load(B, n0, kbeg);
         if (kbeg + C::BK < kend) { la1.load(A, m0, kbeg + C::BK); lb1.load(B, n0, kbeg + C::BK); }
-        la0.template store<C::LDA>(A0);
-        lb0.template store<C::LDB>(B0);
+        la0.template store<AKC ? C::LDK : C::LDA>(A0);
+        lb0.template store<BKC ? C::LDK : C::LDB>(B0);
         __syncthreads();
         for (int k0 = kbeg; k0 < kend; k0 += 2 * C::BK) {
             const int k1 = k0 + C::BK, k2 = k0 + 2 * C::BK, k3 = k0 + 3 * C::BK;
             if (k2 < kend) { la0.load(A, m0, k2); lb0.load(B, n0, k2); }
             mma_slab<T, C, AKC, BKC>(A0, B0, acc, wm, wn, lane);
             if (k1 < kend) {
-                la1.template store<C::LDA>(A1);
-                lb1.template store<C::LDB>(B1);
+                la1.template store<AKC ? C::LDK : C::LDA>(A1);
+                lb1.template store<BKC ? C::LDK : C::LDB>(B1);
             }
             __syncthreads();
             if (k1 >= kend) break;
             if (k3 < kend) { la1.load(A, m0, k3); lb1.load(B, n0, k3); }
             mma_slab<T, C, AKC, BKC>(A1, B1, acc, wm, wn, lane);
             if (k2 < kend) {
-                la0.template store<C::LDA>(A0);
-                lb0.template store<C::LDB>(B0);
+                la0.template store<AKC ? C::LDK : C::LDA>(A0);
+                lb0.template store<BKC ? C::LDK : C::LDB>(B0);
             }
             __syncthreads();
         }
@@ -280,8 +293,8 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
         TileLoader<T, C::BN, C::BK, BKC, BSRC> lb;
         la.load(A, m0, kbeg);
         lb.load(B, n0, kbeg);
-        la.template store<C::LDA>(A0);
-        lb.template store<C::LDB>(B0);
+        la.template store<AKC ? C::LDK : C::LDA>(A0);
+        lb.template store<BKC ? C::LDK : C::LDB>(B0);
         __syncthreads();
         int buf = 0;
         for (int k0 = kbeg; k0 < kend; k0 += C::BK) {
@@ -289,8 +302,8 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
             if (more) { la.load(A, m0, k0 + C::BK); lb.load(B, n0, k0 + C::BK); }
             mma_slab<T, C, AKC, BKC>(buf ? A1 : A0, buf ? B1 : B0, acc, wm, wn, lane);
             if (more) {
-                la.template store<C::LDA>(buf ? A0 : A1);
-                lb.template store<C::LDB>(buf ? B0 : B1);
+                la.template store<AKC ? C::LDK : C::LDA>(buf ? A0 : A1);
+                lb.template store<BKC ? C::LDK : C::LDB>(buf ? B0 : B1);
             }
             __syncthreads();
             buf ^= 1;
