@@ -227,109 +227,230 @@ struct PotrfArgs {
     int fail_bit, tau_bit;
 };
 
-// One column step of the diagonal-block factorization (see potrf_diag_kernel), with the column
-// index K a compile-time constant so every register slot below is static.
+// The 64 x 64 diagonal block is factored in LDS by 16-column panels.  Per panel one wave sweeps
+// the panel's columns (one row of the panel per lane, its 16 values in registers): the pivot
+// and the next pivot travel by v_readlane, the scaled column by LDS, and a bad pivot is only
+// recorded (checked after the sweep), so the sweep is one straight-line block in which the next
+// pivot's reciprocal square root overlaps the current column's broadcast.  The trailing blocks
+// are updated with 16 x 16 MFMA blocks spread over the four waves.  The inverse X = L^-1 then
+// comes from the four 16 x 16 diagonal inverses (forward substitution, one wave each) and two
+// levels of recursive doubling, X_VU = -X_VV (L_VU X_UU), again as MFMA blocks.
+constexpr int kSB = 16, kDLD = kNB + 1;   // panel width; LDS pitch of the block
+
 template <typename T>
-struct DiagCtx {
-    T a[kNB / 4], x[kNB / 4];
-    T (*col)[kNB];
-    T (*xrow)[kNB];
-    T* piv;
-    T* dg;
-    T* Lrow;
-    int i, part, nbj, tid;
-    bool row_ok, ok;
+struct DiagSmem {
+    T a[kNB * kDLD];     // working block, then L (lower); its upper blocks park the doubling products
+    T x[kNB * kDLD];     // L^-1 (lower)
+    T col[2][64];        // column broadcast of the panel sweep
+    T dg[kNB];           // diag(L)
+    T rd[kNB];           // 1 / diag(L)
+    int fail;
 };
 
-template <typename T, int K>
-__device__ __forceinline__ void diag_step(DiagCtx<T>& c) {
-    constexpr int NS = kNB / 4, b = K & 1, sk = K >> 2, q = K & 3;
-    const bool own = c.part == q;
-    if (own) {
-        c.col[b][c.i] = (c.row_ok && c.i > K) ? c.a[sk] : T(0);
-        if (c.i == K) c.piv[b] = c.a[sk];
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int l) {
+    if constexpr (sizeof(T) == 8) {
+        const long long u = __double_as_longlong(v);
+        const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffff), l);
+        const int hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+        return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+    } else {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
     }
-    if (c.i == K) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) c.xrow[b][4 * s + c.part] = c.x[s];
-    }
-    __syncthreads();
-    const T d = c.piv[b];
-    const T ci = c.col[b][c.i];
-    T cj[NS], xk[NS];
-#pragma unroll
-    for (int s = sk; s < NS; ++s) cj[s] = c.col[b][4 * s + c.part];
-#pragma unroll
-    for (int s = 0; s <= sk; ++s) xk[s] = c.xrow[b][4 * s + c.part];
-    if (!(d > T(0)) || !isfinite(d)) { c.ok = false; return; }   // same value in every thread
-    const T lkk = sqrt(d), inv = T(1) / lkk;
-    const T lik = ci * inv;            // zero unless i > K
-    const T coef = lik * inv;
-#pragma unroll
-    for (int s = sk; s < NS; ++s) c.a[s] -= coef * cj[s];
-#pragma unroll
-    for (int s = 0; s <= sk; ++s) c.x[s] -= coef * xk[s];
-    // L_iK replaces the consumed column K in its owner's register slot (stored once at the end:
-    // a global store inside the sweep would make the next column wait for it)
-    if (own) c.a[sk] = (c.i == K) ? lkk : lik;
-    if (c.tid == 0) c.dg[K] = lkk;
 }
 
+// 1 / sqrt(d): the hardware estimate and Newton steps y <- y (3/2 - d y^2 / 2), two in fp64
+// (each doubles the correct bits of the estimate), one in fp32.
+template <typename T>
+__device__ __forceinline__ T rsqrt_newton(T d) {
+    if constexpr (sizeof(T) == 8) {
+        double y = __builtin_amdgcn_rsq(d);
+        const double h = 0.5 * d;
+        double t = y * y; t = __builtin_fma(-h, t, 1.5); y = y * t;
+        t = y * y; t = __builtin_fma(-h, t, 1.5); y = y * t;
+        return y;
+    } else {
+        float y = __builtin_amdgcn_rsqf(d);
+        const float h = 0.5f * d;
+        const float t = __builtin_fmaf(-h, y * y, 1.5f);
+        return y * t;
+    }
+}
+
+// acc += A B over K (a multiple of 4) for one 16 x 16 block held by the calling wave, with
+// A(i,k) = a[i * ai + k * ak] and B(k,j) = b[k * bk + j * bj] in LDS.
+template <typename T>
+__device__ __forceinline__ void blk_mma(const T* a, int ai, int ak, const T* b, int bk, int bj, int K,
+                                        typename Mfma<T>::acc_t& acc, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4) acc = Mfma<T>::mma(a[r * ai + (k0 + kk) * ak], b[(k0 + kk) * bk + r * bj], acc);
+}
+
+// One column K of the panel sweep (lane = row of the panel).  d, r: this column's pivot and
+// 1 / sqrt(pivot); returns the next column's through the recursion.
 template <typename T, int K>
-struct DiagSteps {
-    static __device__ __forceinline__ void run(DiagCtx<T>& c) {
-        if constexpr (K < kNB) {
-            if (c.ok && K < c.nbj) {
-                diag_step<T, K>(c);
-                DiagSteps<T, K + 1>::run(c);
+struct PanelCol {
+    static __device__ __forceinline__ void run(T (&a)[kSB], T d, T r, int lane, T* col, T (&dgv)[kSB],
+                                               T (&rdv)[kSB], bool& bad) {
+        if constexpr (K < kSB) {
+            bad |= !(d > T(0)) || !(d < T(INFINITY));
+            const T lkk = d * r;
+            const T l = lane > K ? a[K] * r : (lane == K ? lkk : T(0));
+            a[K] = l;
+            dgv[K] = lkk;
+            rdv[K] = r;
+            T dn = T(1), rn = T(1);
+            if constexpr (K + 1 < kSB) {   // next pivot from lane K + 1 alone
+                const T ln = read_lane<T>(l, K + 1), an = read_lane<T>(a[K + 1], K + 1);
+                dn = __builtin_fma(-ln, ln, an);
+                rn = rsqrt_newton<T>(dn);
             }
+            T* c = col + (K & 1) * 64;
+            c[lane] = l;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int j = K + 1; j < kSB; ++j) a[j] = __builtin_fma(-l, c[j], a[j]);
+            PanelCol<T, K + 1>::run(a, dn, rn, lane, col, dgv, rdv, bad);
         }
     }
 };
 
+// Sweep of panel p by one wave: columns 16 p .. 16 p + 15, rows 16 p .. 63.  False on a bad pivot.
 template <typename T>
-struct DiagSmem {
-    T col[2][kNB];
-    T xrow[2][kNB];
-    T piv[2];
-    T dg[kNB];
-};
+__device__ bool panel_sweep(DiagSmem<T>& sm, int p, int lane) {
+    const int o = kSB * p, R = o + lane;
+    const bool valid = R < kNB;
+    T a[kSB], dgv[kSB], rdv[kSB];
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) a[j] = valid ? sm.a[R * kDLD + o + j] : T(0);
+    const T d0 = read_lane<T>(a[0], 0);
+    bool bad = false;
+    PanelCol<T, 0>::run(a, d0, rsqrt_newton<T>(d0), lane, &sm.col[0][0], dgv, rdv, bad);
+    if (bad) return false;
+    if (valid) {
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) sm.a[R * kDLD + o + j] = (j <= lane) ? a[j] : T(0);
+    }
+    T dv = T(0), rv = T(0);
+#pragma unroll
+    for (int k = 0; k < kSB; ++k)
+        if (lane == k) { dv = dgv[k]; rv = rdv[k]; }
+    if (lane < kSB) { sm.dg[o + lane] = dv; sm.rd[o + lane] = rv; }
+    return true;
+}
 
-// One fused right-looking sweep over the columns k of the diagonal block of matrix bz:
-//   Cholesky   l_ik = a_ik / l_kk,  a_ij -= l_ik l_jk      (k < j <= i)
-//   inverse    x_i  -= l_ik (x_k / l_kk)                   (rows of X = L^-1, columns c <= k)
-// Thread t owns row i = t / 4 and, in registers, the 16 columns j = 4 s + t % 4 of that row of
-// the working matrix and of X.  Per column, the raw column k (zero at rows <= k), the pivot and
-// row k of X (zero right of the diagonal) travel through double-buffered LDS, so the updates
-// need no predicates and one barrier per column suffices.  Returns false (fail bit set) on a
-// non-positive or non-finite pivot; the decision is the same in every thread.
+// X_ww = L_ww^-1 for the 16 x 16 diagonal block w; lane c < 16 computes column c by forward
+// substitution (two interleaved partial sums per row).
+template <typename T>
+__device__ void diag16_inverse(DiagSmem<T>& sm, int w, int lane) {
+    const int o = kSB * w, c = lane & 15;
+    T t[kSB];
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) {
+        T s0 = (i == c) ? T(1) : T(0), s1 = T(0);
+#pragma unroll
+        for (int q = 0; q < i; ++q) {
+            const T lv = sm.a[(o + i) * kDLD + o + q];
+            if (q & 1) s1 = __builtin_fma(-lv, t[q], s1);
+            else s0 = __builtin_fma(-lv, t[q], s0);
+        }
+        t[i] = (s0 + s1) * sm.rd[o + i];
+    }
+    if (lane < kSB) {
+#pragma unroll
+        for (int i = 0; i < kSB; ++i) sm.x[(o + i) * kDLD + o + c] = t[i];
+    }
+}
+
+// L and X = L^-1 of the block in sm.a (lower part; rows and columns beyond the block's size
+// hold the identity).  256 threads; false (in every thread) on a bad pivot.
+template <typename T>
+__device__ bool chol_inv64(DiagSmem<T>& sm) {
+    using acc_t = typename Mfma<T>::acc_t;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, fr = lane & 15;
+    if (tid == 0) sm.fail = 0;
+    __syncthreads();
+    for (int p = 0; p < 4; ++p) {
+        const int o = kSB * p;
+        if (wave == 0 && !panel_sweep<T>(sm, p, lane) && lane == 0) sm.fail = 1;
+        __syncthreads();
+        if (sm.fail) return false;
+        if (p == 3) break;
+        // trailing blocks (q, s), p < s <= q: A_qs -= L_qp L_sp^T
+        int nb = 0;
+        for (int q = p + 1; q < 4; ++q)
+            for (int s2 = p + 1; s2 <= q; ++s2, ++nb) {
+                if (nb % 4 != wave) continue;
+                acc_t acc = {0, 0, 0, 0};
+                blk_mma<T>(&sm.a[(kSB * q) * kDLD + o], kDLD, 1, &sm.a[(kSB * s2) * kDLD + o], 1, kDLD, kSB, acc, lane);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sm.a[(kSB * q + Mfma<T>::row(lane, v)) * kDLD + kSB * s2 + fr] -= acc[v];
+            }
+        __syncthreads();
+    }
+    diag16_inverse<T>(sm, wave, lane);
+    __syncthreads();
+    // doubling over 16-blocks: X_10 = -X_11 (L_10 X_00), X_32 = -X_33 (L_32 X_22); the products
+    // L_VU X_UU park in the (unused) upper blocks (0, 1) and (2, 3) of sm.a
+    const int u0 = 32 * wave, v0 = u0 + kSB;
+    if (wave < 2) {
+        acc_t y = {0, 0, 0, 0};
+        blk_mma<T>(&sm.a[v0 * kDLD + u0], kDLD, 1, &sm.x[u0 * kDLD + u0], kDLD, 1, kSB, y, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.a[(u0 + Mfma<T>::row(lane, v)) * kDLD + v0 + fr] = y[v];
+    }
+    __syncthreads();
+    if (wave < 2) {
+        acc_t t = {0, 0, 0, 0};
+        blk_mma<T>(&sm.x[v0 * kDLD + v0], kDLD, 1, &sm.a[u0 * kDLD + v0], kDLD, 1, kSB, t, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.x[(v0 + Mfma<T>::row(lane, v)) * kDLD + u0 + fr] = -t[v];
+    }
+    __syncthreads();
+    // over 32-blocks: X_VU = -X_VV (L_VU X_UU), U = 0..31, V = 32..63; wave = output block (bi, bj);
+    // L_VU X_UU parks in the upper 32 x 32 block of sm.a
+    const int bi = wave >> 1, bj = wave & 1;
+    {
+        acc_t y = {0, 0, 0, 0};
+        const int k0 = kSB * bj;   // X_UU is lower: rows below 16 bj only
+        blk_mma<T>(&sm.a[(32 + kSB * bi) * kDLD + k0], kDLD, 1, &sm.x[k0 * kDLD + kSB * bj], kDLD, 1, 32 - k0, y, lane);
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.a[(kSB * bi + Mfma<T>::row(lane, v)) * kDLD + 32 + kSB * bj + fr] = y[v];
+    }
+    __syncthreads();
+    {
+        acc_t t = {0, 0, 0, 0};
+        const int kend = kSB * (bi + 1);   // X_VV is lower
+        blk_mma<T>(&sm.x[(32 + kSB * bi) * kDLD + 32], kDLD, 1, &sm.a[32 + kSB * bj], kDLD, 1, kend, t, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.x[(32 + kSB * bi + Mfma<T>::row(lane, v)) * kDLD + kSB * bj + fr] = -t[v];
+    }
+    __syncthreads();
+    return true;
+}
+
+// Diagonal block jblk of matrix bz: read from p.S, factor and invert (chol_inv64), write L to
+// p.L and the inverse to p.Td, and track the diagonal ratio.  Returns false (fail bit set) on
+// a non-positive or non-finite pivot; the decision is the same in every thread.
 template <typename T>
 __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
-    constexpr int NB = kNB, NS = NB / 4;
-    static_assert(NB * 4 == 256, "one row per four threads");
-    T* L = (T*)p.L + bz * p.sL;
-    DiagCtx<T> c;
-    c.col = sm.col; c.xrow = sm.xrow; c.piv = sm.piv; c.dg = sm.dg;
-    c.nbj = p.nbj; c.tid = threadIdx.x;
-    c.i = c.tid >> 2; c.part = c.tid & 3;
-    c.row_ok = c.i < c.nbj;
-    c.ok = true;
-    const int64_t roff = (int64_t)(p.j0 + (c.row_ok ? c.i : 0)) * p.ldl + p.j0;
-    c.Lrow = L + roff;
-    const T* Srow = (const T*)p.S + bz * p.sL + roff;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int j = 4 * s + c.part;
-        c.a[s] = (c.row_ok && j <= c.i) ? Srow[j] : T(0);
-        c.x[s] = (j == c.i) ? T(1) : T(0);
+    const int tid = threadIdx.x, nbj = p.nbj;
+    const T* S = (const T*)p.S + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
+    T* L = (T*)p.L + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
+    for (int idx = tid; idx < kNB * kNB; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        T v = (i == j) ? T(1) : T(0);
+        if (i < nbj && j <= i) v = S[(int64_t)i * p.ldl + j];
+        sm.a[i * kDLD + j] = v;
     }
-    DiagSteps<T, 0>::run(c);
-    const int tid = c.tid, i = c.i, part = c.part, nbj = c.nbj;
-    if (!c.ok) {
+    __syncthreads();
+    if (!chol_inv64<T>(sm)) {
         if (tid == 0) p.st[bz] |= p.fail_bit;
         return false;
     }
-    __syncthreads();
     if (tid == 0) {
         double mn = (double)sm.dg[0], mx = (double)sm.dg[0];
         for (int q = 1; q < nbj; ++q) {
@@ -343,12 +464,11 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
     }
     T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * p.blkTd;
-    const T rinv = c.row_ok ? T(1) / sm.dg[i] : T(0);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int j = 4 * s + part;
-        if (c.row_ok && j <= i) c.Lrow[j] = c.a[s];
-        if (p.tdfull || (c.row_ok && j < nbj)) Td[i * p.ldTd + j] = (c.row_ok && j <= i) ? c.x[s] * rinv : T(0);
+    for (int idx = tid; idx < kNB * kNB; idx += 256) {
+        const int i = idx >> 6, j = idx & 63;
+        const bool in = i < nbj && j < nbj;
+        if (in && j <= i) L[(int64_t)i * p.ldl + j] = sm.a[i * kDLD + j];
+        if (in || p.tdfull) Td[i * p.ldTd + j] = (in && j <= i) ? sm.x[i * kDLD + j] : T(0);
     }
     return true;
 }
