@@ -809,8 +809,71 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
             __syncthreads();
         }
     }
-    // epilogue in the MFMA layout, in two halves of rows: all loads of a half before its stores
     const int64_t mn = (int64_t)u.m * u.n;
+    // full tiles: each product tile goes through LDS to rows of 64 consecutive columns, so M, G
+    // and X move as 16-byte (bf16: 8-byte) vectors; all loads of a pass before its stores
+    if (m0 + BM <= u.m && n0 + BN <= u.n && (u.n & 3) == 0) {
+        constexpr int TP = BN + 4;
+        float* tl = (float*)lds;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        tl[(wm * 64 + 16 * i + 4 * fc + v) * TP + wn * 32 + 16 * j + fr] = pass ? acc2[i][j][v] : acc1[i][j][v];
+            __syncthreads();
+            float4 av[8], xv[8], gv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = 4 * (t + 256 * q), row = e >> 6, col = e & 63;
+                av[q] = *(const float4*)&tl[row * TP + col];
+                const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
+                if (pass == 0) {
+                    xv[q] = *(const float4*)(u.M + off);
+                    if constexpr (G_BF16) {
+                        const uint2 w = *(const uint2*)((const uint16_t*)u.G + off);
+                        gv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
+                                       bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
+                    } else {
+                        gv[q] = *(const float4*)((const float*)u.G + off);
+                    }
+                } else {
+                    if constexpr (X_BF16) {
+                        const uint2 w = *(const uint2*)((const uint16_t*)u.X + off);
+                        xv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
+                                       bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
+                    } else {
+                        xv[q] = *(const float4*)((const float*)u.X + off);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = 4 * (t + 256 * q), row = e >> 6, col = e & 63;
+                const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
+                if (pass == 0) {
+                    const float c = u.one_minus_mu;
+                    *(float4*)(u.M + off) = float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
+                                                   (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w};
+                } else {
+                    const float c = u.lr_s;
+                    const float4 x = float4{xv[q].x - c * av[q].x, xv[q].y - c * av[q].y, xv[q].z - c * av[q].z,
+                                            xv[q].w - c * av[q].w};
+                    if constexpr (X_BF16)
+                        *(uint2*)((uint16_t*)u.X + off) =
+                            uint2{(uint32_t)float_to_bf16_bits(x.x) | ((uint32_t)float_to_bf16_bits(x.y) << 16),
+                                  (uint32_t)float_to_bf16_bits(x.z) | ((uint32_t)float_to_bf16_bits(x.w) << 16)};
+                    else *(float4*)((float*)u.X + off) = x;
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    // partial tiles: in the MFMA layout, in two halves of rows, all loads of a half before its stores
     float* Mp = u.M + bz * mn;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -169,11 +169,13 @@ def test_sticky_hint_is_bitwise_neutral(cuda):
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("base", [1, 3])
-def test_wide_update_tiles(cuda, base):
-    """A stack large enough for the 128 x 128 weight-pass tiles (16 x 520 x 1000: 640 tiles, both
-    edges ragged, r = 72 padded to 96 in the split planes), fp32 and bf16 weights."""
-    wl = W.SMALL[base].with_groups(W.Group(16, 520, 1000, 72), name=f"wide-tiles-{base}", steps=2)
+@pytest.mark.parametrize("base,n", [(1, 1000), (3, 1000), (1, 998)])
+def test_wide_update_tiles(cuda, base, n):
+    """A stack large enough for the 128 x 64 weight-pass tiles (16 x 520 x n: both edges ragged,
+    r = 72 padded to 96 in the split planes), fp32 and bf16 weights.  With n = 1000 the interior
+    tiles take the vectorized epilogue and the edge tiles the element-wise one; n = 998 (rows
+    not 16-byte aligned) sends every tile to the element-wise epilogue."""
+    wl = W.SMALL[base].with_groups(W.Group(16, 520, n, 72), name=f"wide-tiles-{base}-{n}", steps=2)
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
 
