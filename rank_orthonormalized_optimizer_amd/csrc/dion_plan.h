@@ -61,13 +61,13 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.nblk = (r + kNB - 1) / kNB;
     q.nchunk = (n + kNormChunk - 1) / kNormChunk;
     q.kp = (r + 31) / 32 * 32;
-    {   // split the Gram's long K (= m) over the grid: with three 64 x 64 workgroups resident per
+    {   // split the Gram's long K (= m) over the grid: with four 64 x 64 workgroups resident per
         // CU (the register budget of the fp64 tile), pick the split count minimizing
         // rounds x (slabs per split + 3 slabs of fill and drain), keeping >= 128 rows per split
         // and the partials within 512 MB
         const int64_t nt = (r + 63) / 64;
         const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
-        const int64_t slots = 256 * 3, slabs = (m + 15) / 16;
+        const int64_t slots = 256 * 4, slabs = (m + 15) / 16;
         int64_t best = 1;
         double best_cost = 0.0;
         for (int64_t s = 1; s <= 16; ++s) {
