@@ -86,7 +86,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmA
     const TileId tid = xcd_tile_id();
     const int bz = tid.z / zdiv, grp = tid.z % zdiv;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
-    const int m0 = tid.y * BM, n0 = tid.x * BN;
+    // triangular K ranges: the longest tiles get the lowest dispatch order, so the launch does
+    // not end on them
+    const int tx = g.kskip == 1 ? (int)gridDim.x - 1 - tid.x : tid.x;
+    const int ty = g.kskip == 3 ? (int)gridDim.y - 1 - tid.y : tid.y;
+    const int m0 = ty * BM, n0 = tx * BN;
     if (g.lower && n0 >= m0 + BM) return;
     int kbeg = 0, kend = g.K;
     if (g.kskip == 1) kend = min(g.K, n0 + BN);
@@ -767,6 +771,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
 // (two barriers per slab).  Two workgroups fit on a CU, so one workgroup's memory-bound
 // epilogue (the loads of each half-tile issued before its stores) runs while the other keeps
 // the matrix cores busy.
+
+// Streaming (non-temporal) 16- and 8-byte accesses for the weight pass's M, G and X, which are
+// touched once: they then leave the L2 to the split planes that every tile re-reads.
+__device__ __forceinline__ float4 nt_ld4(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+    return float4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void nt_st4(float* p, float4 v) { __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, (f32x4*)p); }
+__device__ __forceinline__ uint2 nt_ld2(const uint16_t* p) {
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+    return uint2{v[0], v[1]};
+}
+__device__ __forceinline__ void nt_st2(uint16_t* p, uint2 v) { __builtin_nontemporal_store(u32x2{v.x, v.y}, (u32x2*)p); }
 template <bool G_BF16, bool X_BF16>
 __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     constexpr int BM = 128, BN = 64, PA = BM * kSplitK, PB = BN * kSplitK, FM = 4, FN = 2;
@@ -832,21 +849,21 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                 av[q] = *(const float4*)&tl[row * TP + col];
                 const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
                 if (pass == 0) {
-                    xv[q] = *(const float4*)(u.M + off);
+                    xv[q] = nt_ld4(u.M + off);
                     if constexpr (G_BF16) {
-                        const uint2 w = *(const uint2*)((const uint16_t*)u.G + off);
+                        const uint2 w = nt_ld2((const uint16_t*)u.G + off);
                         gv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
                                        bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
                     } else {
-                        gv[q] = *(const float4*)((const float*)u.G + off);
+                        gv[q] = nt_ld4((const float*)u.G + off);
                     }
                 } else {
                     if constexpr (X_BF16) {
-                        const uint2 w = *(const uint2*)((const uint16_t*)u.X + off);
+                        const uint2 w = nt_ld2((const uint16_t*)u.X + off);
                         xv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
                                        bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
                     } else {
-                        xv[q] = *(const float4*)((const float*)u.X + off);
+                        xv[q] = nt_ld4((const float*)u.X + off);
                     }
                 }
             }
@@ -856,17 +873,17 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                 const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
                 if (pass == 0) {
                     const float c = u.one_minus_mu;
-                    *(float4*)(u.M + off) = float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
-                                                   (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w};
+                    nt_st4(u.M + off, float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
+                                                   (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w});
                 } else {
                     const float c = u.lr_s;
                     const float4 x = float4{xv[q].x - c * av[q].x, xv[q].y - c * av[q].y, xv[q].z - c * av[q].z,
                                             xv[q].w - c * av[q].w};
                     if constexpr (X_BF16)
-                        *(uint2*)((uint16_t*)u.X + off) =
+                        nt_st2((uint16_t*)u.X + off,
                             uint2{(uint32_t)float_to_bf16_bits(x.x) | ((uint32_t)float_to_bf16_bits(x.y) << 16),
-                                  (uint32_t)float_to_bf16_bits(x.z) | ((uint32_t)float_to_bf16_bits(x.w) << 16)};
-                    else *(float4*)((float*)u.X + off) = x;
+                                  (uint32_t)float_to_bf16_bits(x.z) | ((uint32_t)float_to_bf16_bits(x.w) << 16)});
+                    else nt_st4((float*)u.X + off, x);
                 }
             }
             __syncthreads();
