@@ -171,6 +171,21 @@ struct TileLoader {
             }
         }
     }
+    // Interior tiles with vector-legal operands: the same vector loads, with no bounds tests.
+    // Branch-free, so the compiler can count the loads in flight and wait for exactly the
+    // ones a store needs (the bounds-tested loader's paths force it to wait for all of them).
+    __device__ __forceinline__ void load_fast(const Operand& op, int x0, int k0) {
+#pragma unroll
+        for (int g = 0; g < PER; ++g) {
+            const int idx = threadIdx.x + g * 256;
+            int x, k;
+            if constexpr (KC) { x = x0 + idx / (BK / 4); k = k0 + (idx % (BK / 4)) * 4; }
+            else { k = k0 + idx / (BX / 4); x = x0 + (idx % (BX / 4)) * 4; }
+            const int64_t off = KC ? (int64_t)x * op.ld + k : (int64_t)k * op.ld + x;
+            load4_raw<S0>(op.p0, off, r0[g]);
+            if constexpr (St::two) load4_raw<S1>(op.p1, off, r1[g]);
+        }
+    }
     __device__ __forceinline__ T value(int g, int v) const {
         if constexpr (St::two) return widen<T, S0>(r0[g][v]) + widen<T, S1>(r1[g][v]);
         else return widen<T, S0>(r0[g][v]);
@@ -247,6 +262,61 @@ __device__ __forceinline__ void mma_slab(const T* As, const T* Bs, typename C::a
             for (int j = 0; j < C::FN; ++j) acc[i][j] = Mfma<T>::mma(a[i][q], b[j][q], acc[i][j]);
 }
 
+// fp64 main loop of an interior tile whose K range is whole slabs: slab s in LDS buffer s % 2,
+// register set s % 2 loaded two slabs ahead, and a steady loop with no conditional loads.
+template <typename T, class C, bool AKC, int ASRC, bool BKC, int BSRC>
+__device__ __forceinline__ void mainloop_fast2(const Operand& A, const Operand& B, int m0, int n0, int kbeg,
+                                               int nslab, T* As, T* Bs, typename C::acc_t (&acc)[C::FM][C::FN]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    T* A0 = As;
+    T* A1 = As + C::A_STAGE;
+    T* B0 = Bs;
+    T* B1 = Bs + C::B_STAGE;
+    constexpr int LA = AKC ? C::LDK : C::LDA, LB = BKC ? C::LDK : C::LDB;
+    TileLoader<T, C::BM, C::BK, AKC, ASRC> la0, la1;
+    TileLoader<T, C::BN, C::BK, BKC, BSRC> lb0, lb1;
+    la0.load_fast(A, m0, kbeg);
+    lb0.load_fast(B, n0, kbeg);
+    if (nslab > 1) { la1.load_fast(A, m0, kbeg + C::BK); lb1.load_fast(B, n0, kbeg + C::BK); }
+    la0.template store<LA>(A0);
+    lb0.template store<LB>(B0);
+    __syncthreads();
+    // invariant: LDS buffer 0 holds slab s, register set 1 slab s + 1
+    int s = 0;
+    for (; s + 3 < nslab; s += 2) {
+        const int k2 = kbeg + (s + 2) * C::BK;
+        la0.load_fast(A, m0, k2);
+        lb0.load_fast(B, n0, k2);
+        mma_slab<T, C, AKC, BKC>(A0, B0, acc, wm, wn, lane);
+        la1.template store<LA>(A1);
+        lb1.template store<LB>(B1);
+        __syncthreads();
+        la1.load_fast(A, m0, k2 + C::BK);
+        lb1.load_fast(B, n0, k2 + C::BK);
+        mma_slab<T, C, AKC, BKC>(A1, B1, acc, wm, wn, lane);
+        la0.template store<LA>(A0);
+        lb0.template store<LB>(B0);
+        __syncthreads();
+    }
+    const int r = nslab - s;   // 1, 2 or 3 slabs left
+    if (r == 3) { la0.load_fast(A, m0, kbeg + (s + 2) * C::BK); lb0.load_fast(B, n0, kbeg + (s + 2) * C::BK); }
+    mma_slab<T, C, AKC, BKC>(A0, B0, acc, wm, wn, lane);
+    if (r >= 2) {
+        la1.template store<LA>(A1);
+        lb1.template store<LB>(B1);
+        __syncthreads();
+        mma_slab<T, C, AKC, BKC>(A1, B1, acc, wm, wn, lane);
+        if (r == 3) {
+            la0.template store<LA>(A0);
+            lb0.template store<LB>(B0);
+            __syncthreads();
+            mma_slab<T, C, AKC, BKC>(A0, B0, acc, wm, wn, lane);
+        }
+    }
+    __syncthreads();
+}
+
 // Main loop over the K range [kbeg, kend), slab k in LDS buffer k % 2 (one barrier per slab).
 // fp64: two register staging sets, the raw loads of slab k + 2 issued before slab k is
 // multiplied, so each has two slabs of MFMA work to arrive.  fp32 (four times the MFMA rate,
@@ -262,6 +332,11 @@ __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int
     T* B0 = Bs;
     T* B1 = Bs + C::B_STAGE;
     if constexpr (sizeof(T) == 8) {
+        if (A.vec && B.vec && m0 + C::BM <= A.xext && n0 + C::BN <= B.xext && kend <= A.kext && kend <= B.kext &&
+            (kend - kbeg) % C::BK == 0) {
+            mainloop_fast2<T, C, AKC, ASRC, BKC, BSRC>(A, B, m0, n0, kbeg, (kend - kbeg) / C::BK, As, Bs, acc);
+            return;
+        }
         TileLoader<T, C::BM, C::BK, AKC, ASRC> la0, la1;
         TileLoader<T, C::BN, C::BK, BKC, BSRC> lb0, lb1;
         la0.load(A, m0, kbeg);
