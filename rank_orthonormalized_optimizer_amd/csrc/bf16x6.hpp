@@ -145,6 +145,16 @@ struct Loader6<BX, S6_PLANES, ADD> {
                 r[p][q] = ok ? *(const u32x4*)((const uint16_t*)op.p0 + p * op.plane + o) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    // interior tile: no bounds tests (branch-free, so the loads in flight can be counted)
+    __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int x = (t >> 2) + 64 * q, c = t & 3;
+            const int64_t o = (int64_t)(x0 + x) * op.ld + k0 + 8 * c;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) r[p][q] = *(const u32x4*)((const uint16_t*)op.p0 + p * op.plane + o);
+        }
+    }
     __device__ __forceinline__ void split() {}
     __device__ __forceinline__ void store(uint16_t* lds, int t) const {
 #pragma unroll
@@ -166,26 +176,30 @@ struct Loader6<BX, S6_KC, ADD> {
     float a[PER][4];
     AT b[ADD == A6_NONE ? 1 : PER][4];
     Parts4 sp[PER];
+    // interior tile (vector-legal, whole slab): no bounds tests
+    __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
+        const int xr = t >> 3, kk = 4 * (t & 7);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int64_t o = (int64_t)(x0 + xr + 32 * q) * op.ld + k0 + kk;
+            const float4 v = *(const float4*)((const float*)op.p0 + o);
+            a[q][0] = v.x; a[q][1] = v.y; a[q][2] = v.z; a[q][3] = v.w;
+            if constexpr (ADD == A6_F32) {
+                const float4 w = *(const float4*)((const float*)op.p1 + o);
+                b[q][0] = w.x; b[q][1] = w.y; b[q][2] = w.z; b[q][3] = w.w;
+            } else if constexpr (ADD == A6_BF16) {
+                const uint2 w = *(const uint2*)((const uint16_t*)op.p1 + o);
+                b[q][0] = (uint16_t)w.x; b[q][1] = (uint16_t)(w.x >> 16);
+                b[q][2] = (uint16_t)w.y; b[q][3] = (uint16_t)(w.y >> 16);
+            }
+        }
+    }
+    static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
+        return op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
+    }
     __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
         const int xr = t >> 3, kk = 4 * (t & 7);
-        const bool interior = op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
-        if (interior) {
-#pragma unroll
-            for (int q = 0; q < PER; ++q) {
-                const int64_t o = (int64_t)(x0 + xr + 32 * q) * op.ld + k0 + kk;
-                const float4 v = *(const float4*)((const float*)op.p0 + o);
-                a[q][0] = v.x; a[q][1] = v.y; a[q][2] = v.z; a[q][3] = v.w;
-                if constexpr (ADD == A6_F32) {
-                    const float4 w = *(const float4*)((const float*)op.p1 + o);
-                    b[q][0] = w.x; b[q][1] = w.y; b[q][2] = w.z; b[q][3] = w.w;
-                } else if constexpr (ADD == A6_BF16) {
-                    const uint2 w = *(const uint2*)((const uint16_t*)op.p1 + o);
-                    b[q][0] = (uint16_t)w.x; b[q][1] = (uint16_t)(w.x >> 16);
-                    b[q][2] = (uint16_t)w.y; b[q][3] = (uint16_t)(w.y >> 16);
-                }
-            }
-            return;
-        }
+        if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int x = x0 + xr + 32 * q, k = k0 + kk;
@@ -239,20 +253,27 @@ struct Loader6<BX, S6_XC, ADD> {
     float a[KPT];
     AT b[ADD == A6_NONE ? 1 : KPT];
     Parts4 sp[KPT / 4];
+    // interior tile (whole slab): no bounds tests
+    __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
+        const int x = x0 + t % BX;
+        const int kb = __builtin_amdgcn_readfirstlane(k0 + (t / BX) * KPT);   // uniform per wave
+        const float* pa = (const float*)op.p0 + (int64_t)kb * op.ld;
+        const AT* pb = ADD != A6_NONE ? (const AT*)op.p1 + (int64_t)kb * op.ld : nullptr;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            a[e] = pa[(int64_t)e * op.ld + x];
+            if constexpr (ADD != A6_NONE) b[e] = pb[(int64_t)e * op.ld + x];
+        }
+    }
+    static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
+        return x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
+    }
     __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
         const int x = x0 + t % BX;
         const int kb = __builtin_amdgcn_readfirstlane(k0 + (t / BX) * KPT);   // uniform per wave
-        const bool interior = x0 + BX <= op.xext && kb + KPT <= op.kext;
         const float* pa = (const float*)op.p0 + (int64_t)kb * op.ld;
         const AT* pb = ADD != A6_NONE ? (const AT*)op.p1 + (int64_t)kb * op.ld : nullptr;
-        if (interior) {
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) {
-                a[e] = pa[(int64_t)e * op.ld + x];
-                if constexpr (ADD != A6_NONE) b[e] = pb[(int64_t)e * op.ld + x];
-            }
-            return;
-        }
+        if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
         const bool xin = x < op.xext;
         const int xs = xin ? x : 0;
 #pragma unroll

@@ -1600,6 +1600,24 @@ struct Stage6 {
         lb[J].split_store(lds + 3 * PT, t);
         load<J>(A, B, m0, n0, k + D * kSplitK, K, t);
     }
+    // Interior tiles (every slab whole and inside both operands): the same steps without bounds
+    // tests or conditional loads, so the compiler waits only for the set a store consumes.
+    static __device__ __forceinline__ bool all_interior(const Op6& A, const Op6& B, int m0, int n0, int K) {
+        return K % kSplitK == 0 && Loader6<BT, AK, AADD>::interior(A, m0, K - kSplitK) &&
+               Loader6<BT, BK6, A6_NONE>::interior(B, n0, K - kSplitK);
+    }
+    template <int J>
+    __device__ __forceinline__ void load_fast(const Op6& A, const Op6& B, int m0, int n0, int k, int t) {
+        la[J].load_fast(A, m0, k, t);
+        lb[J].load_fast(B, n0, k, t);
+    }
+    template <int J>
+    __device__ __forceinline__ void stage_fast(const Op6& A, const Op6& B, int m0, int n0, int knext, uint16_t* lds,
+                                               int t) {
+        la[J].split_store(lds, t);
+        lb[J].split_store(lds + 3 * PT, t);
+        load_fast<J>(A, B, m0, n0, knext, t);
+    }
 };
 
 template <int AK, int AADD, int BK6>
@@ -1627,13 +1645,37 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     // with the same barriers, so their registers (raw slabs, accumulators) never overlap.
     if (stager) {
         St sg;
-        sg.template load<0>(A, B, m0, n0, 0, K, st_t);
-        sg.template load<1>(A, B, m0, n0, kSplitK, K, st_t);
-        sg.template load<2>(A, B, m0, n0, 2 * kSplitK, K, st_t);
-        sg.template stage<0>(A, B, m0, n0, 0, K, lds[0], st_t);
-        if (kSplitK < K) sg.template stage<1>(A, B, m0, n0, kSplitK, K, lds[1], st_t);
-        __syncthreads();
-        for (int k0 = 0; k0 < K; k0 += 3 * kSplitK) {
+        int k0 = 0;
+        // (the x-contiguous summed operand of the back-projection keeps 32 raw values a set, and
+        // three sets of it do not fit next to the general path: it stays on the general loop)
+        if (AK == S6_KC && K >= 8 * kSplitK && St::all_interior(A, B, m0, n0, K)) {
+            // steady state: buffers 0, 1 hold slabs s, s + 1; register sets 2, 0, 1 hold s + 2 .. s + 4
+            sg.template load_fast<0>(A, B, m0, n0, 0, st_t);
+            sg.template load_fast<1>(A, B, m0, n0, kSplitK, st_t);
+            sg.template load_fast<2>(A, B, m0, n0, 2 * kSplitK, st_t);
+            sg.template stage_fast<0>(A, B, m0, n0, 3 * kSplitK, lds[0], st_t);
+            sg.template stage_fast<1>(A, B, m0, n0, 4 * kSplitK, lds[1], st_t);
+            __syncthreads();
+            const int nslab = K / kSplitK;
+            int s = 0;
+            for (; s + 8 <= nslab; s += 3) {
+                sg.template stage_fast<2>(A, B, m0, n0, (s + 5) * kSplitK, lds[2], st_t);
+                __syncthreads();
+                sg.template stage_fast<0>(A, B, m0, n0, (s + 6) * kSplitK, lds[0], st_t);
+                __syncthreads();
+                sg.template stage_fast<1>(A, B, m0, n0, (s + 7) * kSplitK, lds[1], st_t);
+                __syncthreads();
+            }
+            k0 = s * kSplitK;   // the last slabs: the general loop below, same state
+        } else {
+            sg.template load<0>(A, B, m0, n0, 0, K, st_t);
+            sg.template load<1>(A, B, m0, n0, kSplitK, K, st_t);
+            sg.template load<2>(A, B, m0, n0, 2 * kSplitK, K, st_t);
+            sg.template stage<0>(A, B, m0, n0, 0, K, lds[0], st_t);
+            if (kSplitK < K) sg.template stage<1>(A, B, m0, n0, kSplitK, K, lds[1], st_t);
+            __syncthreads();
+        }
+        for (; k0 < K; k0 += 3 * kSplitK) {
             if (k0 + 2 * kSplitK < K) sg.template stage<2>(A, B, m0, n0, k0 + 2 * kSplitK, K, lds[2], st_t);
             __syncthreads();
             if (k0 + kSplitK >= K) break;

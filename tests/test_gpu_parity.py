@@ -179,6 +179,13 @@ def test_wide_update_tiles(cuda, base, n):
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
 
+def test_split_product_interior_and_edge_tiles(cuda):
+    """fp32-chain product with whole 128 x 128 tiles and K = 512 (16 slabs): the first two row
+    tiles take the branch-free staging loop, the ragged third (m = 300) the general one."""
+    wl = W.SMALL[1].with_groups(W.Group(4, 300, 512, 128), name="split-product-tiles", steps=2)
+    check(run_teacher_forced(wl, cuda), tol_for(wl))
+
+
 @pytest.mark.parametrize("force64", [False, True])
 def test_shifted_first_pass(cuda, force64):
     """8 decades of spectrum: the fp64 chain's plain Cholesky of P0^T P0 breaks down (host fp64
