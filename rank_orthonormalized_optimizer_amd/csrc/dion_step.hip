@@ -1600,12 +1600,8 @@ struct Stage6 {
         lb[J].split_store(lds + 3 * PT, t);
         load<J>(A, B, m0, n0, k + D * kSplitK, K, t);
     }
-    // Interior tiles (every slab whole and inside both operands): the same steps without bounds
-    // tests or conditional loads, so the compiler waits only for the set a store consumes.
-    static __device__ __forceinline__ bool all_interior(const Op6& A, const Op6& B, int m0, int n0, int K) {
-        return K % kSplitK == 0 && Loader6<BT, AK, AADD>::interior(A, m0, K - kSplitK) &&
-               Loader6<BT, BK6, A6_NONE>::interior(B, n0, K - kSplitK);
-    }
+    // Launches whose tiles are all interior (every slab whole and inside both operands) use the
+    // same steps without bounds tests, so the compiler waits only for the set a store consumes.
     template <int J>
     __device__ __forceinline__ void load_fast(const Op6& A, const Op6& B, int m0, int n0, int k, int t) {
         la[J].load_fast(A, m0, k, t);
@@ -1618,9 +1614,16 @@ struct Stage6 {
         lb[J].split_store(lds + 3 * PT, t);
         load_fast<J>(A, B, m0, n0, knext, t);
     }
+    template <int J>
+    __device__ __forceinline__ void stage_fast_if(const Op6& A, const Op6& B, int m0, int n0, int knext, int K,
+                                                  uint16_t* lds, int t) {
+        la[J].split_store(lds, t);
+        lb[J].split_store(lds + 3 * PT, t);
+        if (knext < K) load_fast<J>(A, B, m0, n0, knext, t);
+    }
 };
 
-template <int AK, int AADD, int BK6>
+template <int AK, int AADD, int BK6, bool FAST>
 __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     // Eight waves: waves 0-3 multiply (a 64 x 64 sub-tile each), waves 4-7 stage the operands
     // (load, split into bf16 parts, write LDS).  Each SIMD holds one wave of each kind, so the
@@ -1645,18 +1648,16 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     // with the same barriers, so their registers (raw slabs, accumulators) never overlap.
     if (stager) {
         St sg;
-        int k0 = 0;
-        // (the x-contiguous summed operand of the back-projection keeps 32 raw values a set, and
-        // three sets of it do not fit next to the general path: it stays on the general loop)
-        if (AK == S6_KC && K >= 8 * kSplitK && St::all_interior(A, B, m0, n0, K)) {
-            // steady state: buffers 0, 1 hold slabs s, s + 1; register sets 2, 0, 1 hold s + 2 .. s + 4
+        if constexpr (FAST) {
+            // every tile interior, K a multiple of the slab and at least three slabs.  Steady
+            // state: buffers 0, 1 hold slabs s, s + 1; register sets 2, 0, 1 hold s + 2 .. s + 4.
+            const int nslab = K / kSplitK;
             sg.template load_fast<0>(A, B, m0, n0, 0, st_t);
             sg.template load_fast<1>(A, B, m0, n0, kSplitK, st_t);
             sg.template load_fast<2>(A, B, m0, n0, 2 * kSplitK, st_t);
-            sg.template stage_fast<0>(A, B, m0, n0, 3 * kSplitK, lds[0], st_t);
-            sg.template stage_fast<1>(A, B, m0, n0, 4 * kSplitK, lds[1], st_t);
+            sg.template stage_fast_if<0>(A, B, m0, n0, 3 * kSplitK, K, lds[0], st_t);
+            sg.template stage_fast_if<1>(A, B, m0, n0, 4 * kSplitK, K, lds[1], st_t);
             __syncthreads();
-            const int nslab = K / kSplitK;
             int s = 0;
             for (; s + 8 <= nslab; s += 3) {
                 sg.template stage_fast<2>(A, B, m0, n0, (s + 5) * kSplitK, lds[2], st_t);
@@ -1666,7 +1667,17 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
                 sg.template stage_fast<1>(A, B, m0, n0, (s + 7) * kSplitK, lds[1], st_t);
                 __syncthreads();
             }
-            k0 = s * kSplitK;   // the last slabs: the general loop below, same state
+            for (int k0 = s * kSplitK; k0 < K; k0 += 3 * kSplitK) {
+                if (k0 + 2 * kSplitK < K) sg.template stage_fast_if<2>(A, B, m0, n0, k0 + 5 * kSplitK, K, lds[2], st_t);
+                __syncthreads();
+                if (k0 + kSplitK >= K) break;
+                if (k0 + 3 * kSplitK < K) sg.template stage_fast_if<0>(A, B, m0, n0, k0 + 6 * kSplitK, K, lds[0], st_t);
+                __syncthreads();
+                if (k0 + 2 * kSplitK >= K) break;
+                if (k0 + 4 * kSplitK < K) sg.template stage_fast_if<1>(A, B, m0, n0, k0 + 7 * kSplitK, K, lds[1], st_t);
+                __syncthreads();
+            }
+            return;
         } else {
             sg.template load<0>(A, B, m0, n0, 0, K, st_t);
             sg.template load<1>(A, B, m0, n0, kSplitK, K, st_t);
@@ -1674,18 +1685,18 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
             sg.template stage<0>(A, B, m0, n0, 0, K, lds[0], st_t);
             if (kSplitK < K) sg.template stage<1>(A, B, m0, n0, kSplitK, K, lds[1], st_t);
             __syncthreads();
+            for (int k0 = 0; k0 < K; k0 += 3 * kSplitK) {
+                if (k0 + 2 * kSplitK < K) sg.template stage<2>(A, B, m0, n0, k0 + 2 * kSplitK, K, lds[2], st_t);
+                __syncthreads();
+                if (k0 + kSplitK >= K) break;
+                if (k0 + 3 * kSplitK < K) sg.template stage<0>(A, B, m0, n0, k0 + 3 * kSplitK, K, lds[0], st_t);
+                __syncthreads();
+                if (k0 + 2 * kSplitK >= K) break;
+                if (k0 + 4 * kSplitK < K) sg.template stage<1>(A, B, m0, n0, k0 + 4 * kSplitK, K, lds[1], st_t);
+                __syncthreads();
+            }
+            return;
         }
-        for (; k0 < K; k0 += 3 * kSplitK) {
-            if (k0 + 2 * kSplitK < K) sg.template stage<2>(A, B, m0, n0, k0 + 2 * kSplitK, K, lds[2], st_t);
-            __syncthreads();
-            if (k0 + kSplitK >= K) break;
-            if (k0 + 3 * kSplitK < K) sg.template stage<0>(A, B, m0, n0, k0 + 3 * kSplitK, K, lds[0], st_t);
-            __syncthreads();
-            if (k0 + 2 * kSplitK >= K) break;
-            if (k0 + 4 * kSplitK < K) sg.template stage<1>(A, B, m0, n0, k0 + 4 * kSplitK, K, lds[1], st_t);
-            __syncthreads();
-        }
-        return;
     }
     const int lane = threadIdx.x & 63, wm = (wave >> 1) & 1, wn = wave & 1;
     const int fr = lane & 15, fc = lane >> 4;
@@ -1717,7 +1728,19 @@ template <int AK, int AADD, int BK6>
 static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
     dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128), (unsigned)batch);
-    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6>), grid, dim3(512), 0, s, g);
+    // every tile interior: whole 128-tiles along both output edges, whole slabs, vector-legal
+    // k-contiguous operands (the operand extents are the output extents and K)
+    // (the back-projection's x-contiguous summed operand is not taken: its hoisted row addresses
+    // for three register sets overflow the register file)
+    const bool fast = AK == S6_KC && g.a.vec && g.M % 128 == 0 && g.N % 128 == 0 && g.K % kSplitK == 0 &&
+                      g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K && g.b.xext == g.N && g.b.kext == g.K;
+    if constexpr (AK == S6_KC) {
+        if (fast) {
+            hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true>), grid, dim3(512), 0, s, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false>), grid, dim3(512), 0, s, g);
     return hipGetLastError();
 }
 

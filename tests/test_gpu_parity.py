@@ -179,10 +179,13 @@ def test_wide_update_tiles(cuda, base, n):
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
 
-def test_split_product_interior_and_edge_tiles(cuda):
-    """fp32-chain product with whole 128 x 128 tiles and K = 512 (16 slabs): the first two row
-    tiles take the branch-free staging loop, the ragged third (m = 300) the general one."""
-    wl = W.SMALL[1].with_groups(W.Group(4, 300, 512, 128), name="split-product-tiles", steps=2)
+@pytest.mark.parametrize("m,n", [(256, 512), (256, 448), (256, 480), (300, 512)])
+def test_split_product_launch_kinds(cuda, m, n):
+    """fp32-chain product, r = 128: with whole 128 x 128 tiles and whole slabs (m = 256; K = n =
+    512, 448 or 480, i.e. 16, 14 or 15 slabs, leaving 7, 5 and 6 slabs to the drain after the
+    steady loop) the launch takes the branch-free staging loop; m = 300 (a ragged row tile)
+    takes the general one."""
+    wl = W.SMALL[1].with_groups(W.Group(4, m, n, 128), name=f"split-product-{m}x{n}", steps=2)
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
 
