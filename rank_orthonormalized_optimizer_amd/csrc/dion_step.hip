@@ -48,9 +48,7 @@ constexpr double kTau64 = 1.0e7;
 // eps = 3e-7 (error ~ eps^2 <= 1e-13); up to 1e-3 two fixed-point steps (error eps^2 (2 eps)^2
 // <= 4e-12) and S up to F^3 (truncation eps^4 <= 1e-12); beyond, the Cholesky pass.
 constexpr double kNearId32 = 1.0e-4;
-constexpr double kNearIdFast64 = 3.0e-7;
-constexpr double kNearId64 = 1.0e-3;
-constexpr int kNearIdIters64 = 2, kNearIdTerms64 = 2;
+constexpr double kNearId64 = 1.0e-6;
 
 // ---------------------------------------------------------------------------
 // generic batched GEMM:  C = alpha * A B + beta * C
@@ -72,8 +70,6 @@ struct GemmArgs {
     int ksplit_total;          // > 0: group g covers K rows [g K, min((g + 1) K, ksplit_total)) of
                                // the operands (their base advanced by ga0 / gb0 per group)
     const void* csrc;          // beta term read from here instead of c (same layout), if set
-    int phi;                   // epilogue c = Phi(csrc - I + alpha acc): strictly lower part kept,
-                               // diagonal halved, upper part zero (square outputs only)
 };
 
 // fp64 tiles are held to 128 registers a lane so that four workgroups share a CU (their LDS
@@ -125,7 +121,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmA
     T* Cp = (T*)((char*)g.c + bz * g.sc + grp * g.gc);
     const T* Sp = g.csrc ? (const T*)((const char*)g.csrc + bz * g.sc + grp * g.gc) : Cp;
     const T alpha = (T)g.alpha, beta = (T)g.beta;
-    const bool need_src = g.phi || beta != T(0);
+    const bool need_src = beta != T(0);
     // all source loads of the tile before the first store (see the update kernel's epilogue)
     T sv[C::FM][C::FN][4];
     if (need_src) {
@@ -150,12 +146,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmA
                 const int col = n0 + wn * C::WTN + j * 16 + (lane & 15);
                 if (row < g.M && col < g.N) {
                     T val = alpha * acc[i][j][v];
-                    if (g.phi) {
-                        val += sv[i][j][v] - (row == col ? T(1) : T(0));
-                        val = row > col ? val : (row == col ? T(0.5) * val : T(0));
-                    } else if (beta != T(0)) {
-                        val += beta * sv[i][j][v];
-                    }
+                    if (need_src) val += beta * sv[i][j][v];
                     Cp[(int64_t)row * g.ldc + col] = val;
                 }
             }
@@ -1401,28 +1392,26 @@ static int cholqr_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int v
 
 // Re-orthonormalization of a nearly orthonormal P1 (the second CholeskyQR pass) without a
 // sequential factorization.  With W = P1^T P1 = I + E and chol(W) = I + F, F lower triangular,
-// F + F^T + F F^T = E, i.e. F = Phi(E - F F^T) where Phi keeps the strictly lower part and half
-// the diagonal.  Then (I + F)^-1 = I - S with S = F - F^2 + F^3 - ..., and
-// P = P1 (I + F)^-T = P1 - P1 S^T.  With eps = ||E||_F (>= ||E||_2, >= ||F||_2 up to O(eps^2)):
-//   eps <= tau_fast:            F = Phi(E), S = F; error O(eps^2)
-//   tau_fast < eps <= tau_chol: nit fixed-point steps F <- Phi(E - F F^T) (error eps^2 (2 eps)^nit)
-//                               and S <- F - F S nn times (truncation eps^(nn + 2))  [ST_SERIES]
-//   eps > tau_chol (or not finite): the blocked Cholesky pass                        [ST_CHOL2]
-// all decided per matrix on the device.
+// F + F^T + F F^T = E, so F = Phi(E) + O(eps^2), where Phi keeps the strictly lower part and half
+// the diagonal and eps = ||E||_F (>= ||E||_2).  Then (I + F)^-1 = I - F + O(eps^2), and
+// P = P1 (I + F)^-T = P1 (I - Phi(E))^T with error O(eps^2).  Per matrix, decided on the device:
+//   eps <= tau:               T = I - Phi(E)          (error <= ~eps^2)
+//   eps > tau, or not finite: T = L^-1 of the blocked Cholesky pass              [ST_CHOL2]
+// and one apply P = P1 T^T serves both.
 // Setup of a re-orthonormalization pass (grid: parts x matrices): W = the sum of the split-K
-// Gram partials in split order (when the Gram was split; lower triangle), F = Phi(E) with
+// Gram partials in split order (when the Gram was split; lower triangle), T = I - Phi(E) with
 // E = W - I, and per workgroup the sum of squares of E over its share.  (A last-arriving
 // workgroup could decide in place, but its device-scope fence writes back the L2 of every XCD;
 // a separate launch is cheaper.)
 template <typename T>
-__global__ __launch_bounds__(256) void near_id_setup_kernel(const T* gpart, int64_t splits, T* W, T* F,
+__global__ __launch_bounds__(256) void near_id_setup_kernel(const T* gpart, int64_t splits, T* W, T* Tm,
                                                             double* part, int64_t r, const int* st, int st_mask,
                                                             int st_val) {
     const int bz = blockIdx.y;
     if ((st[bz] & st_mask) != st_val) return;
     const int64_t total = r * r;
     W += bz * total;
-    F += bz * total;
+    Tm += bz * total;
     if (gpart) gpart += bz * splits * total;
     double ss = 0.0;   // sum of squares of E over the full symmetric matrix
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
@@ -1440,12 +1429,11 @@ __global__ __launch_bounds__(256) void near_id_setup_kernel(const T* gpart, int6
             const T e = w - (i == k ? T(1) : T(0));
             const double d = (double)e;
             ss += (i == k ? 1.0 : 2.0) * d * d;
-            v = (i == k) ? T(0.5) * e : e;
+            v = (i == k) ? T(1) - T(0.5) * e : -e;
         }
-        F[idx] = v;
+        Tm[idx] = v;
     }
     __shared__ double red[256];
-    __shared__ int last;
     red[threadIdx.x] = ss;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -1455,51 +1443,22 @@ __global__ __launch_bounds__(256) void near_id_setup_kernel(const T* gpart, int6
     if (threadIdx.x == 0) part[(int64_t)bz * kNearIdParts + blockIdx.x] = red[0];
 }
 
-// Regime bits of each selected matrix from ||E||_F, the partial sums added in part order.
+// Regime bit of each selected matrix from ||E||_F, the partial sums added in part order.
 __global__ void near_id_decide_kernel(const double* part, int nparts, int* st, int64_t b, int st_mask, int st_val,
-                                      double tau_fast, double tau_chol) {
+                                      double tau) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= b || (st[i] & st_mask) != st_val) return;
     double ss = 0.0;
     for (int q = 0; q < nparts; ++q) ss += part[i * kNearIdParts + q];
     const double e = sqrt(ss);
-    int sv = st[i] & ~(ST_CHOL2 | ST_SERIES);
-    if (!(e <= tau_chol)) sv |= ST_CHOL2;            // also NaN / Inf
-    else if (e > tau_fast) sv |= ST_SERIES;
-    st[i] = sv;
-}
-
-// Pout = Pin - Pin S^T for the matrices selected by (mask, val).
-template <typename T>
-static int near_id_apply(const ChainCtx& c, const T* Pin, T* Pout, const T* S, int mask, int val) {
-    const Plan& p = *c.p;
-    const int64_t m = p.m, r = p.r;
-    constexpr int SR = SrcOf<T>::v;
-    const bool vr = (r % 4) == 0;
-    GemmArgs g{};
-    g.a = Operand{Pin, nullptr, r, (int)m, (int)r, vr};   // A(i,k) = Pin[i][k]
-    g.b = Operand{S, nullptr, r, (int)r, (int)r, vr};     // B(k,j) = S[j][k]
-    g.sa0 = m * r * (int64_t)sizeof(T);
-    g.sb0 = r * r * (int64_t)sizeof(T);
-    g.c = Pout; g.ldc = r; g.sc = m * r * (int64_t)sizeof(T); g.csrc = Pin;
-    g.M = (int)m; g.N = (int)r; g.K = (int)r;
-    g.alpha = -1; g.beta = 1; g.kskip = 1;
-    g.st = c.st; g.st_mask = mask; g.st_val = val;
-    DION_TRY((launch_gemm<T, 64, 64, true, SR, true, SR>(g, p.b, c.s)));
-    return 0;
+    st[i] = (e <= tau) ? (st[i] & ~ST_CHOL2) : (st[i] | ST_CHOL2);   // not finite: Cholesky
 }
 
 template <typename T>
-static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, int nit, int nn, double tau_fast,
-                        double tau_chol, int fail_bit) {
+static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val, double tau, int fail_bit) {
     const Plan& p = *c.p;
     const int64_t r = p.r, b = p.b;
-    constexpr int S = SrcOf<T>::v;
-    const bool vr = (r % 4) == 0;
-    const bool series = nit + nn > 0;
-    if (!series) tau_fast = tau_chol;
     T* W = (T*)(c.ws + p.W);
-    T* bufs[3] = {(T*)(c.ws + p.L), (T*)(c.ws + p.Tf), W};
     double* part = (double*)(c.ws + p.emax);
     int e;
     if ((e = gram<T>(c, Pin, mask, val, false))) return e;
@@ -1510,55 +1469,17 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
         const unsigned nparts = grid_1d(r * r, per);
         dim3 grid(nparts, (unsigned)b);
         const T* gp = p.gsplit > 1 ? (const T*)(c.ws + p.gpart) : nullptr;
-        hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, p.gsplit, W, bufs[0], part, r,
-                           (const int*)c.st, mask, val);
+        hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, p.gsplit, W, (T*)(c.ws + p.Tf),
+                           part, r, (const int*)c.st, mask, val);
         DION_TRY(hipGetLastError());
         hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part,
-                           (int)nparts, c.st, b, mask, val, tau_fast, tau_chol);
+                           (int)nparts, c.st, b, mask, val, tau);
         DION_TRY(hipGetLastError());
     }
-    const int nmask = mask | ST_CHOL2 | ST_SERIES;
-    // first-order matrices: S = F = Phi(E)
-    if ((e = near_id_apply<T>(c, Pin, Pout, bufs[0], nmask, val))) return e;
-    if (series) {
-        const int smask = nmask, sval = val | ST_SERIES;
-        const int64_t rr = r * r * (int64_t)sizeof(T);
-        int fi = 0;                                                // buffer holding F
-        for (int it = 0; it < nit; ++it) {                         // F <- Phi(W - I - F F^T)
-            const int fo = fi ^ 1;
-            GemmArgs g{};
-            g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
-            g.b = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = F[j][k]
-            g.sa0 = g.sb0 = g.sc = rr;
-            g.c = bufs[fo]; g.ldc = r; g.csrc = W; g.phi = 1;
-            g.M = g.N = (int)r; g.K = (int)r;
-            g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 1;
-            g.st = c.st; g.st_mask = smask; g.st_val = sval;
-            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
-            fi = fo;
-        }
-        int si = fi;                                               // buffer holding S (S0 = F)
-        int free_[2], nf = 0;
-        for (int q = 0; q < 3; ++q) if (q != fi) free_[nf++] = q;
-        for (int it = 0; it < nn; ++it) {                          // S <- F - F S
-            const int so = free_[it & 1];
-            GemmArgs g{};
-            g.a = Operand{bufs[fi], nullptr, r, (int)r, (int)r, vr};   // A(i,k) = F[i][k]
-            g.b = Operand{bufs[si], nullptr, r, (int)r, (int)r, vr};   // B(k,j) = S[k][j]
-            g.sa0 = g.sb0 = g.sc = rr;
-            g.c = bufs[so]; g.ldc = r; g.csrc = bufs[fi];
-            g.M = g.N = (int)r; g.K = (int)r;
-            g.alpha = -1; g.beta = 1; g.lower = 1; g.kskip = 4;
-            g.st = c.st; g.st_mask = smask; g.st_val = sval;
-            DION_TRY((launch_gemm<T, 64, 64, true, S, false, S>(g, b, c.s)));
-            si = so;
-        }
-        if ((e = near_id_apply<T>(c, Pin, Pout, bufs[si], smask, sval))) return e;
-    }
-    // the others: a full Cholesky pass (W is untouched for them)
+    // matrices far from orthonormal: a full Cholesky pass (W is untouched), T = L^-1
     const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
     if ((e = factor_invert<T>(c, cmask, cval, 0.0, fail_bit, 0, 0, true))) return e;
-    return apply<T>(c, Pin, Pout, cmask, cval);
+    return apply<T>(c, Pin, Pout, mask, val);
 }
 
 // ---------------------------------------------------------------------------
@@ -1828,7 +1749,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
         DION_TRY(c.open_gate());
         DION_TRY(mark(1));
         if ((e = cholqr_pass<T>(c, P, tmp, mask, val, force32 ? 0.0 : kTau32, fail, ST_PATH64))) return e;
-        if ((e = reortho_pass<T>(c, tmp, P, mask, val, 0, 0, kNearId32, kNearId32, fail))) return e;
+        if ((e = reortho_pass<T>(c, tmp, P, mask, val, kNearId32, fail))) return e;
         DION_TRY(mark(2));
         return g_bf16 ? btp_gemm<T, SRC_SUM_BF16>(c, M, G, gsz, P, R, mask, val)
                       : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, mask, val);
@@ -1848,12 +1769,9 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     if ((e = factor_invert<T>(c, A64 | SH | F, A64 | SH, 0.0, F, 0, 1, true))) return e;
     if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
     // pass 2
-    if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearIdIters64, kNearIdTerms64, kNearIdFast64, kNearId64, F)))
-        return e;
+    if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearId64, F))) return e;
     // pass 3, only after a shifted first pass
-    if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearIdIters64, kNearIdTerms64, kNearIdFast64, kNearId64,
-                             F)))
-        return e;
+    if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearId64, F))) return e;
     {
         dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
         hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st, A64 | SH | F,
