@@ -1157,6 +1157,11 @@ struct CholInvArgs {
     double tau;
     int fail_bit, tau_bit, shift;
     double c_shift;
+    // second-pass use: the near-identity partial sums of ||P^T P - I||_F^2 ([b][kNearIdParts],
+    // nparts used); a matrix whose norm is <= ntau keeps its first-order T and returns
+    const double* npart;
+    int nparts;
+    double ntau;
 };
 
 // C (M x N <= 64 x 64, ldc) = alpha A B + beta C with A(i,k) k-contiguous and B either
@@ -1205,6 +1210,17 @@ __global__ __launch_bounds__(256) void cholinv_kernel(CholInvArgs a) {
     __shared__ T As[2 * C::A_STAGE];
     __shared__ T Bs[2 * C::B_STAGE];
     __shared__ double red[256];
+    if (a.npart) {   // the regime test of the second pass, partial sums added by a fixed tree
+        red[threadIdx.x] = (int)threadIdx.x < a.nparts ? a.npart[(int64_t)bz * kNearIdParts + threadIdx.x] : 0.0;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+            __syncthreads();
+        }
+        const double e = sqrt(red[0]);
+        __syncthreads();
+        if (e <= a.ntau) return;   // first-order: T = I - Phi(E) is already in place (not finite: go on)
+    }
     const int64_t r = a.r, rr = r * r, nblk = a.nblk;
     const T* W = (const T*)a.W + bz * rr;
     T* L = (T*)a.L + bz * rr;
@@ -1281,7 +1297,7 @@ __global__ __launch_bounds__(256) void cholinv_kernel(CholInvArgs a) {
 // factor + invert for the matrices with (st & mask) == val
 template <typename T>
 static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
-                         bool rare);
+                         bool rare, const double* npart = nullptr, int nparts = 0, double ntau = 0.0);
 
 // Tf = L^-1 (lower, [b][r][r]) from the factor L and the inverted diagonal blocks already in
 // Tf, by recursive doubling over the blocks: for neighbouring block ranges U (above) and V
@@ -1340,7 +1356,7 @@ static int invert(const ChainCtx& c, int mask, int val) {
 // factorization, which spreads the panel and trailing products over many CUs.
 template <typename T>
 static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
-                         bool rare) {
+                         bool rare, const double* npart, int nparts, double ntau) {
     const Plan& p = *c.p;
     if (!rare || p.nblk > kFusedMaxBlocks) {
         int e;
@@ -1356,6 +1372,7 @@ static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int f
     a.tau = tau; a.fail_bit = fail_bit; a.tau_bit = tau_bit; a.shift = shift;
     const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
     a.c_shift = 11.0 * ((double)p.m * p.r + (double)p.r * (p.r + 1)) * u;
+    a.npart = npart; a.nparts = nparts; a.ntau = ntau;
     hipLaunchKernelGGL((cholinv_kernel<T>), dim3((unsigned)p.b), dim3(256), 0, c.s, a);
     return (int)hipGetLastError();
 }
@@ -1472,11 +1489,16 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
         hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, p.gsplit, W, (T*)(c.ws + p.Tf),
                            part, r, (const int*)c.st, mask, val);
         DION_TRY(hipGetLastError());
+        if (p.nblk <= kFusedMaxBlocks) {
+            // matrices far from orthonormal: a full Cholesky pass (W is untouched), T = L^-1, in
+            // the fused factorization, which makes the regime test itself
+            if ((e = factor_invert<T>(c, mask, val, 0.0, fail_bit, 0, 0, true, part, (int)nparts, tau))) return e;
+            return apply<T>(c, Pin, Pout, mask, val);
+        }
         hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part,
                            (int)nparts, c.st, b, mask, val, tau);
         DION_TRY(hipGetLastError());
     }
-    // matrices far from orthonormal: a full Cholesky pass (W is untouched), T = L^-1
     const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
     if ((e = factor_invert<T>(c, cmask, cval, 0.0, fail_bit, 0, 0, true))) return e;
     return apply<T>(c, Pin, Pout, mask, val);
