@@ -7,9 +7,8 @@
 // core adds the kept products in fp32.  One bf16 MFMA does 16 x 16 x 32 at about 14 times the
 // flop rate of the fp32 MFMA, so the six cost about 0.42 of the fp32 MFMA work.
 //
-// Split operands are stored as three planes [part][rows][kp] of bf16 (h, m, l), with kp the
-// contraction length rounded up to a multiple of 32 and zero padding, so every row starts on
-// a 64-byte boundary and a k-slab of 32 is four 16-byte chunks per row.
+// Operands stay fp32 in memory and are split while they are staged into LDS, as three bf16
+// part tiles (h, m, l) of one 32-k slab, with zeros beyond the contraction length.
 //
 // Lane layout of v_mfma_f32_16x16x32_bf16 (measured on gfx950 with a one-wave probe):
 //   A: lane l holds A[l % 16][8 (l / 16) + i], i = 0..7
@@ -26,7 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitK = 32;   // k-slab of one bf16 MFMA and padding unit of the planes
+constexpr int kSplitK = 32;   // k-slab of one bf16 MFMA
 
 __host__ __device__ constexpr int64_t split_kp(int64_t k) { return (k + kSplitK - 1) / kSplitK * kSplitK; }
 
@@ -65,7 +64,7 @@ namespace dion {
 // fetches its raw values, split() turns them into bf16 parts in registers, store() writes them.
 // ---------------------------------------------------------------------------
 enum Src6 : int {
-    S6_PLANES = 0,   // pre-split planes p0[3][rows][ld] (h, m, l), k contiguous, zero padded to ld
+    S6_KC8 = 0,      // fp32 p0[x * ld + k], k contiguous, staged in chunks of eight k
     S6_KC = 1,       // fp32 p0[x * ld + k] (+ addend p1 at the same index), k contiguous
     S6_XC = 2,       // fp32 p0[k * ld + x] (+ addend p1 at the same index), x contiguous
 };
@@ -75,7 +74,6 @@ struct Op6 {
     const void* p0;
     const void* p1;     // addend (B = M + G), or null
     int64_t ld;         // pitch in elements between rows of the stored array
-    int64_t plane;      // elements per plane (S6_PLANES)
     int xext, kext;     // valid extents along x and k (outside: zeros)
     bool vec;           // S6_KC: 4-element vector loads are legal (ld, bases aligned)
 };
@@ -129,42 +127,50 @@ __device__ __forceinline__ void store4(uint16_t* lds, int part_stride, int x, in
 template <int BX, int KIND, int ADD>
 struct Loader6;
 
-// pre-split planes: BX * 4 chunks of 16 bytes per part, BX / 64 per thread
+// k-contiguous fp32, no addend, in chunks of eight k: BX * 4 chunks, BX / 64 per thread (four
+// threads per row), so each part of a chunk is one 16-byte LDS write at its swizzled slot.
 template <int BX, int ADD>
-struct Loader6<BX, S6_PLANES, ADD> {
+struct Loader6<BX, S6_KC8, ADD> {
+    static_assert(ADD == A6_NONE, "no addend");
     static constexpr int PER = BX / 64;
-    u32x4 r[3][PER];
-    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int x = (t >> 2) + 64 * q, c = t & 3;
-            const bool ok = x0 + x < op.xext;
-            const int64_t o = (int64_t)(ok ? x0 + x : 0) * op.ld + k0 + 8 * c;
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-                r[p][q] = ok ? *(const u32x4*)((const uint16_t*)op.p0 + p * op.plane + o) : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-    // interior tile: no bounds tests (branch-free, so the loads in flight can be counted)
+    float a[PER][8];
     __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
+        const int xr = t >> 2, kk = 8 * (t & 3);
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int x = (t >> 2) + 64 * q, c = t & 3;
-            const int64_t o = (int64_t)(x0 + x) * op.ld + k0 + 8 * c;
-#pragma unroll
-            for (int p = 0; p < 3; ++p) r[p][q] = *(const u32x4*)((const uint16_t*)op.p0 + p * op.plane + o);
+            const float* src = (const float*)op.p0 + (int64_t)(x0 + xr + 64 * q) * op.ld + k0 + kk;
+            const float4 v0 = *(const float4*)src, v1 = *(const float4*)(src + 4);
+            a[q][0] = v0.x; a[q][1] = v0.y; a[q][2] = v0.z; a[q][3] = v0.w;
+            a[q][4] = v1.x; a[q][5] = v1.y; a[q][6] = v1.z; a[q][7] = v1.w;
         }
     }
-    __device__ __forceinline__ void split() {}
-    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
+    static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
+        return op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
+    }
+    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
+        if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
+        const int xr = t >> 2, kk = 8 * (t & 3);
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
+            const int x = x0 + xr + 64 * q, k = k0 + kk;
+            const int64_t o = (int64_t)(x < op.xext ? x : 0) * op.ld + k;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a[q][e] = (x < op.xext && k + e < op.kext) ? ((const float*)op.p0)[o + e] : 0.f;
+        }
+    }
+    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const float v0[4] = {a[q][0], a[q][1], a[q][2], a[q][3]};
+            const float v1[4] = {a[q][4], a[q][5], a[q][6], a[q][7]};
+            const Parts4 lo = split4(v0), hi = split4(v1);
             const int off = part_off((t >> 2) + 64 * q, t & 3);
 #pragma unroll
-            for (int p = 0; p < 3; ++p) *(u32x4*)&lds[p * BX * kSplitK + off] = r[p][q];
+            for (int p = 0; p < 3; ++p)
+                *(u32x4*)&lds[p * BX * kSplitK + off] = u32x4{lo.p[p].x, lo.p[p].y, hi.p[p].x, hi.p[p].y};
         }
     }
-    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const { store(lds, t); }
 };
 
 // k-contiguous fp32 (+ addend): BX * 8 groups of four k, BX / 32 per thread (8 threads per row).

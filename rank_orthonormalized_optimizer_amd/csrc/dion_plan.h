@@ -28,12 +28,12 @@ struct Plan {
     int64_t nblk;      // number of rank column blocks
     int64_t nchunk;    // row chunks of the column-norm reduction
     int64_t gsplit;    // K-splits of the Gram products (partials reduced in fixed order)
-    int64_t kp;        // rank padded to a multiple of 32 (bf16 split planes of P, R, Q)
+    int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
     // byte offsets into the workspace (all 256-byte aligned)
-    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, Pp, Rp, Qp;
+    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart;
     size_t total;
     // bytes per matrix of each region (a region is [batch][...] and contiguous)
-    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, sPp, sRp, sQp;
+    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart;
 };
 
 // The sub-plan of matrices [c0, c0 + cb): same sizes, region offsets advanced to matrix c0.
@@ -44,7 +44,6 @@ inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
     q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart; q.gpart += c * p.sgpart;
-    q.Pp += c * p.sPp; q.Rp += c * p.sRp; q.Qp += c * p.sQp;
     return q;
 }
 
@@ -80,8 +79,8 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     size_t off = 0;
     auto take = [&](double bytes) { size_t o = off; off = align256(off + (size_t)bytes); return o; };
     const double B = (double)b;
-    q.P32 = take(B * m * r * 4);           // fp32 P (fp32 chain works in place here)
-    q.R32 = take(B * n * r * 4);           // fp32 R
+    q.P32 = take(B * m * r * 4);           // fp32 P (fp32 chain works in place here; weight pass)
+    q.R32 = take(B * n * r * 4);           // fp32 R (weight pass)
     q.cs = take(B * r * 8);                // 1 / (||r_j|| + eps), fp64
     q.st = take(B * 4);                    // state words
     q.kap = take(B * 2 * 8);               // running min / max Cholesky diagonal
@@ -95,16 +94,12 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.R64 = take(B * n * r * 8);           // fp64 chain R
     q.part = take(B * q.nchunk * r * 8);   // column-norm partial sums (fp64)
     q.gpart = take(q.gsplit > 1 ? B * q.gsplit * r * r * 8 : 0);   // Gram partials
-    q.Pp = take(B * 3 * m * q.kp * 2);     // bf16 split planes of P (weight pass)
-    q.Rp = take(B * 3 * n * q.kp * 2);     // ... of R
-    q.Qp = take(B * 3 * n * q.kp * 2);     // ... of the next Q
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
     q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = kNearIdParts * 8;
     q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
     q.sgpart = q.gsplit > 1 ? (size_t)(q.gsplit * r * r * 8) : 0;
-    q.sPp = (size_t)(3 * m * q.kp * 2); q.sRp = q.sQp = (size_t)(3 * n * q.kp * 2);
     *p = q;
     return true;
 }

@@ -569,58 +569,39 @@ __device__ __forceinline__ void row4(const double* p64src, float* p32, int64_t o
     }
 }
 
-// Q <- R * c (fp32), for fp64-chain matrices R32 <- R64 rounded, and the bf16 split planes of
-// R32 and Q (k padded to kp with zeros) for the weight pass; four k per thread.
+// Q <- R * c (fp32), and for fp64-chain matrices R32 <- R64 rounded (the weight pass reads the
+// fp32 R); four k per thread.
 __global__ __launch_bounds__(256) void next_q_kernel(const double* R64, float* R32, const double* cs, float* Q,
-                                                     uint16_t* Rp, uint16_t* Qp, int64_t n, int64_t r, int64_t kp,
-                                                     const int* st) {
+                                                     int64_t n, int64_t r, const int* st) {
     const int bz = blockIdx.y;
     const bool p64 = (st[bz] & ST_PATH64) != 0, vec = (r % 4) == 0;
-    const int64_t nr = n * r, total = n * kp, groups = total / 4, gpr = kp / 4;
-    uint16_t* rp = Rp + bz * 3 * total;
-    uint16_t* qp = Qp + bz * 3 * total;
+    const int64_t nr = n * r, gpr = (r + 3) / 4, groups = n * gpr;
     const double* c = cs + bz * r;
     for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
         const int64_t i = gi / gpr, k = 4 * (gi % gpr), o = bz * nr + i * r + k;
         double v[4];
         row4(R64, R32, o, k, r, p64, vec, v);
-        float rv[4], qv[4];
+        float qv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            rv[e] = (float)v[e];
-            qv[e] = k + e < r ? (float)(v[e] * c[k + e]) : 0.f;
-        }
-        if (vec && k < r) *(float4*)(Q + o) = float4{qv[0], qv[1], qv[2], qv[3]};
+        for (int e = 0; e < 4; ++e) qv[e] = k + e < r ? (float)(v[e] * c[k + e]) : 0.f;
+        if (vec) *(float4*)(Q + o) = float4{qv[0], qv[1], qv[2], qv[3]};
         else
 #pragma unroll
             for (int e = 0; e < 4; ++e) if (k + e < r) Q[o + e] = qv[e];
-        const Parts4 pr = split4(rv), pq = split4(qv);
-        const int64_t pidx = i * kp + k;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            *(u32x2*)(rp + q * total + pidx) = pr.p[q];
-            *(u32x2*)(qp + q * total + pidx) = pq.p[q];
-        }
     }
 }
 
-// P32 <- P64 rounded for fp64-chain matrices, and the bf16 split planes of P32 for all; four
-// k per thread.
-__global__ __launch_bounds__(256) void split_p_kernel(const double* P64, float* P32, uint16_t* Pp, int64_t m,
-                                                      int64_t r, int64_t kp, const int* st) {
+// P32 <- P64 rounded, for fp64-chain matrices (the fp32 chain's P is already there).
+__global__ __launch_bounds__(256) void round_p_kernel(const double* P64, float* P32, int64_t m, int64_t r,
+                                                      const int* st) {
     const int bz = blockIdx.y;
-    const bool p64 = (st[bz] & ST_PATH64) != 0, vec = (r % 4) == 0;
-    const int64_t mr = m * r, total = m * kp, groups = total / 4, gpr = kp / 4;
-    uint16_t* pp = Pp + bz * 3 * total;
+    if ((st[bz] & ST_PATH64) == 0) return;
+    const bool vec = (r % 4) == 0;
+    const int64_t mr = m * r, gpr = (r + 3) / 4, groups = m * gpr;
     for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
         const int64_t i = gi / gpr, k = 4 * (gi % gpr), o = bz * mr + i * r + k;
         double v[4];
-        row4(P64, P32, o, k, r, p64, vec, v);
-        const float f[4] = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        const Parts4 pr = split4(f);
-        const int64_t pidx = i * kp + k;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) *(u32x2*)(pp + q * total + pidx) = pr.p[q];
+        row4(P64, P32, o, k, r, true, vec, v);
     }
 }
 
@@ -628,50 +609,44 @@ __global__ __launch_bounds__(256) void split_p_kernel(const double* P64, float* 
 // momentum / weight pass:  M <- (M + G) - (1 - mu) P R^T,  X <- X - lr s P Q^T
 // ---------------------------------------------------------------------------
 struct UpdArgs {
-    const uint16_t* Pp; const uint16_t* Rp; const uint16_t* Qp;   // split planes [b][3][rows][kp]
+    const float* P; const float* R; const float* Q;   // fp32 [b][rows][r], k contiguous
     float* M; const void* G; void* X;
-    int m, n, kp;
+    int m, n, r, kp;                                  // kp: r rounded up to whole 32-k slabs
+    bool vec;                                         // r % 4 == 0: 16-byte row loads
     float one_minus_mu, lr_s;
 };
 
 // One BM x BN tile of M and X per workgroup of WGM x WGN waves: both rank-kp products on the
 // bf16 matrix cores in the six-term split form (fp32 accuracy), sharing the P fragments, then
-// one pass over the tile of M, G and X.  Nine part tiles (P, R, Q x h, m, l) per 32-k slab,
-// double-buffered in LDS; each thread stages one 16-byte chunk of each.
+// one pass over the tile of M, G and X.  P, R and Q are read as fp32 and split into their
+// three bf16 parts on the way into LDS; nine part tiles (P, R, Q x h, m, l) per 32-k slab,
+// double-buffered.
 template <int BM, int BN, int WGM, int WGN, bool G_BF16, bool X_BF16>
 __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
     constexpr int NT = WGM * WGN * 64, BK = kSplitK;
     constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
-    static_assert(BM * 4 == NT && BN * 4 == NT, "one staged chunk per thread and part tile");
+    static_assert(NT == 256, "the split loaders stage with 256 threads");
     static_assert(FM * WGM * 16 == BM && FN * WGN * 16 == BN, "whole MFMA blocks per wave");
     const TileId tid = xcd_tile_id();
     const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
     __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][3][BM * BK];   // P h m l
     __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][6][BN * BK];   // R h m l | Q h m l
-    const int64_t ps = (int64_t)u.m * u.kp, ns = (int64_t)u.n * u.kp;
-    const uint16_t* srcP = u.Pp + (int64_t)bz * 3 * ps;
-    const uint16_t* srcR = u.Rp + (int64_t)bz * 3 * ns;
-    const uint16_t* srcQ = u.Qp + (int64_t)bz * 3 * ns;
-    const int t = threadIdx.x, lx = t >> 2, lc = t & 3;        // staging: row lx, 16-byte chunk lc
-    const bool okA = m0 + lx < u.m, okB = n0 + lx < u.n;
-    const int64_t gA = (int64_t)(okA ? m0 + lx : 0) * u.kp + 8 * lc;
-    const int64_t gB = (int64_t)(okB ? n0 + lx : 0) * u.kp + 8 * lc;
-    const int so = part_off(lx, lc);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    u32x4 stg[9];
+    const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
+    const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
+    const Op6 oR{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
+    const Op6 oQ{u.Q + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
+    const int t = threadIdx.x;
+    Loader6<BM, S6_KC8, A6_NONE> lp;
+    Loader6<BN, S6_KC8, A6_NONE> lr, lq;
     auto gload = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            stg[q] = okA ? *(const u32x4*)(srcP + q * ps + gA + k0) : z;
-            stg[3 + q] = okB ? *(const u32x4*)(srcR + q * ns + gB + k0) : z;
-            stg[6 + q] = okB ? *(const u32x4*)(srcQ + q * ns + gB + k0) : z;
-        }
+        lp.load(oP, m0, k0, t);
+        lr.load(oR, n0, k0, t);
+        lq.load(oQ, n0, k0, t);
     };
     auto lstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 3; ++q) *(u32x4*)&ldsA[buf][q][so] = stg[q];
-#pragma unroll
-        for (int q = 0; q < 6; ++q) *(u32x4*)&ldsB[buf][q][so] = stg[3 + q];
+        lp.split_store(&ldsA[buf][0][0], t);
+        lr.split_store(&ldsB[buf][0][0], t);
+        lq.split_store(&ldsB[buf][3][0], t);
     };
 
     const int lane = t & 63, wave = t >> 6, wm = wave / WGN, wn = wave % WGN;
@@ -758,13 +733,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
 }
 
 // The weight pass for large stacks: 128 x 64 tiles of M and X, four waves of 64 x 32 that
-// both stage (a copy of the split planes) and multiply, and a single-buffered 48 KB LDS stage
-// (two barriers per slab).  Two workgroups fit on a CU, so one workgroup's memory-bound
+// both stage (fp32 P, R and Q rows, split into bf16 parts on the way into LDS: 32 KB read per
+// slab where pre-split parts would take 48 KB) and multiply, and a single-buffered 48 KB LDS
+// stage (two barriers per slab).  Two workgroups fit on a CU, so one workgroup's memory-bound
 // epilogue (the loads of each half-tile issued before its stores) runs while the other keeps
 // the matrix cores busy.
 
 // Streaming (non-temporal) 16- and 8-byte accesses for the weight pass's M, G and X, which are
-// touched once: they then leave the L2 to the split planes that every tile re-reads.
+// touched once: they then leave the L2 to the P, R and Q rows that every tile re-reads.
 __device__ __forceinline__ float4 nt_ld4(const float* p) {
     const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
     return float4{v[0], v[1], v[2], v[3]};
@@ -781,12 +757,12 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     const TileId tid = xcd_tile_id();
     const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
     __shared__ __attribute__((aligned(16))) uint16_t lds[3 * PA + 6 * PB];   // P h m l | R h m l | Q h m l
-    const int64_t ps = (int64_t)u.m * u.kp, ns = (int64_t)u.n * u.kp;
-    const Op6 oP{u.Pp + (int64_t)bz * 3 * ps, nullptr, u.kp, ps, u.m, u.kp, true};
-    const Op6 oR{u.Rp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
-    const Op6 oQ{u.Qp + (int64_t)bz * 3 * ns, nullptr, u.kp, ns, u.n, u.kp, true};
-    Loader6<BM, S6_PLANES, A6_NONE> lp;
-    Loader6<BN, S6_PLANES, A6_NONE> lr, lq;
+    const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
+    const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
+    const Op6 oR{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
+    const Op6 oQ{u.Q + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
+    Loader6<BM, S6_KC8, A6_NONE> lp;
+    Loader6<BN, S6_KC8, A6_NONE> lr, lq;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     const int fr = lane & 15, fc = lane >> 4;
     f32x4 acc1[FM][FN], acc2[FM][FN];
@@ -800,9 +776,9 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
         lq.load(oQ, n0, k, t);
     };
     auto store = [&]() {
-        lp.store(lds, t);
-        lr.store(lds + 3 * PA, t);
-        lq.store(lds + 3 * PA + 3 * PB, t);
+        lp.split_store(lds, t);
+        lr.split_store(lds + 3 * PA, t);
+        lq.split_store(lds + 3 * PA + 3 * PB, t);
     };
     load(0);
     store();
@@ -1695,8 +1671,8 @@ static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, co
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
         const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
         Prod6Args g{};
-        g.a = Op6{M, G, n, 0, (int)m, (int)n, va};               // A(i,k) = B[i][k]  (k contiguous)
-        g.b = Op6{Q, nullptr, r, 0, (int)r, (int)n, false};      // B(k,j) = Q[k][j]  (j contiguous)
+        g.a = Op6{M, G, n, (int)m, (int)n, va};               // A(i,k) = B[i][k]  (k contiguous)
+        g.b = Op6{Q, nullptr, r, (int)r, (int)n, false};      // B(k,j) = Q[k][j]  (j contiguous)
         g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = n * r * 4;
         g.c = (float*)P; g.ldc = r; g.sc = m * r;
         g.M = (int)m; g.N = (int)r; g.K = (int)n;
@@ -1725,8 +1701,8 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
     const int64_t m = p.m, n = p.n, r = p.r;
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
         Prod6Args g{};
-        g.a = Op6{M, G, n, 0, (int)n, (int)m, false};            // A(i,k) = B[k][i]  (i contiguous)
-        g.b = Op6{P, nullptr, r, 0, (int)r, (int)m, false};      // B(k,j) = P[k][j]  (j contiguous)
+        g.a = Op6{M, G, n, (int)n, (int)m, false};            // A(i,k) = B[k][i]  (i contiguous)
+        g.b = Op6{P, nullptr, r, (int)r, (int)m, false};      // B(k,j) = P[k][j]  (j contiguous)
         g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = m * r * 4;
         g.c = (float*)R; g.ldc = r; g.sc = n * r;
         g.M = (int)n; g.N = (int)r; g.K = (int)m;
@@ -1806,14 +1782,15 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
 }
 
 template <bool GB, bool XB>
-static hipError_t launch_update(const Plan& p, const char* ws, float* M, const void* G, void* X, float mu,
-                                float lr, hipStream_t s) {
+static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, float* M, const void* G, void* X,
+                                float mu, float lr, hipStream_t s) {
     UpdArgs u{};
-    u.Pp = (const uint16_t*)(ws + p.Pp);
-    u.Rp = (const uint16_t*)(ws + p.Rp);
-    u.Qp = (const uint16_t*)(ws + p.Qp);
+    u.P = (const float*)(ws + p.P32);
+    u.R = (const float*)(ws + p.R32);
+    u.Q = Q;
     u.M = M; u.G = G; u.X = X;
-    u.m = (int)p.m; u.n = (int)p.n; u.kp = (int)p.kp;
+    u.m = (int)p.m; u.n = (int)p.n; u.r = (int)p.r; u.kp = (int)p.kp;
+    u.vec = (p.r % 4) == 0;
     u.one_minus_mu = 1.0f - mu;
     u.lr_s = (float)((double)lr * sqrt((double)p.m / (double)p.n));
     // 128 x 64 tiles while they still fill the chip, else 64 x 64
@@ -1880,22 +1857,21 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
         hipLaunchKernelGGL(colscale_kernel, g2, dim3(256), 0, s, (const double*)(ws + p.part), (double*)(ws + p.cs),
                            p.r, (int)p.nchunk, (double)eps);
         DION_TRY(hipGetLastError());
-        dim3 g3(grid_1d(p.n * p.kp / 4, 1024), (unsigned)p.b);
+        dim3 g3(grid_1d(p.n * ((p.r + 3) / 4), 1024), (unsigned)p.b);
         hipLaunchKernelGGL(next_q_kernel, g3, dim3(256), 0, s, (const double*)(ws + p.R64), (float*)(ws + p.R32),
-                           (const double*)(ws + p.cs), Q, (uint16_t*)(ws + p.Rp), (uint16_t*)(ws + p.Qp), p.n, p.r,
-                           p.kp, c.st);
+                           (const double*)(ws + p.cs), Q, p.n, p.r, c.st);
         DION_TRY(hipGetLastError());
-        dim3 g4(grid_1d(p.m * p.kp / 4, 1024), (unsigned)p.b);
-        hipLaunchKernelGGL(split_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
-                           (uint16_t*)(ws + p.Pp), p.m, p.r, p.kp, c.st);
+        dim3 g4(grid_1d(p.m * ((p.r + 3) / 4), 1024), (unsigned)p.b);
+        hipLaunchKernelGGL(round_p_kernel, g4, dim3(256), 0, s, (const double*)(ws + p.P64), (float*)(ws + p.P32),
+                           p.m, p.r, c.st);
         DION_TRY(hipGetLastError());
     }
     DION_TRY(mark(DION_PHASE_UPDATE));
     hipError_t he;
-    if (g_bf16) he = x_bf16 ? launch_update<true, true>(p, ws, M, G, X, mu, lr, s)
-                            : launch_update<true, false>(p, ws, M, G, X, mu, lr, s);
-    else he = x_bf16 ? launch_update<false, true>(p, ws, M, G, X, mu, lr, s)
-                     : launch_update<false, false>(p, ws, M, G, X, mu, lr, s);
+    if (g_bf16) he = x_bf16 ? launch_update<true, true>(p, ws, Q, M, G, X, mu, lr, s)
+                            : launch_update<true, false>(p, ws, Q, M, G, X, mu, lr, s);
+    else he = x_bf16 ? launch_update<false, true>(p, ws, Q, M, G, X, mu, lr, s)
+                     : launch_update<false, false>(p, ws, Q, M, G, X, mu, lr, s);
     DION_TRY(he);
     DION_TRY(mark(DION_PHASE_FLAGS));
     if (flags) {
