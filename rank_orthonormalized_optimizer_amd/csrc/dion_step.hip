@@ -294,9 +294,10 @@ struct PanelCol {
             a[K] = l;
             dgv[K] = lkk;
             rdv[K] = r;
-            T dn = T(1), rn = T(1);
+            T dn = T(1), rn = T(1), ln = T(0);
             if constexpr (K + 1 < kSB) {   // next pivot from lane K + 1 alone
-                const T ln = read_lane<T>(l, K + 1), an = read_lane<T>(a[K + 1], K + 1);
+                ln = read_lane<T>(l, K + 1);
+                const T an = read_lane<T>(a[K + 1], K + 1);
                 dn = __builtin_fma(-ln, ln, an);
                 rn = rsqrt_newton<T>(dn);
             }
@@ -305,8 +306,11 @@ struct PanelCol {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // column K + 1, which the next step scales, takes lane K + 1's value from the
+            // v_readlane above rather than from LDS, so no LDS round trip is on the pivot chain
+            if constexpr (K + 1 < kSB) a[K + 1] = __builtin_fma(-l, ln, a[K + 1]);
 #pragma unroll
-            for (int j = K + 1; j < kSB; ++j) a[j] = __builtin_fma(-l, c[j], a[j]);
+            for (int j = K + 2; j < kSB; ++j) a[j] = __builtin_fma(-l, c[j], a[j]);
             PanelCol<T, K + 1>::run(a, dn, rn, lane, col, dgv, rdv, bad);
         }
     }
@@ -435,11 +439,19 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
     const int tid = threadIdx.x, nbj = p.nbj;
     const T* S = (const T*)p.S + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
     T* L = (T*)p.L + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
-    for (int idx = tid; idx < kNB * kNB; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        T v = (i == j) ? T(1) : T(0);
-        if (i < nbj && j <= i) v = S[(int64_t)i * p.ldl + j];
-        sm.a[i * kDLD + j] = v;
+    {   // all sixteen loads of a thread in flight at once (addresses clamped, values selected)
+        T v[kNB * kNB / 256];
+        const int64_t o0 = (int64_t)(tid >> 6) * p.ldl + (tid & 63), step = 4 * p.ldl;   // row tid / 64 + 4 q
+#pragma unroll
+        for (int q = 0; q < kNB * kNB / 256; ++q) {
+            const int idx = tid + 256 * q, i = idx >> 6, j = idx & 63;
+            v[q] = S[(i < nbj && j <= i) ? o0 + q * step : 0];
+        }
+#pragma unroll
+        for (int q = 0; q < kNB * kNB / 256; ++q) {
+            const int idx = tid + 256 * q, i = idx >> 6, j = idx & 63;
+            sm.a[i * kDLD + j] = (i < nbj && j <= i) ? v[q] : (i == j ? T(1) : T(0));
+        }
     }
     __syncthreads();
     if (!chol_inv64<T>(sm)) {
@@ -459,8 +471,9 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
     }
     T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * p.blkTd;
-    for (int idx = tid; idx < kNB * kNB; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
+#pragma unroll
+    for (int q = 0; q < kNB * kNB / 256; ++q) {
+        const int idx = tid + 256 * q, i = idx >> 6, j = idx & 63;
         const bool in = i < nbj && j < nbj;
         if (in && j <= i) L[(int64_t)i * p.ldl + j] = sm.a[i * kDLD + j];
         if (in || p.tdfull) Td[i * p.ldTd + j] = (in && j <= i) ? sm.x[i * kDLD + j] : T(0);
