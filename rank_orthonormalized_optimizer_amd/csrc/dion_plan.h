@@ -27,7 +27,8 @@ struct Plan {
     int64_t m, n, b, r;
     int64_t nblk;      // number of rank column blocks
     int64_t nchunk;    // row chunks of the column-norm reduction
-    int64_t gsplit;    // K-splits of the Gram products (partials reduced in fixed order)
+    int64_t gsplit;    // K-splits of the fp64 Gram products (partials reduced in fixed order)
+    int64_t gsplit6;   // K-splits of the fp32 Gram products (split-bf16 kernel, 128 x 128 tiles)
     int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
     // byte offsets into the workspace (all 256-byte aligned)
     size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart;
@@ -76,6 +77,21 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
         }
         q.gsplit = tiles > 0 ? best : 1;
     }
+    {   // the same model for the fp32 Gram on the split-bf16 kernel: one 128 x 128 workgroup per
+        // CU, 32-k slabs, >= 256 rows per split
+        const int64_t nt = (r + 127) / 128;
+        const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
+        const int64_t slots = 256, slabs = (m + 31) / 32;
+        int64_t best = 1;
+        double best_cost = 0.0;
+        for (int64_t s = 1; s <= 16; ++s) {
+            if (s > 1 && (s > m / 256 || (double)(b > 0 ? b : 1) * s * r * r * 4 > 512.0 * (1 << 20))) break;
+            const double rounds = (double)((s * tiles + slots - 1) / slots);
+            const double cost = rounds * (double)((slabs + s - 1) / s + 3);
+            if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
+        }
+        q.gsplit6 = tiles > 0 ? best : 1;
+    }
     size_t off = 0;
     auto take = [&](double bytes) { size_t o = off; off = align256(off + (size_t)bytes); return o; };
     const double B = (double)b;
@@ -93,13 +109,16 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.P64b = take(B * m * r * 8);          // second P buffer (fp64 chain; fp32 chain's scratch)
     q.R64 = take(B * n * r * 8);           // fp64 chain R
     q.part = take(B * q.nchunk * r * 8);   // column-norm partial sums (fp64)
-    q.gpart = take(q.gsplit > 1 ? B * q.gsplit * r * r * 8 : 0);   // Gram partials
+    const double gp64 = q.gsplit > 1 ? (double)q.gsplit * r * r * 8 : 0.0;
+    const double gp32 = q.gsplit6 > 1 ? (double)q.gsplit6 * r * r * 4 : 0.0;
+    const double gpm = gp64 > gp32 ? gp64 : gp32;
+    q.gpart = take(B * gpm);               // Gram partials (either chain)
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
     q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = kNearIdParts * 8;
     q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
-    q.sgpart = q.gsplit > 1 ? (size_t)(q.gsplit * r * r * 8) : 0;
+    q.sgpart = (size_t)gpm;
     *p = q;
     return true;
 }

@@ -185,6 +185,9 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, int64_t batch, hipStream_t
 #define DION_BIG_MIN_TILES 256
 #endif
 constexpr int kBigTileMinTiles = DION_BIG_MIN_TILES;
+#ifndef DION_PROD6
+#define DION_PROD6 1
+#endif
 #ifndef DION_UPD_BIG_MIN_TILES
 #define DION_UPD_BIG_MIN_TILES 256
 #endif
@@ -477,6 +480,10 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         const bool in = i < nbj && j < nbj;
         if (in && j <= i) L[(int64_t)i * p.ldl + j] = sm.a[i * kDLD + j];
         if (in || p.tdfull) Td[i * p.ldTd + j] = (in && j <= i) ? sm.x[i * kDLD + j] : T(0);
+    }
+    if (!p.tdfull) {   // Td lies in L^-1: zero the rest of its block row, which 128-wide apply tiles read
+        const int rest = (int)(p.ldTd - p.j0) - kNB;
+        for (int idx = tid; idx < nbj * rest; idx += 256) Td[(int64_t)(idx / rest) * p.ldTd + kNB + idx % rest] = T(0);
     }
     return true;
 }
@@ -1017,34 +1024,46 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const T* part, T* W, i
 
 // W = P^T P; a split Gram leaves its partials in gpart and, unless `reduce` is false (the
 // caller then sums them itself), adds them into W.
+// fp32-chain Gram and apply on the split-bf16 kernel (defined with it below)
+static int gram6(const ChainCtx& c, const float* P, int mask, int val, int64_t splits, int64_t kc);
+static int apply6(const ChainCtx& c, const float* Pin, float* Pout, int mask, int val);
+template <typename T>
+static int64_t gram_splits(const Plan& p) { return (sizeof(T) == 4 && DION_PROD6) ? p.gsplit6 : p.gsplit; }
+
 template <typename T>
 static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = true) {
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
-    const int64_t splits = p.gsplit, kc = (m + splits - 1) / splits;
-    GemmArgs g{};
-    g.a = Operand{P, nullptr, r, (int)r, (int)m, vr};   // A(i,k) = P[k][i]
-    g.b = Operand{P, nullptr, r, (int)r, (int)m, vr};   // B(k,j) = P[k][j]
-    g.sa0 = g.sb0 = m * r * (int64_t)sizeof(T);
-    g.M = g.N = (int)r;
-    g.alpha = 1; g.beta = 0;
-    g.st = c.st; g.st_mask = mask; g.st_val = val; g.lower = 1;
-    if (splits <= 1) {
-        g.c = c.ws + p.W; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
-        g.K = (int)m;
+    const int64_t splits = gram_splits<T>(p), kc = (m + splits - 1) / splits;
+    if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        int e;
+        if ((e = gram6(c, P, mask, val, splits, kc))) return e;
+        if (splits <= 1) return 0;
+    } else {
+        GemmArgs g{};
+        g.a = Operand{P, nullptr, r, (int)r, (int)m, vr};   // A(i,k) = P[k][i]
+        g.b = Operand{P, nullptr, r, (int)r, (int)m, vr};   // B(k,j) = P[k][j]
+        g.sa0 = g.sb0 = m * r * (int64_t)sizeof(T);
+        g.M = g.N = (int)r;
+        g.alpha = 1; g.beta = 0;
+        g.st = c.st; g.st_mask = mask; g.st_val = val; g.lower = 1;
+        if (splits <= 1) {
+            g.c = c.ws + p.W; g.ldc = r; g.sc = r * r * (int64_t)sizeof(T);
+            g.K = (int)m;
+            DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
+            return 0;
+        }
+        g.K = (int)kc;
+        g.zdiv = (int)splits;
+        g.ksplit_total = (int)m;
+        g.ga0 = g.gb0 = kc * r * (int64_t)sizeof(T);
+        g.c = c.ws + p.gpart; g.ldc = r;
+        g.sc = splits * r * r * (int64_t)sizeof(T);
+        g.gc = r * r * (int64_t)sizeof(T);
         DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
-        return 0;
     }
-    g.K = (int)kc;
-    g.zdiv = (int)splits;
-    g.ksplit_total = (int)m;
-    g.ga0 = g.gb0 = kc * r * (int64_t)sizeof(T);
-    g.c = c.ws + p.gpart; g.ldc = r;
-    g.sc = splits * r * r * (int64_t)sizeof(T);
-    g.gc = r * r * (int64_t)sizeof(T);
-    DION_TRY((launch_gemm<T, 64, 64, false, S, false, S>(g, p.b, c.s)));
     if (!reduce) return 0;
     dim3 grid(grid_1d(r * r, 512), (unsigned)p.b);
     hipLaunchKernelGGL((gram_reduce_kernel<T>), grid, dim3(256), 0, c.s, (const T*)(c.ws + p.gpart), (T*)(c.ws + p.W),
@@ -1369,6 +1388,7 @@ static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int f
 // Pout = Pin Tf^T = Pin L^-T  (Tf lower: output column tile n0 needs only k < n0 + BN)
 template <typename T>
 static int apply(const ChainCtx& c, const T* Pin, T* Pout, int mask, int val) {
+    if constexpr (sizeof(T) == 4 && DION_PROD6) return apply6(c, Pin, Pout, mask, val);
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     constexpr int S = SrcOf<T>::v;
@@ -1474,8 +1494,9 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
         const int64_t per = std::min<int64_t>(kNearIdParts, std::max<int64_t>(16, (2048 + b - 1) / b));
         const unsigned nparts = grid_1d(r * r, per);
         dim3 grid(nparts, (unsigned)b);
-        const T* gp = p.gsplit > 1 ? (const T*)(c.ws + p.gpart) : nullptr;
-        hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, p.gsplit, W, (T*)(c.ws + p.Tf),
+        const int64_t splits = gram_splits<T>(p);
+        const T* gp = splits > 1 ? (const T*)(c.ws + p.gpart) : nullptr;
+        hipLaunchKernelGGL((near_id_setup_kernel<T>), grid, dim3(256), 0, c.s, gp, splits, W, (T*)(c.ws + p.Tf),
                            part, r, (const int*)c.st, mask, val);
         DION_TRY(hipGetLastError());
         if (p.nblk <= kFusedMaxBlocks) {
@@ -1499,9 +1520,6 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
 // four multiplying waves of 64 x 64 (so each LDS fragment feeds four MFMA blocks) and four
 // staging waves, triple-buffered part tiles in 144 KB of LDS: one workgroup per CU.
 // ---------------------------------------------------------------------------
-#ifndef DION_PROD6
-#define DION_PROD6 1
-#endif
 struct Prod6Args {
     Op6 a, b;
     int64_t sa0, sa1, sb0;       // batch strides in bytes of a.p0, a.p1, b.p0
@@ -1510,6 +1528,13 @@ struct Prod6Args {
     int M, N, K;
     const int* st;
     int st_mask, st_val;
+    // split K (no addend): grid z = matrix * splits + split; split s covers k in
+    // [s kc, min(K, (s + 1) kc)), its operands start ska / skb bytes further and its output
+    // slice scs elements further
+    int splits;
+    int64_t kc, ska, skb, scs;
+    bool lower;                  // square output: tiles entirely above the diagonal are skipped
+    bool tri;                    // B(k, j) = 0 for k > j: output column tile n0 stops at k = n0 + 128
 };
 
 // Staging side of prod6_kernel: three register sets of raw operand values and three LDS buffers,
@@ -1563,8 +1588,9 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     using St = Stage6<AK, AADD, BK6>;
     constexpr int BT = St::BT, PT = St::PT;
     const TileId tid = xcd_tile_id();
-    const int bz = tid.z;
+    const int sp = g.splits > 1 ? g.splits : 1, bz = tid.z / sp, ks = tid.z % sp;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
+    if (g.lower && tid.x > tid.y) return;
     const int m0 = tid.y * BT, n0 = tid.x * BT;
     __shared__ __attribute__((aligned(16))) uint16_t lds[3][6 * PT];   // A h m l | B h m l
     const int wave = threadIdx.x >> 6;
@@ -1574,7 +1600,15 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
     A.p0 = (const char*)A.p0 + bz * g.sa0;
     if (A.p1) A.p1 = (const char*)A.p1 + bz * g.sa1;
     B.p0 = (const char*)B.p0 + bz * g.sb0;
-    const int K = g.K;
+    int K = g.K;
+    if (sp > 1) {
+        A.p0 = (const char*)A.p0 + ks * g.ska;
+        B.p0 = (const char*)B.p0 + ks * g.skb;
+        K = (int)(g.kc < (int64_t)g.K - ks * g.kc ? g.kc : (int64_t)g.K - ks * g.kc);
+        A.kext = K;
+        B.kext = K;
+    }
+    if (g.tri && n0 + BT < K) K = n0 + BT;
     // slab s is multiplied from LDS buffer s % 3 while the staging waves write slab s + 2 to
     // buffer (s + 2) % 3 and issue the loads of slab s + 5.  The two roles run separate loops
     // with the same barriers, so their registers (raw slabs, accumulators) never overlap.
@@ -1644,7 +1678,7 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
         __syncthreads();
         buf = buf == 2 ? 0 : buf + 1;
     }
-    float* C = g.c + bz * g.sc;
+    float* C = g.c + bz * g.sc + ks * g.scs;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1664,8 +1698,10 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
     // k-contiguous operands (the operand extents are the output extents and K)
     // (the back-projection's x-contiguous summed operand is not taken: its hoisted row addresses
     // for three register sets overflow the register file)
-    const bool fast = AK == S6_KC && g.a.vec && g.M % 128 == 0 && g.N % 128 == 0 && g.K % kSplitK == 0 &&
-                      g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K && g.b.xext == g.N && g.b.kext == g.K;
+    // (with a triangular B every tile's K is still a whole number of slabs, at least four)
+    const bool fast = AK == S6_KC && g.a.vec && (BK6 != S6_KC || g.b.vec) && g.M % 128 == 0 && g.N % 128 == 0 &&
+                      g.K % kSplitK == 0 && g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K &&
+                      g.b.xext == g.N && g.b.kext == g.K && g.splits <= 1;
     if constexpr (AK == S6_KC) {
         if (fast) {
             hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true>), grid, dim3(512), 0, s, g);
@@ -1674,6 +1710,47 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
     }
     hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false>), grid, dim3(512), 0, s, g);
     return hipGetLastError();
+}
+
+// W = P^T P (lower 128 x 128 tiles) for the fp32 chain; with splits > 1 the split partials go
+// to the Gram partial buffer (summed in split order by the consumer).
+static int gram6(const ChainCtx& c, const float* P, int mask, int val, int64_t splits, int64_t kc) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r;
+    Prod6Args g{};
+    g.a = Op6{P, nullptr, r, (int)r, (int)m, false};   // A(i,k) = P[k][i]  (i contiguous)
+    g.b = Op6{P, nullptr, r, (int)r, (int)m, false};   // B(k,j) = P[k][j]  (j contiguous)
+    g.sa0 = g.sb0 = m * r * 4;
+    g.M = g.N = (int)r; g.K = (int)m;
+    g.lower = true;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    if (splits <= 1) {
+        g.c = (float*)(c.ws + p.W); g.ldc = r; g.sc = r * r;
+        DION_TRY((launch_prod6<S6_XC, A6_NONE, S6_XC>(g, p.b, c.s)));
+        return 0;
+    }
+    g.splits = (int)splits; g.kc = kc;
+    g.ska = g.skb = kc * r * 4;
+    g.c = (float*)(c.ws + p.gpart); g.ldc = r; g.sc = splits * r * r; g.scs = r * r;
+    DION_TRY((launch_prod6<S6_XC, A6_NONE, S6_XC>(g, p.b * splits, c.s)));
+    return 0;
+}
+
+// Pout = Pin Tf^T for the fp32 chain (Tf lower: column tile n0 needs k < n0 + 128 only).
+static int apply6(const ChainCtx& c, const float* Pin, float* Pout, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r;
+    const bool vr = (r % 4) == 0;
+    Prod6Args g{};
+    g.a = Op6{Pin, nullptr, r, (int)m, (int)r, vr};                    // A(i,k) = Pin[i][k]
+    g.b = Op6{c.ws + p.Tf, nullptr, r, (int)r, (int)r, vr};            // B(k,j) = Tf[j][k]
+    g.sa0 = m * r * 4; g.sb0 = r * r * 4;
+    g.c = Pout; g.ldc = r; g.sc = m * r;
+    g.M = (int)m; g.N = (int)r; g.K = (int)r;
+    g.tri = true;
+    g.st = c.st; g.st_mask = mask; g.st_val = val;
+    DION_TRY((launch_prod6<S6_KC, A6_NONE, S6_KC>(g, p.b, c.s)));
+    return 0;
 }
 
 // P0 = (M + G) Q  and  R = (M + G)^T P for one chain.

@@ -189,6 +189,21 @@ def test_split_product_launch_kinds(cuda, m, n):
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
 
+@pytest.mark.parametrize("batch,m,n,r", [(4, 1000, 300, 200), (2, 2048, 512, 256), (3, 640, 384, 128)])
+def test_fp32_chain_gram_splits(cuda, batch, m, n, r):
+    """fp32-chain Gram and apply on the split-bf16 kernel.  The Gram's K = m is cut into
+    partials summed in split order: m = 1000, r = 200 gives three splits (334, 334, 332 rows)
+    over ragged 128-tiles; m = 2048, r = 256 eight splits, and its apply has whole tiles (the
+    branch-free staging loop, with the triangular K limit per column tile); m = 640, r = 128
+    two splits.  Every matrix must stay on the fp32 chain."""
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.SMALL[1].with_groups(W.Group(batch, m, n, r), name=f"gram6-{batch}x{m}x{n}-r{r}", steps=2)
+    rep = run_teacher_forced(wl, cuda)
+    for _, _, _, flags in rep:
+        assert not np.any(flags & dion.FLAG_F64), flags
+    check(rep, tol_for(wl))
+
+
 @pytest.mark.parametrize("force64", [False, True])
 def test_shifted_first_pass(cuda, force64):
     """8 decades of spectrum: the fp64 chain's plain Cholesky of P0^T P0 breaks down (host fp64
