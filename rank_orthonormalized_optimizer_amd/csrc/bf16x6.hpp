@@ -67,6 +67,7 @@ enum Src6 : int {
     S6_KC8 = 0,      // fp32 p0[x * ld + k], k contiguous, staged in chunks of eight k
     S6_KC = 1,       // fp32 p0[x * ld + k] (+ addend p1 at the same index), k contiguous
     S6_XC = 2,       // fp32 p0[k * ld + x] (+ addend p1 at the same index), x contiguous
+    S6_XC4 = 4,      // the same layout, staged as 16-byte row vectors (four x by four k per thread)
 };
 enum Add6 : int { A6_NONE = 0, A6_F32 = 1, A6_BF16 = 2 };
 
@@ -318,6 +319,68 @@ struct Loader6<BX, S6_XC, ADD> {
                 else v[e] = sum6<ADD>(a[4 * g + e], b[4 * g + e]);
             }
             store4(lds, BX * kSplitK, x, kb + 4 * g, split4(v));
+        }
+    }
+};
+
+// x-contiguous fp32 (+ addend), 16-byte rows: each thread owns four consecutive x and four consecutive k
+// (32 x 8 threads over the 128 x 32 tile), read as one 16-byte vector (8 bytes for a bf16
+// addend) per k row when the rows allow it (op.vec: ld, x0 and the bases 4-element aligned);
+// the split then writes each x's four k as one 8-byte chunk per part.
+template <int BX, int ADD>
+struct Loader6<BX, S6_XC4, ADD> {
+    static_assert(BX == 128, "32 x 8 threads of 4 x 4 values");
+    using AT = typename Add6T<ADD>::t;
+    float a[16];                          // [k][x]: a[4 k + x]
+    AT b[ADD == A6_NONE ? 1 : 16];
+    static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
+        return op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
+    }
+    // interior tile with vector-legal rows: no bounds tests
+    __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
+        const int64_t o = (int64_t)(k0 + 4 * (t >> 5)) * op.ld + x0 + 4 * (t & 31);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 v = *(const float4*)((const float*)op.p0 + o + e * op.ld);
+            a[4 * e + 0] = v.x; a[4 * e + 1] = v.y; a[4 * e + 2] = v.z; a[4 * e + 3] = v.w;
+            if constexpr (ADD == A6_F32) {
+                const float4 w = *(const float4*)((const float*)op.p1 + o + e * op.ld);
+                b[4 * e + 0] = w.x; b[4 * e + 1] = w.y; b[4 * e + 2] = w.z; b[4 * e + 3] = w.w;
+            } else if constexpr (ADD == A6_BF16) {
+                const uint2 w = *(const uint2*)((const uint16_t*)op.p1 + o + e * op.ld);
+                b[4 * e + 0] = (uint16_t)w.x; b[4 * e + 1] = (uint16_t)(w.x >> 16);
+                b[4 * e + 2] = (uint16_t)w.y; b[4 * e + 3] = (uint16_t)(w.y >> 16);
+            }
+        }
+    }
+    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
+        if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
+        // element loads from clamped addresses (element 0 is always valid), values selected
+        const int x = x0 + 4 * (t & 31), k = k0 + 4 * (t >> 5);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int e = q >> 2, i = q & 3;
+            const bool in = x + i < op.xext && k + e < op.kext;
+            const int64_t o = in ? (int64_t)(k + e) * op.ld + x + i : 0;
+            const float va = ((const float*)op.p0)[o];
+            a[4 * e + i] = in ? va : 0.f;
+            if constexpr (ADD != A6_NONE) {
+                const AT vb = ((const AT*)op.p1)[o];
+                b[4 * e + i] = in ? vb : AT(0);
+            }
+        }
+    }
+    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
+        const int xl = 4 * (t & 31), kl = 4 * (t >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ADD == A6_NONE) v[e] = a[4 * e + i];
+                else v[e] = sum6<ADD>(a[4 * e + i], b[4 * e + i]);
+            }
+            store4(lds, BX * kSplitK, xl + i, kl, split4(v));
         }
     }
 };

@@ -1699,7 +1699,7 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
     // (the back-projection's x-contiguous summed operand is not taken: its hoisted row addresses
     // for three register sets overflow the register file)
     // (with a triangular B every tile's K is still a whole number of slabs, at least four)
-    const bool fast = AK == S6_KC && g.a.vec && (BK6 != S6_KC || g.b.vec) && g.M % 128 == 0 && g.N % 128 == 0 &&
+    const bool fast = AK == S6_KC && g.a.vec && g.b.vec && g.M % 128 == 0 && g.N % 128 == 0 &&
                       g.K % kSplitK == 0 && g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K &&
                       g.b.xext == g.N && g.b.kext == g.K && g.splits <= 1;
     if constexpr (AK == S6_KC) {
@@ -1718,8 +1718,8 @@ static int gram6(const ChainCtx& c, const float* P, int mask, int val, int64_t s
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     Prod6Args g{};
-    g.a = Op6{P, nullptr, r, (int)r, (int)m, false};   // A(i,k) = P[k][i]  (i contiguous)
-    g.b = Op6{P, nullptr, r, (int)r, (int)m, false};   // B(k,j) = P[k][j]  (j contiguous)
+    g.a = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // A(i,k) = P[k][i]  (i contiguous)
+    g.b = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // B(k,j) = P[k][j]  (j contiguous)
     g.sa0 = g.sb0 = m * r * 4;
     g.M = g.N = (int)r; g.K = (int)m;
     g.lower = true;
@@ -1762,13 +1762,13 @@ static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, co
         const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
         Prod6Args g{};
         g.a = Op6{M, G, n, (int)m, (int)n, va};               // A(i,k) = B[i][k]  (k contiguous)
-        g.b = Op6{Q, nullptr, r, (int)r, (int)n, false};      // B(k,j) = Q[k][j]  (j contiguous)
+        g.b = Op6{Q, nullptr, r, (int)r, (int)n, r % 4 == 0};   // B(k,j) = Q[k][j]  (j contiguous)
         g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = n * r * 4;
         g.c = (float*)P; g.ldc = r; g.sc = m * r;
         g.M = (int)m; g.N = (int)r; g.K = (int)n;
         g.st = c.st; g.st_mask = mask; g.st_val = val;
-        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC>(g, p.b, c.s)
-                                                   : launch_prod6<S6_KC, A6_F32, S6_XC>(g, p.b, c.s);
+        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC4>(g, p.b, c.s)
+                                                   : launch_prod6<S6_KC, A6_F32, S6_XC4>(g, p.b, c.s);
         DION_TRY(he);
         return 0;
     }
@@ -1790,9 +1790,10 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
     const Plan& p = *c.p;
     const int64_t m = p.m, n = p.n, r = p.r;
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
         Prod6Args g{};
-        g.a = Op6{M, G, n, (int)n, (int)m, false};            // A(i,k) = B[k][i]  (i contiguous)
-        g.b = Op6{P, nullptr, r, (int)r, (int)m, false};      // B(k,j) = P[k][j]  (j contiguous)
+        g.a = Op6{M, G, n, (int)n, (int)m, va};               // A(i,k) = B[k][i]  (i contiguous)
+        g.b = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // B(k,j) = P[k][j]  (j contiguous)
         g.sa0 = m * n * 4; g.sa1 = m * n * gsz; g.sb0 = m * r * 4;
         g.c = (float*)R; g.ldc = r; g.sc = n * r;
         g.M = (int)n; g.N = (int)r; g.K = (int)m;
