@@ -1072,8 +1072,26 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = 
     return 0;
 }
 
+// arguments of panel_inv_kernel (defined with the tile device GEMM below)
+struct PanelInvArgs {
+    const void* S; void* L; void* Tf;
+    void* Y;            // scratch, [b][nblk][64][64]: the partial products of the inverse tiles
+    int64_t r;
+    int jb, nblk;
+    const int* st;
+    int st_mask, st_val;
+};
+
 template <typename T>
-static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift) {
+__global__ __launch_bounds__(256) void panel_inv_kernel(PanelInvArgs a);
+
+// Blocked right-looking Cholesky L = chol(W (+ s I)).  With `with_inverse` (ranks up to
+// kFusedMaxBlocks blocks) the panel launches also build Tf = L^-1 (panel_inv_kernel); a matrix
+// that tau_bit marks at the last diagonal block skips the last inverse tiles (a later shifted
+// call refactors it).
+template <typename T>
+static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
+                  bool with_inverse) {
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r, b = p.b;
     T* W = (T*)(c.ws + p.W);
@@ -1107,6 +1125,15 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         pa.tau = tau; pa.fail_bit = fail_bit; pa.tau_bit = tau_bit;
         hipLaunchKernelGGL((potrf_diag_kernel<T>), dim3((unsigned)b), dim3(256), 0, c.s, pa);
         DION_TRY(hipGetLastError());
+        if (with_inverse && p.nblk > 1) {
+            PanelInvArgs pi{};
+            pi.S = src; pi.L = L; pi.Tf = Tf; pi.Y = c.ws + p.Td;
+            pi.r = r; pi.jb = (int)jb; pi.nblk = (int)p.nblk;
+            pi.st = c.st; pi.st_mask = jb == p.nblk - 1 ? (mask | tau_bit) : mask; pi.st_val = val;
+            hipLaunchKernelGGL((panel_inv_kernel<T>), dim3((unsigned)(p.nblk - 1), (unsigned)b), dim3(256), 0, c.s,
+                               pi);
+            DION_TRY(hipGetLastError());
+        }
         if (rest > 0) {
             const int64_t ob = (int64_t)(j0 + nbj) * r + j0, ot = (int64_t)(j0 + nbj) * (r + 1);
             T* below = L + ob;
@@ -1120,7 +1147,7 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
             g.M = rest; g.N = nbj; g.K = nbj;
             g.alpha = 1; g.beta = 0;
             g.st = c.st; g.st_mask = mask; g.st_val = val;
-            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+            if (!with_inverse) DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
             // trailing: L22 <- L22 - L21 L21^T (lower tiles only)
             GemmArgs h = g;
             h.a = Operand{below, nullptr, r, rest, nbj, vr};
@@ -1207,6 +1234,45 @@ __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int 
                 if (row < M && col < N) Cp[(int64_t)row * ldc + col] = alpha * acc[i][j][v] + beta * sv[i][j][v];
             }
     __syncthreads();
+}
+
+// Off-diagonal tiles of step jb of the right-looking factorization, with L^-1 built alongside
+// (ranks up to kFusedMaxBlocks blocks; grid: nblk - 1 tiles x matrices):
+//   below the diagonal block (ib > jb):  L_ib,jb = S_ib,jb Td_jb^T   (S: the updated block)
+//   left of it in L^-1 (kb < jb):        X_jb,kb = -Td_jb (sum_{kb<=q<jb} L_jb,q X_q,kb)
+// The inverse tiles need only blocks finished at earlier steps, so they ride along with the
+// panel; the last step is a launch of inverse tiles only.  No separate inversion launches.
+template <typename T>
+__global__ __launch_bounds__(256) void panel_inv_kernel(PanelInvArgs a) {
+    const int bz = blockIdx.y, t = blockIdx.x;
+    if ((a.st[bz] & a.st_mask) != a.st_val) return;
+    using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
+    __shared__ T As[2 * C::A_STAGE];
+    __shared__ T Bs[2 * C::B_STAGE];
+    const int64_t r = a.r, rr = r * r;
+    const T* S = (const T*)a.S + bz * rr;
+    T* L = (T*)a.L + bz * rr;
+    T* Tf = (T*)a.Tf + bz * rr;
+    const bool vr = (r % 4) == 0;
+    auto nb = [&](int q) { return (int)((r - (int64_t)q * kNB) < kNB ? (r - (int64_t)q * kNB) : kNB); };
+    const int jb = a.jb, j0 = jb * kNB, nbj = nb(jb), nL = a.nblk - 1 - jb;
+    const Operand Td{Tf + (int64_t)j0 * (r + 1), nullptr, r, nbj, nbj, vr};   // Td(i,k) = X_jb,jb[i][k]
+    if (t < nL) {
+        // one tile holds all nbj columns, so in place (S == L once shifted) is safe
+        const int64_t i0 = (int64_t)(jb + 1 + t) * kNB;
+        const int nbi = nb(jb + 1 + t);
+        tile_gemm<T, true>(Operand{S + i0 * r + j0, nullptr, r, nbi, nbj, vr}, Td, nbi, nbj, nbj, L + i0 * r + j0, r,
+                           T(1), T(0), As, Bs);
+    } else {
+        const int kb = t - nL, k0 = kb * kNB, nbk = nb(kb), K = j0 - k0;
+        T* Y = (T*)a.Y + ((int64_t)bz * a.nblk + kb) * kNB * kNB;
+        // Y = L_jb,[kb,jb) X_[kb,jb),kb  (nbj x nbk, ld 64); X_jb,kb = -Td Y
+        const Operand A{L + (int64_t)j0 * r + k0, nullptr, r, nbj, K, vr};
+        const Operand B{Tf + (int64_t)k0 * r + k0, nullptr, r, nbk, K, vr};
+        tile_gemm<T, false>(A, B, nbj, nbk, K, Y, kNB, T(1), T(0), As, Bs);
+        const Operand B2{Y, nullptr, kNB, nbk, nbj, true};
+        tile_gemm<T, false>(Td, B2, nbj, nbk, nbj, Tf + (int64_t)j0 * r + k0, r, T(-1), T(0), As, Bs);
+    }
 }
 
 template <typename T>
@@ -1368,7 +1434,9 @@ static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int f
     const Plan& p = *c.p;
     if (!rare || p.nblk > kFusedMaxBlocks) {
         int e;
-        if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, shift))) return e;
+        const bool inv = p.nblk <= kFusedMaxBlocks;   // L^-1 built by the panel launches
+        if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, shift, inv))) return e;
+        if (inv) return 0;
         // a matrix marked by tau_bit here is refactored (shifted) by a later call, which inverts
         return invert<T>(c, tau_bit ? (mask | tau_bit) : mask, val);
     }
