@@ -1763,14 +1763,14 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
     dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128), (unsigned)batch);
     // every tile interior: whole 128-tiles along both output edges, whole slabs, vector-legal
-    // k-contiguous operands (the operand extents are the output extents and K)
-    // (the back-projection's x-contiguous summed operand is not taken: its hoisted row addresses
-    // for three register sets overflow the register file)
+    // operands (the operand extents are the output extents and K); the A operand k-contiguous
+    // or staged as 16-byte x rows (the four-byte x-contiguous loader's per-row addresses for
+    // three register sets overflow the register file)
     // (with a triangular B every tile's K is still a whole number of slabs, at least four)
-    const bool fast = AK == S6_KC && g.a.vec && g.b.vec && g.M % 128 == 0 && g.N % 128 == 0 &&
+    const bool fast = (AK == S6_KC || AK == S6_XC4) && g.a.vec && g.b.vec && g.M % 128 == 0 && g.N % 128 == 0 &&
                       g.K % kSplitK == 0 && g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K &&
                       g.b.xext == g.N && g.b.kext == g.K && g.splits <= 1;
-    if constexpr (AK == S6_KC) {
+    if constexpr (AK == S6_KC || AK == S6_XC4) {
         if (fast) {
             hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true>), grid, dim3(512), 0, s, g);
             return hipGetLastError();
@@ -1866,8 +1866,8 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
         g.c = (float*)R; g.ldc = r; g.sc = n * r;
         g.M = (int)n; g.N = (int)r; g.K = (int)m;
         g.st = c.st; g.st_mask = mask; g.st_val = val;
-        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC, A6_BF16, S6_XC>(g, p.b, c.s)
-                                                   : launch_prod6<S6_XC, A6_F32, S6_XC>(g, p.b, c.s);
+        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b, c.s)
+                                                   : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b, c.s);
         DION_TRY(he);
         return 0;
     }
