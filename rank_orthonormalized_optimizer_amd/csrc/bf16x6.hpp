@@ -66,8 +66,8 @@ namespace dion {
 enum Src6 : int {
     S6_KC8 = 0,      // fp32 p0[x * ld + k], k contiguous, staged in chunks of eight k
     S6_KC = 1,       // fp32 p0[x * ld + k] (+ addend p1 at the same index), k contiguous
-    S6_XC = 2,       // fp32 p0[k * ld + x] (+ addend p1 at the same index), x contiguous
-    S6_XC4 = 4,      // the same layout, staged as 16-byte row vectors (four x by four k per thread)
+    S6_XC4 = 4,      // fp32 p0[k * ld + x] (+ addend p1 at the same index), x contiguous, staged as
+                     // 16-byte row vectors (four x by four k per thread)
 };
 enum Add6 : int { A6_NONE = 0, A6_F32 = 1, A6_BF16 = 2 };
 
@@ -250,80 +250,7 @@ struct Loader6<BX, S6_KC, ADD> {
     }
 };
 
-// x-contiguous fp32 (+ addend): thread owns one x and BX / 8 consecutive k (coalesced along x).
-// The k rows a wave reads are the same for all its lanes, so their offsets are made scalar.
-template <int BX, int ADD>
-struct Loader6<BX, S6_XC, ADD> {
-    static constexpr int KPT = BX * kSplitK / 256;   // k values per thread
-    static_assert(KPT % 4 == 0 && 256 % BX == 0 && BX % 64 == 0, "whole groups of four k per thread");
-    using AT = typename Add6T<ADD>::t;
-    float a[KPT];
-    AT b[ADD == A6_NONE ? 1 : KPT];
-    Parts4 sp[KPT / 4];
-    // interior tile (whole slab): no bounds tests
-    __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
-        const int x = x0 + t % BX;
-        const int kb = __builtin_amdgcn_readfirstlane(k0 + (t / BX) * KPT);   // uniform per wave
-        const float* pa = (const float*)op.p0 + (int64_t)kb * op.ld;
-        const AT* pb = ADD != A6_NONE ? (const AT*)op.p1 + (int64_t)kb * op.ld : nullptr;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            a[e] = pa[(int64_t)e * op.ld + x];
-            if constexpr (ADD != A6_NONE) b[e] = pb[(int64_t)e * op.ld + x];
-        }
-    }
-    static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
-        return x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
-    }
-    __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
-        const int x = x0 + t % BX;
-        const int kb = __builtin_amdgcn_readfirstlane(k0 + (t / BX) * KPT);   // uniform per wave
-        const float* pa = (const float*)op.p0 + (int64_t)kb * op.ld;
-        const AT* pb = ADD != A6_NONE ? (const AT*)op.p1 + (int64_t)kb * op.ld : nullptr;
-        if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
-        const bool xin = x < op.xext;
-        const int xs = xin ? x : 0;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const bool in = xin && kb + e < op.kext;
-            const int64_t o = (int64_t)(kb + e < op.kext ? e : 0) * op.ld + xs;
-            a[e] = in ? pa[o] : 0.f;
-            if constexpr (ADD != A6_NONE) b[e] = in ? pb[o] : AT(0);
-        }
-    }
-    __device__ __forceinline__ void split() {
-#pragma unroll
-        for (int g = 0; g < KPT / 4; ++g) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (ADD == A6_NONE) v[e] = a[4 * g + e];
-                else v[e] = sum6<ADD>(a[4 * g + e], b[4 * g + e]);
-            }
-            sp[g] = split4(v);
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* lds, int t) const {
-        const int x = t % BX, kb = (t / BX) * KPT;
-#pragma unroll
-        for (int g = 0; g < KPT / 4; ++g) store4(lds, BX * kSplitK, x, kb + 4 * g, sp[g]);
-    }
-    __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
-        const int x = t % BX, kb = (t / BX) * KPT;
-#pragma unroll
-        for (int g = 0; g < KPT / 4; ++g) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (ADD == A6_NONE) v[e] = a[4 * g + e];
-                else v[e] = sum6<ADD>(a[4 * g + e], b[4 * g + e]);
-            }
-            store4(lds, BX * kSplitK, x, kb + 4 * g, split4(v));
-        }
-    }
-};
-
-// x-contiguous fp32 (+ addend), 16-byte rows: each thread owns four consecutive x and four consecutive k
+// x-contiguous fp32 (+ addend): each thread owns four consecutive x and four consecutive k
 // (32 x 8 threads over the 128 x 32 tile), read as one 16-byte vector (8 bytes for a bf16
 // addend) per k row when the rows allow it (op.vec: ld, x0 and the bases 4-element aligned);
 // the split then writes each x's four k as one 8-byte chunk per part.

@@ -1036,8 +1036,13 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = 
     const int64_t m = p.m, r = p.r;
     constexpr int S = SrcOf<T>::v;
     const bool vr = (r % 4) == 0;
-    const int64_t splits = gram_splits<T>(p), kc = (m + splits - 1) / splits;
+    const int64_t splits = gram_splits<T>(p);
+    int64_t kc = (m + splits - 1) / splits;
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        // whole 32-k slabs per split where that still leaves the last split some rows, so the
+        // split-bf16 kernel can take its branch-free path
+        const int64_t kc32 = (kc + kSplitK - 1) / kSplitK * kSplitK;
+        if ((splits - 1) * kc32 < m) kc = kc32;
         int e;
         if ((e = gram6(c, P, mask, val, splits, kc))) return e;
         if (splits <= 1) return 0;
@@ -1766,10 +1771,13 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
     // operands (the operand extents are the output extents and K); the A operand k-contiguous
     // or staged as 16-byte x rows (the four-byte x-contiguous loader's per-row addresses for
     // three register sets overflow the register file)
-    // (with a triangular B every tile's K is still a whole number of slabs, at least four)
+    // (with a triangular B every tile's K is still a whole number of slabs, at least four; with
+    // split K every split must be whole slabs, at least three)
     const bool fast = (AK == S6_KC || AK == S6_XC4) && g.a.vec && g.b.vec && g.M % 128 == 0 && g.N % 128 == 0 &&
                       g.K % kSplitK == 0 && g.K >= 3 * kSplitK && g.a.xext == g.M && g.a.kext == g.K &&
-                      g.b.xext == g.N && g.b.kext == g.K && g.splits <= 1;
+                      g.b.xext == g.N && g.b.kext == g.K &&
+                      (g.splits <= 1 || (g.kc % kSplitK == 0 && g.kc >= 3 * kSplitK &&
+                                         g.K - (g.splits - 1) * g.kc >= 3 * kSplitK));
     if constexpr (AK == S6_KC || AK == S6_XC4) {
         if (fast) {
             hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true>), grid, dim3(512), 0, s, g);
@@ -1786,21 +1794,21 @@ static int gram6(const ChainCtx& c, const float* P, int mask, int val, int64_t s
     const Plan& p = *c.p;
     const int64_t m = p.m, r = p.r;
     Prod6Args g{};
-    g.a = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // A(i,k) = P[k][i]  (i contiguous)
-    g.b = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // B(k,j) = P[k][j]  (j contiguous)
+    g.a = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // A(i,k) = P[k][i]  (i contiguous, 16-byte rows)
+    g.b = Op6{P, nullptr, r, (int)r, (int)m, r % 4 == 0};   // B(k,j) = P[k][j]  (j contiguous, 16-byte rows)
     g.sa0 = g.sb0 = m * r * 4;
     g.M = g.N = (int)r; g.K = (int)m;
     g.lower = true;
     g.st = c.st; g.st_mask = mask; g.st_val = val;
     if (splits <= 1) {
         g.c = (float*)(c.ws + p.W); g.ldc = r; g.sc = r * r;
-        DION_TRY((launch_prod6<S6_XC, A6_NONE, S6_XC>(g, p.b, c.s)));
+        DION_TRY((launch_prod6<S6_XC4, A6_NONE, S6_XC4>(g, p.b, c.s)));
         return 0;
     }
     g.splits = (int)splits; g.kc = kc;
     g.ska = g.skb = kc * r * 4;
     g.c = (float*)(c.ws + p.gpart); g.ldc = r; g.sc = splits * r * r; g.scs = r * r;
-    DION_TRY((launch_prod6<S6_XC, A6_NONE, S6_XC>(g, p.b * splits, c.s)));
+    DION_TRY((launch_prod6<S6_XC4, A6_NONE, S6_XC4>(g, p.b * splits, c.s)));
     return 0;
 }
 
