@@ -125,14 +125,15 @@ __device__ __forceinline__ void store4(uint16_t* lds, int part_stride, int x, in
     for (int p = 0; p < 3; ++p) *(u32x2*)&lds[p * part_stride + off] = q.p[p];
 }
 
-template <int BX, int KIND, int ADD>
+// NT: the number of staging threads (256 or 512) that share one operand tile
+template <int BX, int KIND, int ADD, int NT = 256>
 struct Loader6;
 
 // k-contiguous fp32, no addend, in chunks of eight k: BX * 4 chunks, BX / 64 per thread (four
 // threads per row), so each part of a chunk is one 16-byte LDS write at its swizzled slot.
-template <int BX, int ADD>
-struct Loader6<BX, S6_KC8, ADD> {
-    static_assert(ADD == A6_NONE, "no addend");
+template <int BX, int ADD, int NT>
+struct Loader6<BX, S6_KC8, ADD, NT> {
+    static_assert(ADD == A6_NONE && NT == 256, "no addend, 256 threads");
     static constexpr int PER = BX / 64;
     float a[PER][8];
     __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
@@ -174,11 +175,11 @@ struct Loader6<BX, S6_KC8, ADD> {
     }
 };
 
-// k-contiguous fp32 (+ addend): BX * 8 groups of four k, BX / 32 per thread (8 threads per row).
+// k-contiguous fp32 (+ addend): BX * 8 groups of four k, BX * 8 / NT per thread (8 threads per row).
 // Interior tiles with vector-aligned rows take unchecked 4-element loads.
-template <int BX, int ADD>
-struct Loader6<BX, S6_KC, ADD> {
-    static constexpr int PER = BX / 32;
+template <int BX, int ADD, int NT>
+struct Loader6<BX, S6_KC, ADD, NT> {
+    static constexpr int RP = NT / 8, PER = BX / RP;   // rows per pass, passes
     using AT = typename Add6T<ADD>::t;
     float a[PER][4];
     AT b[ADD == A6_NONE ? 1 : PER][4];
@@ -188,7 +189,7 @@ struct Loader6<BX, S6_KC, ADD> {
         const int xr = t >> 3, kk = 4 * (t & 7);
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int64_t o = (int64_t)(x0 + xr + 32 * q) * op.ld + k0 + kk;
+            const int64_t o = (int64_t)(x0 + xr + RP * q) * op.ld + k0 + kk;
             const float4 v = *(const float4*)((const float*)op.p0 + o);
             a[q][0] = v.x; a[q][1] = v.y; a[q][2] = v.z; a[q][3] = v.w;
             if constexpr (ADD == A6_F32) {
@@ -209,7 +210,7 @@ struct Loader6<BX, S6_KC, ADD> {
         if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int x = x0 + xr + 32 * q, k = k0 + kk;
+            const int x = x0 + xr + RP * q, k = k0 + kk;
             const int64_t o = (int64_t)(x < op.xext ? x : 0) * op.ld + k;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -233,7 +234,7 @@ struct Loader6<BX, S6_KC, ADD> {
     }
     __device__ __forceinline__ void store(uint16_t* lds, int t) const {
 #pragma unroll
-        for (int q = 0; q < PER; ++q) store4(lds, BX * kSplitK, (t >> 3) + 32 * q, 4 * (t & 7), sp[q]);
+        for (int q = 0; q < PER; ++q) store4(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), sp[q]);
     }
     // split and store group by group (no register copy of the whole split slab)
     __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
@@ -245,67 +246,86 @@ struct Loader6<BX, S6_KC, ADD> {
                 if constexpr (ADD == A6_NONE) v[e] = a[q][e];
                 else v[e] = sum6<ADD>(a[q][e], b[q][e]);
             }
-            store4(lds, BX * kSplitK, (t >> 3) + 32 * q, 4 * (t & 7), split4(v));
+            store4(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), split4(v));
         }
     }
 };
 
-// x-contiguous fp32 (+ addend): each thread owns four consecutive x and four consecutive k
-// (32 x 8 threads over the 128 x 32 tile), read as one 16-byte vector (8 bytes for a bf16
-// addend) per k row when the rows allow it (op.vec: ld, x0 and the bases 4-element aligned);
-// the split then writes each x's four k as one 8-byte chunk per part.
-template <int BX, int ADD>
-struct Loader6<BX, S6_XC4, ADD> {
-    static_assert(BX == 128, "32 x 8 threads of 4 x 4 values");
+// x-contiguous fp32 (+ addend): each thread owns XW consecutive x (4 with 256 staging threads,
+// 2 with 512) and four consecutive k of the 128 x 32 tile, read as one XW-wide vector per k row
+// (half that for a bf16 addend) when the rows allow it (op.vec: ld, x0 and the bases
+// 4-element aligned); the split then writes each x's four k as one 8-byte chunk per part.
+template <int BX, int ADD, int NT>
+struct Loader6<BX, S6_XC4, ADD, NT> {
+    static constexpr int XW = BX * kSplitK / (4 * NT), TX = BX / XW;   // x per thread, threads per k group
+    static_assert(BX == 128 && (XW == 4 || XW == 2), "128 x 32 tile over 256 or 512 threads");
     using AT = typename Add6T<ADD>::t;
-    float a[16];                          // [k][x]: a[4 k + x]
-    AT b[ADD == A6_NONE ? 1 : 16];
+    float a[4 * XW];                      // [k][x]: a[XW k + x]
+    AT b[ADD == A6_NONE ? 1 : 4 * XW];
     static __device__ __forceinline__ bool interior(const Op6& op, int x0, int k0) {
         return op.vec && x0 + BX <= op.xext && k0 + kSplitK <= op.kext;
     }
     // interior tile with vector-legal rows: no bounds tests
     __device__ __forceinline__ void load_fast(const Op6& op, int x0, int k0, int t) {
-        const int64_t o = (int64_t)(k0 + 4 * (t >> 5)) * op.ld + x0 + 4 * (t & 31);
+        const int64_t o = (int64_t)(k0 + 4 * (t / TX)) * op.ld + x0 + XW * (t % TX);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float4 v = *(const float4*)((const float*)op.p0 + o + e * op.ld);
-            a[4 * e + 0] = v.x; a[4 * e + 1] = v.y; a[4 * e + 2] = v.z; a[4 * e + 3] = v.w;
+            const float* pa = (const float*)op.p0 + o + e * op.ld;
+            if constexpr (XW == 4) {
+                const float4 v = *(const float4*)pa;
+                a[4 * e + 0] = v.x; a[4 * e + 1] = v.y; a[4 * e + 2] = v.z; a[4 * e + 3] = v.w;
+            } else {
+                const float2 v = *(const float2*)pa;
+                a[2 * e + 0] = v.x; a[2 * e + 1] = v.y;
+            }
             if constexpr (ADD == A6_F32) {
-                const float4 w = *(const float4*)((const float*)op.p1 + o + e * op.ld);
-                b[4 * e + 0] = w.x; b[4 * e + 1] = w.y; b[4 * e + 2] = w.z; b[4 * e + 3] = w.w;
+                const float* pb = (const float*)op.p1 + o + e * op.ld;
+                if constexpr (XW == 4) {
+                    const float4 w = *(const float4*)pb;
+                    b[4 * e + 0] = w.x; b[4 * e + 1] = w.y; b[4 * e + 2] = w.z; b[4 * e + 3] = w.w;
+                } else {
+                    const float2 w = *(const float2*)pb;
+                    b[2 * e + 0] = w.x; b[2 * e + 1] = w.y;
+                }
             } else if constexpr (ADD == A6_BF16) {
-                const uint2 w = *(const uint2*)((const uint16_t*)op.p1 + o + e * op.ld);
-                b[4 * e + 0] = (uint16_t)w.x; b[4 * e + 1] = (uint16_t)(w.x >> 16);
-                b[4 * e + 2] = (uint16_t)w.y; b[4 * e + 3] = (uint16_t)(w.y >> 16);
+                const uint16_t* pb = (const uint16_t*)op.p1 + o + e * op.ld;
+                if constexpr (XW == 4) {
+                    const uint2 w = *(const uint2*)pb;
+                    b[4 * e + 0] = (uint16_t)w.x; b[4 * e + 1] = (uint16_t)(w.x >> 16);
+                    b[4 * e + 2] = (uint16_t)w.y; b[4 * e + 3] = (uint16_t)(w.y >> 16);
+                } else {
+                    const uint32_t w = *(const uint32_t*)pb;
+                    b[2 * e + 0] = (uint16_t)w; b[2 * e + 1] = (uint16_t)(w >> 16);
+                }
             }
         }
     }
     __device__ __forceinline__ void load(const Op6& op, int x0, int k0, int t) {
         if (interior(op, x0, k0)) { load_fast(op, x0, k0, t); return; }
         // element loads from clamped addresses (element 0 is always valid), values selected
-        const int x = x0 + 4 * (t & 31), k = k0 + 4 * (t >> 5);
+        const int x = x0 + XW * (t % TX), k = k0 + 4 * (t / TX);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int e = q >> 2, i = q & 3;
+        for (int q = 0; q < 4 * XW; ++q) {
+            const int e = q / XW, i = q % XW;
             const bool in = x + i < op.xext && k + e < op.kext;
             const int64_t o = in ? (int64_t)(k + e) * op.ld + x + i : 0;
             const float va = ((const float*)op.p0)[o];
-            a[4 * e + i] = in ? va : 0.f;
+            a[XW * e + i] = in ? va : 0.f;
             if constexpr (ADD != A6_NONE) {
                 const AT vb = ((const AT*)op.p1)[o];
-                b[4 * e + i] = in ? vb : AT(0);
+                b[XW * e + i] = in ? vb : AT(0);
             }
         }
     }
     __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
-        const int xl = 4 * (t & 31), kl = 4 * (t >> 5);
+        const int xl = XW * (t % TX), kl = 4 * (t / TX);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < XW; ++i) {
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if constexpr (ADD == A6_NONE) v[e] = a[4 * e + i];
-                else v[e] = sum6<ADD>(a[4 * e + i], b[4 * e + i]);
+                if constexpr (ADD == A6_NONE) v[e] = a[XW * e + i];
+                else v[e] = sum6<ADD>(a[XW * e + i], b[XW * e + i]);
             }
             store4(lds, BX * kSplitK, xl + i, kl, split4(v));
         }

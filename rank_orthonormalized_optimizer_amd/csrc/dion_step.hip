@@ -1613,11 +1613,11 @@ struct Prod6Args {
 // Staging side of prod6_kernel: three register sets of raw operand values and three LDS buffers,
 // both indexed by slab % 3, so a slab's global loads are issued three slabs before it is split
 // (enough bytes in flight per CU to cover the memory latency at the matrix-core rate).
-template <int AK, int AADD, int BK6>
+template <int AK, int AADD, int BK6, int NT>
 struct Stage6 {
     static constexpr int BT = 128, PT = BT * kSplitK, D = 3;
-    Loader6<BT, AK, AADD> la[D];
-    Loader6<BT, BK6, A6_NONE> lb[D];
+    Loader6<BT, AK, AADD, NT> la[D];
+    Loader6<BT, BK6, A6_NONE, NT> lb[D];
     template <int J>
     __device__ __forceinline__ void load(const Op6& A, const Op6& B, int m0, int n0, int k, int K, int t) {
         if (k < K) { la[J].load(A, m0, k, t); lb[J].load(B, n0, k, t); }
@@ -1653,12 +1653,13 @@ struct Stage6 {
     }
 };
 
-template <int AK, int AADD, int BK6, bool FAST>
-__global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
-    // Eight waves: waves 0-3 multiply (a 64 x 64 sub-tile each), waves 4-7 stage the operands
-    // (load, split into bf16 parts, write LDS).  Each SIMD holds one wave of each kind, so the
-    // staging VALU work issues between the other wave's MFMAs; one barrier per slab.
-    using St = Stage6<AK, AADD, BK6>;
+template <int AK, int AADD, int BK6, bool FAST, int NT>
+__global__ __launch_bounds__(256 + NT) void prod6_kernel(Prod6Args g) {
+    // Waves 0-3 multiply (a 64 x 64 sub-tile each); the NT / 64 waves after them stage the
+    // operands (load, split into bf16 parts, write LDS).  Each SIMD holds one multiplying wave and
+    // NT / 256 staging waves, so the staging work issues between the other wave's MFMAs; one
+    // barrier per slab.
+    using St = Stage6<AK, AADD, BK6, NT>;
     constexpr int BT = St::BT, PT = St::PT;
     const TileId tid = xcd_tile_id();
     const int sp = g.splits > 1 ? g.splits : 1, bz = tid.z / sp, ks = tid.z % sp;
@@ -1763,6 +1764,11 @@ __global__ __launch_bounds__(512) void prod6_kernel(Prod6Args g) {
             }
 }
 
+#ifndef DION_STAGE_THREADS
+#define DION_STAGE_THREADS 512
+#endif
+constexpr int kStageThreads = DION_STAGE_THREADS;   // staging threads of the split-bf16 product kernel
+
 template <int AK, int AADD, int BK6>
 static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
@@ -1780,11 +1786,12 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
                                          g.K - (g.splits - 1) * g.kc >= 3 * kSplitK));
     if constexpr (AK == S6_KC || AK == S6_XC4) {
         if (fast) {
-            hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true, kStageThreads>), grid, dim3(256 + kStageThreads), 0,
+                               s, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false>), grid, dim3(512), 0, s, g);
+    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false, kStageThreads>), grid, dim3(256 + kStageThreads), 0, s, g);
     return hipGetLastError();
 }
 
