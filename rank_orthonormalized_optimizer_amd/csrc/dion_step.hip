@@ -527,6 +527,23 @@ __global__ __launch_bounds__(256) void copy_shift_kernel(const T* W, T* L, int64
 // ---------------------------------------------------------------------------
 // column norms of R, the next Q, and rounding of the fp64 chain to fp32
 // ---------------------------------------------------------------------------
+// R += Rpart for the matrices with (st & mask) == val: the second K-split of the back-projection.
+__global__ __launch_bounds__(256) void add_split_kernel(float* R, const float* Rpart, int64_t total, const int* st,
+                                                        int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    R += bz * total;
+    Rpart += bz * total;
+    for (int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); i < total; i += 4 * (int64_t)gridDim.x * 256) {
+        if (i + 4 <= total && (total & 3) == 0) {
+            const float4 a = *(const float4*)(R + i), b = *(const float4*)(Rpart + i);
+            *(float4*)(R + i) = float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+        } else {
+            for (int64_t j = i; j < i + 4 && j < total; ++j) R[j] += Rpart[j];
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void colnorm_partial_kernel(const float* R32, const double* R64, double* part,
                                                               int64_t n, int64_t r, int nchunk, const int* st) {
     const int bz = blockIdx.z, chunk = blockIdx.y;
@@ -1601,11 +1618,11 @@ struct Prod6Args {
     int M, N, K;
     const int* st;
     int st_mask, st_val;
-    // split K (no addend): grid z = matrix * splits + split; split s covers k in
-    // [s kc, min(K, (s + 1) kc)), its operands start ska / skb bytes further and its output
-    // slice scs elements further
+    // split K: grid z = matrix * splits + split; split s covers k in [s kc, min(K, (s + 1) kc)),
+    // its operands start ska / ska1 / skb bytes further (a.p0, a.p1, b.p0) and its output slice
+    // scs elements further
     int splits;
-    int64_t kc, ska, skb, scs;
+    int64_t kc, ska, ska1, skb, scs;
     bool lower;                  // square output: tiles entirely above the diagonal are skipped
     bool tri;                    // B(k, j) = 0 for k > j: output column tile n0 stops at k = n0 + 128
 };
@@ -1677,6 +1694,7 @@ __global__ __launch_bounds__(256 + NT) void prod6_kernel(Prod6Args g) {
     int K = g.K;
     if (sp > 1) {
         A.p0 = (const char*)A.p0 + ks * g.ska;
+        if (A.p1) A.p1 = (const char*)A.p1 + ks * g.ska1;
         B.p0 = (const char*)B.p0 + ks * g.skb;
         K = (int)(g.kc < (int64_t)g.K - ks * g.kc ? g.kc : (int64_t)g.K - ks * g.kc);
         A.kext = K;
@@ -1881,6 +1899,23 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
         g.c = (float*)R; g.ldc = r; g.sc = n * r;
         g.M = (int)n; g.N = (int)r; g.K = (int)m;
         g.st = c.st; g.st_mask = mask; g.st_val = val;
+        // K split in two (second half into the unused fp64 R region, added back in split order)
+        // when that turns a final partial round of tiles (one workgroup per CU) into whole rounds
+        const int64_t tiles = ((n + 127) / 128) * ((r + 127) / 128) * p.b, slots = 256;
+        const double rounds1 = (double)((tiles + slots - 1) / slots), rounds2 = (double)((2 * tiles + slots - 1) / slots) / 2;
+        if (m % 64 == 0 && m / 2 >= 3 * kSplitK && rounds2 < rounds1 - 0.2) {
+            g.splits = 2; g.kc = m / 2;
+            g.ska = g.kc * n * 4; g.ska1 = g.kc * n * gsz; g.skb = g.kc * r * 4;
+            g.scs = (int64_t)(p.R64 - p.R32) / 4;
+            const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b * 2, c.s)
+                                                       : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b * 2, c.s);
+            DION_TRY(he);
+            dim3 grid(grid_1d(n * r / 4, 1024), (unsigned)p.b);
+            hipLaunchKernelGGL(add_split_kernel, grid, dim3(256), 0, c.s, (float*)R, (const float*)(c.ws + p.R64), n * r,
+                               (const int*)c.st, mask, val);
+            DION_TRY(hipGetLastError());
+            return 0;
+        }
         const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b, c.s)
                                                    : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b, c.s);
         DION_TRY(he);
