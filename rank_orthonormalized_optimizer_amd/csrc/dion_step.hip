@@ -788,7 +788,7 @@ __device__ __forceinline__ uint2 nt_ld2(const uint16_t* p) {
     return uint2{v[0], v[1]};
 }
 __device__ __forceinline__ void nt_st2(uint16_t* p, uint2 v) { __builtin_nontemporal_store(u32x2{v.x, v.y}, (u32x2*)p); }
-template <bool G_BF16, bool X_BF16>
+template <bool G_BF16, bool X_BF16, bool FAST>
 __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     constexpr int BM = 128, BN = 64, PA = BM * kSplitK, PB = BN * kSplitK, FM = 4, FN = 2;
     const TileId tid = xcd_tile_id();
@@ -798,8 +798,6 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
     const Op6 oR{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
     const Op6 oQ{u.Q + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
-    Loader6<BM, S6_KC8, A6_NONE> lp;
-    Loader6<BN, S6_KC8, A6_NONE> lr, lq;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     const int fr = lane & 15, fc = lane >> 4;
     f32x4 acc1[FM][FN], acc2[FM][FN];
@@ -807,27 +805,86 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
-    auto load = [&](int k) {
-        lp.load(oP, m0, k, t);
-        lr.load(oR, n0, k, t);
-        lq.load(oQ, n0, k, t);
-    };
-    auto store = [&]() {
-        lp.split_store(lds, t);
-        lr.split_store(lds + 3 * PA, t);
-        lq.split_store(lds + 3 * PA + 3 * PB, t);
-    };
-    load(0);
-    store();
-    __syncthreads();
-    for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
-        const bool more = k0 + kSplitK < u.kp;
-        if (more) load(k0 + kSplitK);
+    auto mma = [&]() {
         mma6_slab2<BM, BN, FM, FN>(lds, lds + 3 * PA, lds + 3 * PA + 3 * PB, acc1, acc2, wm * 64, wn * 32, fr, fc);
+    };
+    if constexpr (FAST) {
+        // every tile interior and every slab whole: two register sets, so each slab's loads are
+        // issued two slabs before its split (branch-free steady loop, then a drain)
+        Loader6<BM, S6_KC8, A6_NONE> lp[2];
+        Loader6<BN, S6_KC8, A6_NONE> lr[2], lq[2];
+        auto load = [&](auto jc, int k) {
+            constexpr int J = decltype(jc)::value;
+            lp[J].load_fast(oP, m0, k, t);
+            lr[J].load_fast(oR, n0, k, t);
+            lq[J].load_fast(oQ, n0, k, t);
+        };
+        auto store = [&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            lp[J].split_store(lds, t);
+            lr[J].split_store(lds + 3 * PA, t);
+            lq[J].split_store(lds + 3 * PA + 3 * PB, t);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        const int nslab = u.kp / kSplitK;   // >= 2
+        load(I0{}, 0);
+        load(I1{}, kSplitK);
+        store(I0{});
         __syncthreads();
-        if (more) {
-            store();
+        int sl = 0;
+        for (; sl + 3 < nslab; sl += 2) {   // LDS: slab sl; set 1: slab sl + 1
+            load(I0{}, (sl + 2) * kSplitK);
+            mma();
             __syncthreads();
+            store(I1{});
+            __syncthreads();
+            load(I1{}, (sl + 3) * kSplitK);
+            mma();
+            __syncthreads();
+            store(I0{});
+            __syncthreads();
+        }
+        // the last two or three slabs: LDS holds slab sl, set 1 slab sl + 1 (sl + 2 < nslab: set 0
+        // is loaded below)
+        const bool three = sl + 2 < nslab;
+        if (three) load(I0{}, (sl + 2) * kSplitK);
+        mma();
+        __syncthreads();
+        store(I1{});
+        __syncthreads();
+        mma();
+        if (three) {
+            __syncthreads();
+            store(I0{});
+            __syncthreads();
+            mma();
+        }
+    } else {
+        Loader6<BM, S6_KC8, A6_NONE> lp;
+        Loader6<BN, S6_KC8, A6_NONE> lr, lq;
+        auto load = [&](int k) {
+            lp.load(oP, m0, k, t);
+            lr.load(oR, n0, k, t);
+            lq.load(oQ, n0, k, t);
+        };
+        auto store = [&]() {
+            lp.split_store(lds, t);
+            lr.split_store(lds + 3 * PA, t);
+            lq.split_store(lds + 3 * PA + 3 * PB, t);
+        };
+        load(0);
+        store();
+        __syncthreads();
+        for (int k0 = 0; k0 < u.kp; k0 += kSplitK) {
+            const bool more = k0 + kSplitK < u.kp;
+            if (more) load(k0 + kSplitK);
+            mma();
+            __syncthreads();
+            if (more) {
+                store();
+                __syncthreads();
+            }
         }
     }
     const int64_t mn = (int64_t)u.m * u.n;
@@ -2006,7 +2063,10 @@ static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, f
     const int64_t big = ((p.n + 63) / 64) * ((p.m + 127) / 128) * p.b;
     if (big >= kUpdBigMinTiles) {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
-        hipLaunchKernelGGL((update3_kernel<GB, XB>), grid, dim3(256), 0, s, u);
+        // all tiles interior, whole slabs, vector-legal rows: the two-set branch-free loop
+        const bool fast = p.m % 128 == 0 && p.n % 64 == 0 && p.r % kSplitK == 0 && p.r >= 2 * kSplitK && u.vec;
+        if (fast) hipLaunchKernelGGL((update3_kernel<GB, XB, true>), grid, dim3(256), 0, s, u);
+        else hipLaunchKernelGGL((update3_kernel<GB, XB, false>), grid, dim3(256), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
         hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB>), grid, dim3(256), 0, s, u);
