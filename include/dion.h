@@ -28,7 +28,8 @@
  *   Readings where the pages are silent: s = sqrt(m/n); eps is used only as
  *   ||r_j|| + eps; "orth" is the unpivoted thin-QR Q-factor with a positive
  *   diagonal, reached here by Cholesky-based QR (CholeskyQR2) with an fp64
- *   fallback chain for ill-conditioned P0.
+ *   fallback chain for ill-conditioned P0 (fp64 CholeskyQR2, shifted CholeskyQR3,
+ *   and a Householder QR where those break down).
  *
  * Memory and ownership
  *   Every buffer is device memory owned by the caller; the library allocates
@@ -84,7 +85,8 @@ enum {
     DION_ERR_OVERLAP = -6,    /* two of X, G, M, Q, workspace, flags overlap */
     DION_ERR_WORKSPACE = -7,  /* workspace smaller than dion_workspace_size() */
     DION_ERR_DTYPE = -8,      /* x_dtype or g_dtype not a dion_dtype */
-    DION_ERR_OPTION = -9,     /* unknown option bit, or contradictory options */
+    DION_ERR_OPTION = -9,     /* unknown option bit, contradictory options, or
+                                 DION_OPT_HOUSEHOLDER with rank > 4096 */
     DION_ERR_HIP = -100       /* -100 - hipError_t for a failed HIP call */
 };
 
@@ -95,6 +97,10 @@ enum {
     DION_OPT_FORCE_F64 = 2,   /* every matrix uses the fp64 chain */
     DION_OPT_FORCE_F32 = 4,   /* never fall back; an fp32 breakdown is reported as
                                  DION_FLAG_NONFINITE and its results are undefined */
+    DION_OPT_HOUSEHOLDER = 16, /* the fp64 chain orthonormalizes P0 by its last-resort Householder
+                                 QR instead of CholeskyQR (with DION_OPT_FORCE_F64: every
+                                 matrix); not with DION_OPT_FORCE_F32, rank <= 4096.  The
+                                 Householder QR runs one workgroup per matrix: it is slow */
     DION_OPT_CHUNKS_SHIFT = 8 /* bits 8..11: number of concurrent chunks the stack is split into
                                  (0 = automatic, 1 = everything on `stream`); see Execution */
 };
@@ -103,7 +109,9 @@ enum {
 enum {
     DION_FLAG_F64 = 1,        /* this step's P and R came from the fp64 chain */
     DION_FLAG_NONFINITE = 2,  /* a NaN/Inf was met, or the factorization broke down */
-    DION_FLAG_SHIFTED = 4     /* the fp64 chain needed the shifted first pass */
+    DION_FLAG_SHIFTED = 4,    /* the fp64 chain needed the shifted first pass */
+    DION_FLAG_HOUSEHOLDER = 8 /* P came from the fp64 Householder QR (the CholeskyQR passes broke
+                                 down, or DION_OPT_HOUSEHOLDER) */
 };
 
 /* phases of one step, in launch order (for dion_step_batched_profiled) */

@@ -12,7 +12,7 @@ Lion, as the page describes.
 """
 from __future__ import annotations
 
-from ._lib import (BF16, EXPORTS, F32, FLAG_F64, FLAG_NONFINITE, FLAG_SHIFTED,  # noqa: F401
-                   OPT_FORCE_F32, OPT_FORCE_F64, OPT_STICKY_F64, DionError, load,
+from ._lib import (BF16, EXPORTS, F32, FLAG_F64, FLAG_HOUSEHOLDER, FLAG_NONFINITE, FLAG_SHIFTED,  # noqa: F401
+                   OPT_FORCE_F32, OPT_FORCE_F64, OPT_HOUSEHOLDER, OPT_STICKY_F64, DionError, load,
                    step_batched_raw, strerror, version, workspace_size)
 from .api import DionStack, StickyF64Hint, group_matrices, step_  # noqa: F401

@@ -23,14 +23,14 @@ F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_HYPER, ERR_ALIGN = -1, -2, -3, -4, -5
 ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_HIP = -6, -7, -8, -9, -100
-OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32 = 1, 2, 4
+OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32, OPT_HOUSEHOLDER = 1, 2, 4, 16
 OPT_CHUNKS_SHIFT = 8
 
 
 def opt_chunks(n: int) -> int:
     """Option bits asking for n concurrent chunks (1 = everything on the caller's stream)."""
     return (int(n) & 15) << OPT_CHUNKS_SHIFT
-FLAG_F64, FLAG_NONFINITE, FLAG_SHIFTED = 1, 2, 4
+FLAG_F64, FLAG_NONFINITE, FLAG_SHIFTED, FLAG_HOUSEHOLDER = 1, 2, 4, 8
 
 NUM_PHASES = 10
 PHASES = ("init", "f32_product", "f32_qr", "f32_backproject", "f64_product", "f64_qr", "f64_backproject",

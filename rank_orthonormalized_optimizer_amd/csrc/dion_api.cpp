@@ -43,9 +43,10 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64
     if (!(mu >= 0.0f && mu < 1.0f) || !isfinite(lr) || !isfinite(eps) || !(eps >= 0.0f)) return DION_ERR_HYPER;
     if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
         return DION_ERR_DTYPE;
-    const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 |
+    const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 | DION_OPT_HOUSEHOLDER |
                            (15u << DION_OPT_CHUNKS_SHIFT);
-    if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)))
+    if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)) ||
+        ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)))
         return DION_ERR_OPTION;
     dion::Plan p;
     if (!dion::make_plan(m, n, batch, rank, &p)) return DION_ERR_SHAPE;

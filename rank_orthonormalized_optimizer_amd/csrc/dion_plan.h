@@ -18,6 +18,7 @@ enum : int {
     ST_SHIFT = 2,    // the fp64 chain needs the shifted first pass (and a third pass)
     ST_FAIL = 4,     // a factorization broke down with no further fallback
     ST_CHOL2 = 8,    // this re-orthonormalization pass uses the Cholesky path (P^T P far from I)
+    ST_HH = 16,      // P came from the fp64 Householder QR
 };
 
 // Partial sums of squares per matrix written by the near-identity test (fixed-order reduction).

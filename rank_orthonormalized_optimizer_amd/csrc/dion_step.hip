@@ -1027,6 +1027,7 @@ __global__ __launch_bounds__(256) void flags_out_kernel(const int* st, const dou
         int f = 0;
         if (s & ST_PATH64) f |= DION_FLAG_F64;
         if (s & ST_SHIFT) f |= DION_FLAG_SHIFTED;
+        if (s & ST_HH) f |= DION_FLAG_HOUSEHOLDER;
         if ((s & ST_FAIL) || bad) f |= DION_FLAG_NONFINITE;
         flags[bz] = f;
     }
@@ -1240,6 +1241,92 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         }
     }
     return 0;
+}
+
+constexpr int64_t kHouseholderMaxRank = 4096;   // the kernel keeps tau and the signs of R in LDS
+
+// Last-resort orthonormalization of the fp64 chain: the thin-QR Q-factor of A (fp64 [m][r] per
+// matrix, overwritten by the Householder vectors and R) written to Q, with a positive diagonal of
+// R.  It follows the textbook Householder QR (the QR decomposition named in the rivista.ai
+// paragraph "Tecnicamente"): for column j, H_j = I - tau_j v_j v_j^T maps A[j:, j] to beta_j e_1
+// with v_j[0] = 1 and beta_j = -sign(A[j][j]) ||A[j:, j]||; H_j is applied to the columns to the
+// right; then Q = H_0 ... H_{r-1} [I; 0] is accumulated backwards and column j is negated where
+// beta_j < 0.  One workgroup per selected matrix, in global memory: this path runs only where the
+// CholeskyQR passes broke down (or when requested), so it favors simplicity over speed.  Each
+// selected matrix leaves ST_FAIL and gains ST_HH.
+__global__ __launch_bounds__(1024) void householder_kernel(double* A, double* Q, int64_t m, int64_t r, int* st,
+                                                           int st_mask, int st_val) {
+    const int bz = blockIdx.x;
+    if ((st[bz] & st_mask) != st_val) return;
+    A += bz * m * r;
+    Q += bz * m * r;
+    constexpr int NT = 1024, RMAX = kHouseholderMaxRank;
+    __shared__ double red[NT];
+    __shared__ double tau[RMAX];
+    __shared__ float sgn[RMAX];
+    const int t = threadIdx.x;
+    auto block_sum = [&](double v) {
+        red[t] = v;
+        __syncthreads();
+        for (int w = NT / 2; w > 0; w >>= 1) {
+            if (t < w) red[t] += red[t + w];
+            __syncthreads();
+        }
+        const double s = red[0];
+        __syncthreads();
+        return s;
+    };
+    for (int64_t j = 0; j < r; ++j) {
+        const double x0 = A[j * r + j];   // read before the barriers below, after which thread 0 overwrites it
+        double ss = 0.0;
+        for (int64_t i = j + 1 + t; i < m; i += NT) { const double a = A[i * r + j]; ss += a * a; }
+        const double s = block_sum(ss);
+        double tj = 0.0, beta = x0;
+        if (s > 0.0) {
+            const double alpha = sqrt(x0 * x0 + s);
+            beta = x0 >= 0.0 ? -alpha : alpha;
+            tj = (beta - x0) / beta;
+            const double scale = 1.0 / (x0 - beta);
+            for (int64_t i = j + 1 + t; i < m; i += NT) A[i * r + j] *= scale;
+        }
+        if (t == 0) { tau[j] = tj; sgn[j] = beta < 0.0 ? -1.0f : 1.0f; A[j * r + j] = beta; }
+        __syncthreads();
+        if (tj != 0.0) {   // columns c > j: w = v^T A[j:, c]; A[j:, c] -= tau w v   (v[0] = 1)
+            for (int64_t c = j + 1 + t; c < r; c += NT) {
+                double w = A[j * r + c];
+                for (int64_t i = j + 1; i < m; ++i) w += A[i * r + j] * A[i * r + c];
+                w *= tj;
+                A[j * r + c] -= w;
+                for (int64_t i = j + 1; i < m; ++i) A[i * r + c] -= w * A[i * r + j];
+            }
+        }
+        __syncthreads();
+    }
+    // Q = H_0 ... H_{r-1} [I; 0], built backwards: after step j only columns >= j are non-trivial
+    for (int64_t idx = t; idx < m * r; idx += NT) Q[idx] = (idx / r == idx % r) ? 1.0 : 0.0;
+    __syncthreads();
+    for (int64_t j = r - 1; j >= 0; --j) {
+        const double tj = tau[j];
+        if (tj != 0.0) {
+            for (int64_t c = j + t; c < r; c += NT) {
+                double w = Q[j * r + c];
+                for (int64_t i = j + 1; i < m; ++i) w += A[i * r + j] * Q[i * r + c];
+                w *= tj;
+                Q[j * r + c] -= w;
+                for (int64_t i = j + 1; i < m; ++i) Q[i * r + c] -= w * A[i * r + j];
+            }
+        }
+        __syncthreads();
+    }
+    for (int64_t idx = t; idx < m * r; idx += NT)
+        if (sgn[idx % r] < 0.0f) Q[idx] = -Q[idx];
+    if (t == 0) st[bz] = (st[bz] & ~ST_FAIL) | ST_HH;
+}
+
+// st |= bits for the matrices with (st & mask) == val.
+__global__ void set_bits_kernel(int* st, int64_t b, int st_mask, int st_val, int bits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < b && (st[i] & st_mask) == st_val) st[i] |= bits;
 }
 
 template <typename T>
@@ -1993,7 +2080,7 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
 
 template <typename T>
 static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf16, const float* Q,
-                     bool force32, void* const* ev) {
+                     bool force32, void* const* ev, bool householder = false) {
     // ev: events marking the starts of the chain's three phases (product, QR, back-projection)
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], c.s) : hipSuccess; };
     const Plan& p = *c.p;
@@ -2026,6 +2113,10 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
                     : bq_gemm<T, SRC_SUM_F32>(c, M, G, gsz, Q, P, A64, A64))) return e;
     DION_TRY(c.open_gate());
     DION_TRY(mark(1));
+    if (householder) {   // requested: every fp64-chain matrix goes to the Householder QR below
+        hipLaunchKernelGGL(set_bits_kernel, dim3(grid_1d(p.b)), dim3(256), 0, c.s, c.st, p.b, A64, A64, F);
+        DION_TRY(hipGetLastError());
+    }
     // pass 1: unshifted attempt; a failed pivot or a large diagonal ratio marks SHIFT,
     // and the marked matrices factor W + s I instead (W is kept by the factorization)
     if ((e = gram<T>(c, P, A64 | F, A64))) return e;
@@ -2038,8 +2129,19 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearId64, F))) return e;
     {
         dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
-        hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st, A64 | SH | F,
-                           A64 | SH);
+        // Where a pass broke down, P still holds P0 times an upper-triangular matrix (the passes
+        // before the failing one), whose Q-factor is that of P0: Householder QR of a copy in Pb,
+        // the Q-factor written back to P
+        if constexpr (sizeof(T) == 8) if (p.r <= kHouseholderMaxRank) {
+            hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, (const T*)P, Pb, p.m * p.r, c.st,
+                               A64 | F, A64 | F);
+            DION_TRY(hipGetLastError());
+            hipLaunchKernelGGL(householder_kernel, dim3((unsigned)p.b), dim3(1024), 0, c.s, (double*)Pb, (double*)P,
+                               p.m, p.r, c.st, A64 | F, A64 | F);
+            DION_TRY(hipGetLastError());
+        }
+        hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st,
+                           A64 | SH | F | ST_HH, A64 | SH);
         DION_TRY(hipGetLastError());
     }
     DION_TRY(mark(2));
@@ -2109,7 +2211,8 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
         return e;
     if (force64 && ev)
         for (int i = DION_PHASE_F32_PRODUCT; i <= DION_PHASE_F32_BACKPROJECT; ++i) DION_TRY(mark(i));
-    if (!force32 && (e = run_chain<double>(c, M, G, g_bf16, Q, force32, ev ? ev + DION_PHASE_F64_PRODUCT : nullptr)))
+    if (!force32 && (e = run_chain<double>(c, M, G, g_bf16, Q, force32, ev ? ev + DION_PHASE_F64_PRODUCT : nullptr,
+                                           (options & DION_OPT_HOUSEHOLDER) != 0)))
         return e;
     if (force32 && ev)
         for (int i = DION_PHASE_F64_PRODUCT; i <= DION_PHASE_F64_BACKPROJECT; ++i) DION_TRY(mark(i));

@@ -87,6 +87,9 @@ def call(**kw):
     (dict(g_dtype=-1), _lib.ERR_DTYPE),
     (dict(options=8), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_FORCE_F32 | _lib.OPT_FORCE_F64), _lib.ERR_OPTION),
+    (dict(options=_lib.OPT_HOUSEHOLDER | _lib.OPT_FORCE_F32), _lib.ERR_OPTION),
+    (dict(options=_lib.OPT_HOUSEHOLDER, m=4097, n=4097, batch=1, rank=4097), _lib.ERR_OPTION),
+    (dict(options=32), _lib.ERR_OPTION),
     (dict(X=0), _lib.ERR_NULL),
     (dict(Q=0), _lib.ERR_NULL),
     (dict(workspace=0), _lib.ERR_NULL),

@@ -204,6 +204,19 @@ def test_fp32_chain_gram_splits(cuda, batch, m, n, r):
     check(rep, tol_for(wl))
 
 
+@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+def test_householder_fallback(cuda, wid):
+    """The fp64 chain's last-resort Householder QR (taken where every CholeskyQR pass broke down),
+    requested for every matrix: each matrix must report it, and the step must match the oracle."""
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.SMALL[wid]
+    rep = run_teacher_forced(wl, cuda, options=dion.OPT_FORCE_F64 | dion.OPT_HOUSEHOLDER, steps=2)
+    for _, _, _, flags in rep:
+        assert np.all(flags & dion.FLAG_HOUSEHOLDER) and np.all(flags & dion.FLAG_F64), flags
+        assert not np.any(flags & dion.FLAG_NONFINITE), flags
+    check(rep, tol_for(wl))
+
+
 @pytest.mark.parametrize("force64", [False, True])
 def test_shifted_first_pass(cuda, force64):
     """8 decades of spectrum: the fp64 chain's plain Cholesky of P0^T P0 breaks down (host fp64
