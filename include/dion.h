@@ -177,6 +177,35 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q,
                                int32_t* flags, uint32_t options, void* stream,
                                void* const* events);
 
+/*
+ * The parameters Dion does not take.  The rivista.ai page (the paragraph
+ * beginning "Tecnicamente") leaves biases and 1-D weights to optimizers such as
+ * AdamW or Lion; these are the published rules, one element-wise pass each over
+ * a contiguous array of n elements, in fp32 arithmetic:
+ *
+ *   AdamW, step t >= 1:  p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;
+ *                        v <- b2 v + (1 - b2) g^2;
+ *                        p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ *   Lion:                c = b1 m + (1 - b1) g;  p <- p (1 - lr wd) - lr sign(c);
+ *                        m <- b2 m + (1 - b2) g                       (sign(0) = 0)
+ *
+ *   param    device, [n], p_dtype (DION_F32 or DION_BF16; bf16 rounded to nearest
+ *            even once per step), updated in place
+ *   grad     device, [n], g_dtype, read only
+ *   exp_avg, exp_avg_sq   device, [n], fp32, updated in place (caller-owned state,
+ *            zero before the first step)
+ *   n >= 0 (0 is a no-op); t >= 1; b1, b2 in [0, 1); lr, wd finite; eps finite >= 0
+ * Pointers 16-byte aligned and not overlapping.  Asynchronous on `stream`
+ * (NULL = default stream); no allocation.  Returns DION_OK or a negative status
+ * (checked on the host before anything is enqueued).
+ */
+int dion_adamw_step(void* param, const void* grad, float* exp_avg, float* exp_avg_sq, int64_t n, int64_t t,
+                    float lr, float beta1, float beta2, float eps, float weight_decay,
+                    int p_dtype, int g_dtype, void* stream);
+int dion_lion_step(void* param, const void* grad, float* exp_avg, int64_t n,
+                   float lr, float beta1, float beta2, float weight_decay,
+                   int p_dtype, int g_dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* dion_strerror(int status);
 

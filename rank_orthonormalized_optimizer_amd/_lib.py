@@ -36,8 +36,8 @@ NUM_PHASES = 10
 PHASES = ("init", "f32_product", "f32_qr", "f32_backproject", "f64_product", "f64_qr", "f64_backproject",
           "norms", "update", "flags")
 
-EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_strerror",
-           "dion_version")
+EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_adamw_step",
+           "dion_lion_step", "dion_strerror", "dion_version")
 
 
 class DionError(RuntimeError):
@@ -68,6 +68,11 @@ def load() -> ctypes.CDLL:
                                       vp, ctypes.c_uint32, vp]
     lib.dion_step_batched_profiled.restype = ctypes.c_int
     lib.dion_step_batched_profiled.argtypes = lib.dion_step_batched.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+    f32, i32 = ctypes.c_float, ctypes.c_int
+    lib.dion_adamw_step.restype = ctypes.c_int
+    lib.dion_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, i32, i32, vp]
+    lib.dion_lion_step.restype = ctypes.c_int
+    lib.dion_lion_step.argtypes = [vp, vp, vp, i64, f32, f32, f32, f32, i32, i32, vp]
     lib.dion_strerror.restype = ctypes.c_char_p
     lib.dion_strerror.argtypes = [ctypes.c_int]
     lib.dion_version.restype = ctypes.c_int
@@ -102,3 +107,17 @@ def step_batched_raw(X: int, G: int, M: int, Q: int, m: int, n: int, batch: int,
         return int(load().dion_step_batched(*args))
     arr = (ctypes.c_void_p * (NUM_PHASES + 1))(*[int(e) for e in events])
     return int(load().dion_step_batched_profiled(*args, arr))
+
+
+def adamw_step_raw(param: int, grad: int, exp_avg: int, exp_avg_sq: int, n: int, t: int, lr: float, beta1: float,
+                   beta2: float, eps: float, weight_decay: float, p_dtype: int, g_dtype: int, stream: int) -> int:
+    """dion_adamw_step with integer addresses; returns the status code."""
+    return int(load().dion_adamw_step(param or None, grad or None, exp_avg or None, exp_avg_sq or None, n, t,
+                                      lr, beta1, beta2, eps, weight_decay, p_dtype, g_dtype, stream or None))
+
+
+def lion_step_raw(param: int, grad: int, exp_avg: int, n: int, lr: float, beta1: float, beta2: float,
+                  weight_decay: float, p_dtype: int, g_dtype: int, stream: int) -> int:
+    """dion_lion_step with integer addresses; returns the status code."""
+    return int(load().dion_lion_step(param or None, grad or None, exp_avg or None, n, lr, beta1, beta2,
+                                     weight_decay, p_dtype, g_dtype, stream or None))

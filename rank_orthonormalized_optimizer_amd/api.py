@@ -160,3 +160,94 @@ def group_matrices(params) -> "OrderedDict[tuple, list]":
             raise ValueError(f"parameter {i} has shape {tuple(p.shape)}: only 2-D matrices go to Dion")
         groups.setdefault((tuple(p.shape), p.dtype), []).append(p)
     return groups
+
+
+def _flat_check(t: torch.Tensor, name: str, n: int, dtypes) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.numel() != n or t.dtype not in dtypes:
+        raise ValueError(f"{name}: {t.numel()} elements of {t.dtype}, expected {n} of {dtypes}")
+
+
+def adamw_step_(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, t: int,
+                lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+                *, stream=None) -> None:
+    """One AdamW step (dion_adamw_step) on a contiguous tensor of any shape, in place; t counts from 1."""
+    n = param.numel()
+    _flat_check(param, "param", n, tuple(_DT))
+    _flat_check(grad, "grad", n, tuple(_DT))
+    _flat_check(exp_avg, "exp_avg", n, (torch.float32,))
+    _flat_check(exp_avg_sq, "exp_avg_sq", n, (torch.float32,))
+    if stream is None:
+        stream = torch.cuda.current_stream(param.device)
+    st = _lib.adamw_step_raw(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), n, int(t),
+                             float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                             _DT[param.dtype], _DT[grad.dtype], int(stream.cuda_stream))
+    if st != _lib.OK:
+        raise _lib.DionError(st, "dion_adamw_step")
+
+
+def lion_step_(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, lr: float, beta1: float = 0.9,
+               beta2: float = 0.99, weight_decay: float = 0.0, *, stream=None) -> None:
+    """One Lion step (dion_lion_step) on a contiguous tensor of any shape, in place."""
+    n = param.numel()
+    _flat_check(param, "param", n, tuple(_DT))
+    _flat_check(grad, "grad", n, tuple(_DT))
+    _flat_check(exp_avg, "exp_avg", n, (torch.float32,))
+    if stream is None:
+        stream = torch.cuda.current_stream(param.device)
+    st = _lib.lion_step_raw(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), n, float(lr), float(beta1),
+                            float(beta2), float(weight_decay), _DT[param.dtype], _DT[grad.dtype],
+                            int(stream.cuda_stream))
+    if st != _lib.OK:
+        raise _lib.DionError(st, "dion_lion_step")
+
+
+class MixedDion:
+    """Dion for the 2-D parameters, AdamW or Lion for the rest (rivista.ai, "Tecnicamente").
+
+    ``params``: a list of GPU tensors.  2-D ones are grouped by (shape, dtype) into stacks
+    (each step copies the group's weights and gradients into [b, m, n] stacks and back, since
+    torch parameters are separate tensors); every other tensor gets element-wise state.
+    ``step(grads)`` takes the gradients in the same order.
+    """
+
+    def __init__(self, params, *, lr: float = 0.01, mu: float = 0.95, rank_fraction: float = 0.25,
+                 other: str = "adamw", other_lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0):
+        if other not in ("adamw", "lion"):
+            raise ValueError("other must be 'adamw' or 'lion'")
+        self.params = list(params)
+        self.other, self.other_lr, self.betas, self.eps, self.wd = other, other_lr, betas, eps, weight_decay
+        self.t = 0
+        self.groups = []   # (indices, DionStack)
+        mats = OrderedDict()
+        for i, p in enumerate(self.params):
+            if p.dim() == 2:
+                mats.setdefault((tuple(p.shape), p.dtype), []).append(i)
+        for (shape, _), idx in mats.items():
+            st = DionStack(len(idx), shape[0], shape[1], rank_fraction=rank_fraction, mu=mu, lr=lr,
+                           device=self.params[idx[0]].device)
+            self.groups.append((idx, st))
+        self.rest = [i for i, p in enumerate(self.params) if p.dim() != 2]
+        self.state = {i: (torch.zeros(self.params[i].numel(), dtype=torch.float32, device=self.params[i].device),
+                          torch.zeros(self.params[i].numel(), dtype=torch.float32, device=self.params[i].device)
+                          if other == "adamw" else None) for i in self.rest}
+
+    @torch.no_grad()
+    def step(self, grads) -> None:
+        grads = list(grads)
+        self.t += 1
+        for idx, st in self.groups:
+            X = torch.stack([self.params[i] for i in idx]).contiguous()
+            G = torch.stack([grads[i] for i in idx]).contiguous()
+            st.step(X, G)
+            for k, i in enumerate(idx):
+                self.params[i].copy_(X[k])
+        for i in self.rest:
+            p, g = self.params[i], grads[i].contiguous()
+            m, v = self.state[i]
+            if self.other == "adamw":
+                adamw_step_(p, g, m, v, self.t, self.other_lr, self.betas[0], self.betas[1], self.eps, self.wd)
+            else:
+                lion_step_(p, g, m, self.other_lr, self.betas[0], self.betas[1], self.wd)

@@ -79,13 +79,58 @@ int dion_step_batched(void* X, const void* G, float* M, float* Q, int64_t m, int
                                       workspace_bytes, flags, options, stream, nullptr);
 }
 
+int dion_adamw_step(void* param, const void* grad, float* exp_avg, float* exp_avg_sq, int64_t n, int64_t t,
+                    float lr, float beta1, float beta2, float eps, float weight_decay, int p_dtype, int g_dtype,
+                    void* stream) {
+    if (n < 0 || n > ((int64_t)1 << 46)) return DION_ERR_SHAPE;
+    if (t < 1 || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !isfinite(lr) ||
+        !isfinite(weight_decay) || !isfinite(eps) || !(eps >= 0.0f))
+        return DION_ERR_HYPER;
+    if ((p_dtype != DION_F32 && p_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
+        return DION_ERR_DTYPE;
+    if (n == 0) return DION_OK;
+    if (!param || !grad || !exp_avg || !exp_avg_sq) return DION_ERR_NULL;
+    if (((uintptr_t)param | (uintptr_t)grad | (uintptr_t)exp_avg | (uintptr_t)exp_avg_sq) & 15u) return DION_ERR_ALIGN;
+    const double dn = (double)n;
+    const Range rs[4] = {span(param, dn * (p_dtype == DION_BF16 ? 2 : 4)), span(grad, dn * (g_dtype == DION_BF16 ? 2 : 4)),
+                         span(exp_avg, dn * 4), span(exp_avg_sq, dn * 4)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    const int e = dion::run_adamw(param, grad, exp_avg, exp_avg_sq, n, t, lr, beta1, beta2, eps, weight_decay,
+                                  p_dtype == DION_BF16, g_dtype == DION_BF16, stream);
+    return e ? DION_ERR_HIP - e : DION_OK;
+}
+
+int dion_lion_step(void* param, const void* grad, float* exp_avg, int64_t n, float lr, float beta1, float beta2,
+                   float weight_decay, int p_dtype, int g_dtype, void* stream) {
+    if (n < 0 || n > ((int64_t)1 << 46)) return DION_ERR_SHAPE;
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !isfinite(lr) ||
+        !isfinite(weight_decay))
+        return DION_ERR_HYPER;
+    if ((p_dtype != DION_F32 && p_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
+        return DION_ERR_DTYPE;
+    if (n == 0) return DION_OK;
+    if (!param || !grad || !exp_avg) return DION_ERR_NULL;
+    if (((uintptr_t)param | (uintptr_t)grad | (uintptr_t)exp_avg) & 15u) return DION_ERR_ALIGN;
+    const double dn = (double)n;
+    const Range rs[3] = {span(param, dn * (p_dtype == DION_BF16 ? 2 : 4)), span(grad, dn * (g_dtype == DION_BF16 ? 2 : 4)),
+                         span(exp_avg, dn * 4)};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    const int e = dion::run_lion(param, grad, exp_avg, n, lr, beta1, beta2, weight_decay, p_dtype == DION_BF16,
+                                 g_dtype == DION_BF16, stream);
+    return e ? DION_ERR_HIP - e : DION_OK;
+}
+
 const char* dion_strerror(int status) {
     switch (status) {
         case DION_OK: return "success";
         case DION_ERR_NULL: return "a required pointer is NULL";
         case DION_ERR_SHAPE: return "invalid shape (m, n >= 1, batch >= 0) or size overflow";
         case DION_ERR_RANK: return "rank outside [0, min(m, n)]";
-        case DION_ERR_HYPER: return "invalid hyper-parameter (mu in [0,1), finite lr, finite eps >= 0)";
+        case DION_ERR_HYPER: return "invalid hyper-parameter (mu, betas in [0,1), finite lr and decay, finite eps >= 0, step >= 1)";
         case DION_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
         case DION_ERR_OVERLAP: return "overlapping buffers";
         case DION_ERR_WORKSPACE: return "workspace smaller than dion_workspace_size()";

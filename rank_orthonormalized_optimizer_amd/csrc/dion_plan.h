@@ -129,4 +129,10 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
              float mu, float lr, float eps, int x_bf16, int g_bf16,
              char* ws, int32_t* flags, uint32_t options, void* stream, void* const* events);
 
+// Element-wise optimizers (arguments already validated).  Return a hipError_t value.
+int run_adamw(void* p, const void* g, float* m, float* v, int64_t n, int64_t t, float lr, float b1, float b2,
+              float eps, float wd, int p_bf16, int g_bf16, void* stream);
+int run_lion(void* p, const void* g, float* m, int64_t n, float lr, float b1, float b2, float wd, int p_bf16,
+             int g_bf16, void* stream);
+
 }  // namespace dion

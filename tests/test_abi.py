@@ -122,3 +122,55 @@ def test_group_matrices_rejects_1d():
     assert len(g[((4, 5), torch.float32)]) == 2
     with pytest.raises(ValueError, match="only 2-D"):
         dion.group_matrices([torch.zeros(4, 5), torch.zeros(5)])
+
+
+def adamw(**kw):
+    a = dict(param=BASE, grad=BASE + 64 * MB, exp_avg=BASE + 128 * MB, exp_avg_sq=BASE + 192 * MB, n=1000, t=1,
+             lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, p_dtype=0, g_dtype=0, stream=0)
+    a.update(kw)
+    return _lib.adamw_step_raw(**a)
+
+
+def lion(**kw):
+    a = dict(param=BASE, grad=BASE + 64 * MB, exp_avg=BASE + 128 * MB, n=1000, lr=1e-4, beta1=0.9, beta2=0.99,
+             weight_decay=0.0, p_dtype=0, g_dtype=0, stream=0)
+    a.update(kw)
+    return _lib.lion_step_raw(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), _lib.ERR_SHAPE),
+    (dict(t=0), _lib.ERR_HYPER),
+    (dict(beta1=1.0), _lib.ERR_HYPER),
+    (dict(beta2=-0.5), _lib.ERR_HYPER),
+    (dict(eps=-1.0), _lib.ERR_HYPER),
+    (dict(lr=float("inf")), _lib.ERR_HYPER),
+    (dict(weight_decay=float("nan")), _lib.ERR_HYPER),
+    (dict(p_dtype=3), _lib.ERR_DTYPE),
+    (dict(param=0), _lib.ERR_NULL),
+    (dict(exp_avg_sq=0), _lib.ERR_NULL),
+    (dict(grad=BASE + 64 * MB + 8), _lib.ERR_ALIGN),
+    (dict(grad=BASE + 2048), _lib.ERR_OVERLAP),
+    (dict(exp_avg_sq=BASE + 128 * MB + 1024), _lib.ERR_OVERLAP),
+])
+def test_adamw_invalid_calls_rejected_on_host(kw, status):
+    assert adamw(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), _lib.ERR_SHAPE),
+    (dict(beta1=-0.1), _lib.ERR_HYPER),
+    (dict(beta2=1.0), _lib.ERR_HYPER),
+    (dict(lr=float("nan")), _lib.ERR_HYPER),
+    (dict(g_dtype=7), _lib.ERR_DTYPE),
+    (dict(exp_avg=0), _lib.ERR_NULL),
+    (dict(param=BASE + 4), _lib.ERR_ALIGN),
+    (dict(exp_avg=BASE + 1024), _lib.ERR_OVERLAP),
+])
+def test_lion_invalid_calls_rejected_on_host(kw, status):
+    assert lion(**kw) == status
+
+
+def test_elementwise_empty_is_a_noop():
+    assert adamw(n=0, param=0, grad=0, exp_avg=0, exp_avg_sq=0) == _lib.OK
+    assert lion(n=0, param=0, grad=0, exp_avg=0) == _lib.OK
