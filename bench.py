@@ -126,6 +126,63 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             "s_per_step": step_s}
 
 
+EW_N = 64 << 20    # elements of the element-wise measurement (256 MiB per fp32 array)
+EW_BYTES = {"adamw": 28, "lion": 20}   # algorithmic bytes per fp32 element: reads p, g, m(, v); writes p, m(, v)
+
+
+def elementwise_block(dev, stream, iters: int = 20, cpu_s: float = 3.0, with_cpu: bool = True) -> dict:
+    """AdamW and Lion (the element-wise optimizers for the parameters Dion does not take) on one
+    fp32 array of EW_N elements resident in HBM: achieved GB/s against the 8 TB/s HBM peak,
+    timed with events on the launch stream, and the fp64 oracle on a bounded host sample."""
+    import numpy as np
+    import torch
+
+    import rank_orthonormalized_optimizer_amd as dion
+    gen = torch.Generator(device=dev).manual_seed(7)
+    p = (0.02 * torch.randn(EW_N, generator=gen, device=dev)).contiguous()
+    g = (1e-2 * torch.randn(EW_N, generator=gen, device=dev)).contiguous()
+    m = torch.zeros(EW_N, device=dev)
+    v = torch.zeros(EW_N, device=dev)
+    out = {"n": EW_N, "dtype": "f32", "data": "synthetic"}
+    runs = {"adamw": lambda t: dion.adamw_step_(p, g, m, v, t, 1e-3, 0.9, 0.999, 1e-8, 0.1, stream=stream),
+            "lion": lambda t: dion.lion_step_(p, g, m, 3e-4, 0.9, 0.99, 0.1, stream=stream)}
+    for name, run in runs.items():
+        for t in range(1, 4):
+            run(t)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for t in range(4, 4 + iters):
+            run(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        gbs = EW_BYTES[name] * EW_N / (ms * 1e-3) / 1e9
+        out[name] = {"ms_per_step": ms, "effective_GBps": gbs, "bytes_per_element": EW_BYTES[name],
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": gbs / HBM_PEAK_GBS}}
+    del p, g, m, v
+    if with_cpu:
+        from oracle.elementwise_oracle import adamw_step, lion_step
+        k = 1 << 22
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([7, k])))
+        hp, hg = 0.02 * rng.standard_normal(k), 1e-2 * rng.standard_normal(k)
+        hm, hv = np.zeros(k), np.zeros(k)
+        for name in ("adamw", "lion"):
+            reps, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < cpu_s / 2:
+                if name == "adamw":
+                    adamw_step(hp, hg, hm, hv, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1)
+                else:
+                    lion_step(hp, hg, hm, 3e-4, 0.9, 0.99, 0.1)
+                reps += 1
+            per_elem = (time.perf_counter() - t0) / (reps * k)
+            out[name]["cpu_baseline"] = {"value": EW_BYTES[name] / per_elem / 1e9, "unit": "GB/s", "cores": 1,
+                                         "kind": "oracle",
+                                         "sample": f"{reps} steps of {k} elements (fp64 numpy, one thread)"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +195,10 @@ def main() -> int:
                     help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
     ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-elementwise", action="store_true",
+                    help="skip the AdamW / Lion measurement (the parameters Dion does not take)")
+    ap.add_argument("--elementwise-only", action="store_true",
+                    help="only the AdamW / Lion measurement, printed as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -157,6 +218,10 @@ def main() -> int:
     from rank_orthonormalized_optimizer_amd.api import workspace_for
 
     dev = torch.device("cuda:0")
+    if args.elementwise_only:
+        print(json.dumps(elementwise_block(dev, torch.cuda.current_stream(dev), with_cpu=not args.no_cpu_baseline)),
+              flush=True)
+        return 0
     wl = W.get(args.workload)
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
 
@@ -296,6 +361,9 @@ def main() -> int:
                      "mfma_flops_per_algorithmic_flop": factor,
                      "traffic": measured_traffic(wl.name, dom), "traffic_unit": "bytes/launch"},
     }
+    if not args.no_elementwise:
+        print("[bench] element-wise AdamW / Lion", file=sys.stderr, flush=True)
+        out["elementwise"] = elementwise_block(dev, stream, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
