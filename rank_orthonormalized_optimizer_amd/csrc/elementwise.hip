@@ -8,9 +8,12 @@
 // parameter is rounded to nearest-even once per step).
 //
 // Both passes are HBM-bound streams (AdamW reads 16 bytes and writes 12 per fp32 element, Lion
-// 12 and 8): grid-stride loops over groups of four elements with 16-byte accesses (8-byte for
-// bf16), a scalar loop for the tail, and enough workgroups to keep every CU's memory pipeline
-// busy.
+// 12 and 8): one group of four elements per thread with 16-byte accesses (8-byte for bf16), a
+// grid that covers the whole array (grid-stride only past 2^22 workgroups), and a scalar loop for
+// the tail.  Every access but the parameter's load is non-temporal: the gradient and the moments
+// are touched once per step.  On 64 Mi-element fp32 arrays the covering grid measured about 20%
+// faster than a grid-stride loop over 4096 workgroups, and the non-temporal accesses about 25%
+// more, where a non-temporal parameter load was slower.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -29,23 +32,42 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {   // round to nearest
     return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool BF16>
-struct Vec4 {   // four consecutive elements of an fp32 or bf16 array
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float* p) {
+    if constexpr (NT) {
+        const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)p);
+        return float4{v[0], v[1], v[2], v[3]};
+    } else {
+        return *(const float4*)p;
+    }
+}
+__device__ __forceinline__ void store4_nt(float* p, float4 v) {
+    __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, (f32x4_t*)p);
+}
+
+template <bool BF16, bool NT>
+struct Vec4 {   // four consecutive elements of an fp32 or bf16 array; NT loads stream past the caches
     static __device__ __forceinline__ float4 load(const void* p, int64_t i) {
         if constexpr (BF16) {
-            const uint2 w = *(const uint2*)((const uint16_t*)p + i);
-            return float4{bf16_to_f32((uint16_t)w.x), bf16_to_f32((uint16_t)(w.x >> 16)), bf16_to_f32((uint16_t)w.y),
-                          bf16_to_f32((uint16_t)(w.y >> 16))};
+            u32x2_t w;
+            if constexpr (NT) w = __builtin_nontemporal_load((const u32x2_t*)((const uint16_t*)p + i));
+            else w = *(const u32x2_t*)((const uint16_t*)p + i);
+            return float4{bf16_to_f32((uint16_t)w[0]), bf16_to_f32((uint16_t)(w[0] >> 16)), bf16_to_f32((uint16_t)w[1]),
+                          bf16_to_f32((uint16_t)(w[1] >> 16))};
         } else {
-            return *(const float4*)((const float*)p + i);
+            return load4<NT>((const float*)p + i);
         }
     }
-    static __device__ __forceinline__ void store(void* p, int64_t i, float4 v) {
+    static __device__ __forceinline__ void store(void* p, int64_t i, float4 v) {   // always non-temporal
         if constexpr (BF16) {
-            *(uint2*)((uint16_t*)p + i) = uint2{(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                                                (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+            const u32x2_t w{(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                            (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+            __builtin_nontemporal_store(w, (u32x2_t*)((uint16_t*)p + i));
         } else {
-            *(float4*)((float*)p + i) = v;
+            store4_nt((float*)p + i, v);
         }
     }
     static __device__ __forceinline__ float load1(const void* p, int64_t i) {
@@ -78,18 +100,18 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamWArgs a) {
     const int64_t nv = a.n / 4, stride = (int64_t)gridDim.x * 256;
     for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nv; q += stride) {
         const int64_t i = 4 * q;
-        const float4 th = Vec4<P_BF16>::load(a.p, i), g = Vec4<G_BF16>::load(a.g, i);
-        float4 m = *(const float4*)(a.m + i), v = *(const float4*)(a.v + i);
+        const float4 th = Vec4<P_BF16, false>::load(a.p, i), g = Vec4<G_BF16, true>::load(a.g, i);
+        float4 m = load4<true>(a.m + i), v = load4<true>(a.v + i);
         const float4 out{adamw1(th.x, g.x, m.x, v.x, a), adamw1(th.y, g.y, m.y, v.y, a),
                          adamw1(th.z, g.z, m.z, v.z, a), adamw1(th.w, g.w, m.w, v.w, a)};
-        Vec4<P_BF16>::store(a.p, i, out);
-        *(float4*)(a.m + i) = m;
-        *(float4*)(a.v + i) = v;
+        Vec4<P_BF16, false>::store(a.p, i, out);
+        store4_nt(a.m + i, m);
+        store4_nt(a.v + i, v);
     }
     for (int64_t i = 4 * nv + (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += stride) {
         float m = a.m[i], v = a.v[i];
-        const float out = adamw1(Vec4<P_BF16>::load1(a.p, i), Vec4<G_BF16>::load1(a.g, i), m, v, a);
-        Vec4<P_BF16>::store1(a.p, i, out);
+        const float out = adamw1(Vec4<P_BF16, false>::load1(a.p, i), Vec4<G_BF16, false>::load1(a.g, i), m, v, a);
+        Vec4<P_BF16, false>::store1(a.p, i, out);
         a.m[i] = m;
         a.v[i] = v;
     }
@@ -114,25 +136,25 @@ __global__ __launch_bounds__(256) void lion_kernel(LionArgs a) {
     const int64_t nv = a.n / 4, stride = (int64_t)gridDim.x * 256;
     for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nv; q += stride) {
         const int64_t i = 4 * q;
-        const float4 th = Vec4<P_BF16>::load(a.p, i), g = Vec4<G_BF16>::load(a.g, i);
-        float4 m = *(const float4*)(a.m + i);
+        const float4 th = Vec4<P_BF16, false>::load(a.p, i), g = Vec4<G_BF16, true>::load(a.g, i);
+        float4 m = load4<true>(a.m + i);
         const float4 out{lion1(th.x, g.x, m.x, a), lion1(th.y, g.y, m.y, a), lion1(th.z, g.z, m.z, a),
                          lion1(th.w, g.w, m.w, a)};
-        Vec4<P_BF16>::store(a.p, i, out);
-        *(float4*)(a.m + i) = m;
+        Vec4<P_BF16, false>::store(a.p, i, out);
+        store4_nt(a.m + i, m);
     }
     for (int64_t i = 4 * nv + (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += stride) {
         float m = a.m[i];
-        const float out = lion1(Vec4<P_BF16>::load1(a.p, i), Vec4<G_BF16>::load1(a.g, i), m, a);
-        Vec4<P_BF16>::store1(a.p, i, out);
+        const float out = lion1(Vec4<P_BF16, false>::load1(a.p, i), Vec4<G_BF16, false>::load1(a.g, i), m, a);
+        Vec4<P_BF16, false>::store1(a.p, i, out);
         a.m[i] = m;
     }
 }
 
-// about four resident workgroups of 256 per CU over the 256 CUs, fewer for short arrays
+// one group of four elements per thread; past 2^22 workgroups (2^32 elements) the loops stride
 unsigned stream_grid(int64_t n) {
     const int64_t groups = (n / 4 + 255) / 256;
-    const int64_t cap = 256 * 4 * 4;
+    const int64_t cap = (int64_t)1 << 22;
     return (unsigned)(groups < 1 ? 1 : (groups < cap ? groups : cap));
 }
 
