@@ -183,6 +183,65 @@ def elementwise_block(dev, stream, iters: int = 20, cpu_s: float = 3.0, with_cpu
     return out
 
 
+SPECTRAL_CASES = ((24, 256), (8, 4096))   # (matrices, r): the Gram shapes of the attention and full-rank stacks
+SPECTRAL_K, SPECTRAL_ITERS = 32, 10
+
+
+def spectral_block(dev, stream, reps: int = 10, with_cpu: bool = True) -> dict:
+    """The multi-power-iteration lambda_max estimate (dion_lambda_max_batched) on fp64 Gram
+    stacks A^T A resident in HBM, 32 start vectors, 10 normalized products.  The product kernel
+    is priced against the fp64 vector peak: 2 r^2 k flops per matrix and product, its time the
+    difference between calls with 10 and with 0 iterations (10 more product launches), measured
+    with events on the launch stream.  The fp64 oracle runs on one matrix of each stack."""
+    import numpy as np
+    import torch
+
+    import rank_orthonormalized_optimizer_amd as dion
+    out = {"k": SPECTRAL_K, "iters": SPECTRAL_ITERS, "dtype": "f64", "data": "synthetic", "cases": []}
+    for b, r in SPECTRAL_CASES:
+        gen = torch.Generator(device=dev).manual_seed(41 + r)
+        A = torch.randn(b, r + 8, r, generator=gen, device=dev, dtype=torch.float64)
+        Wm = torch.matmul(A.transpose(1, 2).contiguous(), A).contiguous()   # input preparation only
+        del A
+        lam = torch.empty(b, dtype=torch.float64, device=dev)
+
+        def timed(iters):
+            for _ in range(2):
+                dion.lambda_max_(Wm, k=SPECTRAL_K, iters=iters, out=lam, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                dion.lambda_max_(Wm, k=SPECTRAL_K, iters=iters, out=lam, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms_full, ms_zero = timed(SPECTRAL_ITERS), timed(0)
+        prod_ms = max(ms_full - ms_zero, 0.0) / SPECTRAL_ITERS
+        flops = 2.0 * r * r * SPECTRAL_K * b
+        tf = flops / (prod_ms * 1e-3) / 1e12 if prod_ms > 0 else 0.0
+        case = {"workload": f"{b}x{r}x{r} Gram stack", "ms_per_call": ms_full,
+                "calls_per_s": 1e3 / ms_full, "product_launch_ms": prod_ms,
+                "roofline": {"bound": "alu", "kernel": "mpi_product_kernel", "achieved": tf,
+                             "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s", "frac": tf / PEAK_TFLOPS["f64"],
+                             "flops_per_launch": flops}}
+        if with_cpu:
+            from oracle.spectral_oracle import lambda_max_estimate
+            import workloads as W
+            w0 = Wm[0].cpu().numpy()
+            v0 = W.splitmix_start_vectors(1, r, SPECTRAL_K)[0]
+            t0 = time.perf_counter()
+            lambda_max_estimate(w0, v0, SPECTRAL_ITERS)
+            sec = time.perf_counter() - t0
+            case["cpu_baseline"] = {"value": 1.0 / (sec * b), "unit": "calls/s", "cores": blas_threads(),
+                                    "kind": "oracle",
+                                    "sample": f"one {r}x{r} matrix of the stack (fp64 numpy), time x {b}"}
+        out["cases"].append(case)
+        del Wm
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +258,10 @@ def main() -> int:
                     help="skip the AdamW / Lion measurement (the parameters Dion does not take)")
     ap.add_argument("--elementwise-only", action="store_true",
                     help="only the AdamW / Lion measurement, printed as one JSON line")
+    ap.add_argument("--no-spectral", action="store_true",
+                    help="skip the lambda_max estimate measurement (the spectral shift of the fallback)")
+    ap.add_argument("--spectral-only", action="store_true",
+                    help="only the lambda_max estimate measurement, printed as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -218,6 +281,10 @@ def main() -> int:
     from rank_orthonormalized_optimizer_amd.api import workspace_for
 
     dev = torch.device("cuda:0")
+    if args.spectral_only:
+        print(json.dumps(spectral_block(dev, torch.cuda.current_stream(dev), with_cpu=not args.no_cpu_baseline)),
+              flush=True)
+        return 0
     if args.elementwise_only:
         print(json.dumps(elementwise_block(dev, torch.cuda.current_stream(dev), with_cpu=not args.no_cpu_baseline)),
               flush=True)
@@ -364,6 +431,9 @@ def main() -> int:
     if not args.no_elementwise:
         print("[bench] element-wise AdamW / Lion", file=sys.stderr, flush=True)
         out["elementwise"] = elementwise_block(dev, stream, with_cpu=not args.no_cpu_baseline)
+    if not args.no_spectral:
+        print("[bench] multi-power-iteration lambda_max estimate", file=sys.stderr, flush=True)
+        out["spectral"] = spectral_block(dev, stream, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -101,6 +101,13 @@ enum {
                                  QR instead of CholeskyQR (with DION_OPT_FORCE_F64: every
                                  matrix); not with DION_OPT_FORCE_F32, rank <= 4096.  The
                                  Householder QR runs one workgroup per matrix: it is slow */
+    DION_OPT_SPECTRAL_SHIFT = 32, /* the shifted first pass of the fp64 chain takes its shift from
+                                 a multi-power-iteration estimate of lambda_max(P0^T P0) (32
+                                 start vectors, 10 normalized products; see
+                                 dion_lambda_max_batched) instead of from trace(P0^T P0), which
+                                 exceeds it by up to the rank.  Adds 13 launches to the fp64
+                                 chain, which return at once for the matrices not shifted; not
+                                 with DION_OPT_FORCE_F32 */
     DION_OPT_CHUNKS_SHIFT = 8 /* bits 8..11: number of concurrent chunks the stack is split into
                                  (0 = automatic, 1 = everything on `stream`); see Execution */
 };
@@ -205,6 +212,42 @@ int dion_adamw_step(void* param, const void* grad, float* exp_avg, float* exp_av
 int dion_lion_step(void* param, const void* grad, float* exp_avg, int64_t n,
                    float lr, float beta1, float beta2, float weight_decay,
                    int p_dtype, int g_dtype, void* stream);
+
+/*
+ * Multi-power-iteration estimate of the largest eigenvalue of a stack of
+ * symmetric positive semi-definite matrices, such as the Gram matrices P0^T P0 of
+ * the step.  The DASH summary (gist.science, "Methodologie", 2. "Efficiënte
+ * Inverse-Root Solvers", the item on multi-power-iteration scaling) estimates the
+ * spectral radius by power iteration run in parallel from a pool of up to 32 start
+ * vectors, in place of the Frobenius-norm scale.  Per matrix W:
+ *
+ *   each pool vector v, `iters` times:  v <- W v / ||W v||
+ *   lambda = max over the pool of v^T W v / v^T v     (0 for a vector W maps to 0)
+ *
+ * The estimate never exceeds lambda_max(W) (up to rounding) and converges to it as
+ * (lambda_2 / lambda_1)^(2 iters) for start vectors not orthogonal to its
+ * eigenvector.  fp64 throughout.
+ *
+ *   W        device fp64 [batch][r][r], row-major; only the lower triangle (j <= i) is
+ *            read, so the upper one may hold anything
+ *   V0       device fp64 [batch][r][k], row-major (the k start vectors of a matrix side
+ *            by side), or NULL: the library's start vectors, 2u - 1 with u the top 53
+ *            bits of output number b*r*k + i*k + j + 1 of SplitMix64 seeded with 0 for
+ *            entry (i, j) of matrix b
+ *   k        pool size, 1..32;   iters  normalized products before the quotient, 0..64
+ *   lambda   device fp64 [batch], written
+ *   workspace  device, >= dion_lambda_max_workspace_size(r, batch, k) bytes,
+ *            256-byte aligned, caller-owned scratch (contents on entry ignored)
+ *   r >= 1, 0 <= batch <= 65535 (0 is a no-op)
+ * W, V0 and lambda 8-byte aligned; lambda and workspace overlap nothing.
+ * Asynchronous on `stream` (NULL = default stream): iters + 3 launches, no
+ * allocation, no host synchronization.  Returns DION_OK or a negative status
+ * (DION_ERR_SHAPE for r, batch or k, DION_ERR_HYPER for iters), checked on the host
+ * before anything is enqueued.
+ */
+size_t dion_lambda_max_workspace_size(int64_t r, int64_t batch, int32_t k);
+int dion_lambda_max_batched(const double* W, int64_t r, int64_t batch, const double* V0, int32_t k, int32_t iters,
+                            double* lambda, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* dion_strerror(int status);

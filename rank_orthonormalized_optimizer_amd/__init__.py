@@ -14,7 +14,8 @@ element-wise AdamW or Lion, as the page describes.
 from __future__ import annotations
 
 from ._lib import (BF16, EXPORTS, F32, FLAG_F64, FLAG_HOUSEHOLDER, FLAG_NONFINITE, FLAG_SHIFTED,  # noqa: F401
-                   OPT_FORCE_F32, OPT_FORCE_F64, OPT_HOUSEHOLDER, OPT_STICKY_F64, DionError, adamw_step_raw,
-                   lion_step_raw, load, step_batched_raw, strerror, version, workspace_size)
-from .api import (DionStack, MixedDion, StickyF64Hint, adamw_step_, group_matrices, lion_step_,  # noqa: F401
-                  step_)
+                   OPT_FORCE_F32, OPT_FORCE_F64, OPT_HOUSEHOLDER, OPT_SPECTRAL_SHIFT, OPT_STICKY_F64, DionError,
+                   adamw_step_raw, lambda_max_raw, lambda_max_workspace_size, lion_step_raw, load,
+                   step_batched_raw, strerror, version, workspace_size)
+from .api import (DionStack, MixedDion, StickyF64Hint, adamw_step_, group_matrices, lambda_max_,  # noqa: F401
+                  lion_step_, step_)

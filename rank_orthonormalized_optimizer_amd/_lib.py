@@ -23,7 +23,7 @@ F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_HYPER, ERR_ALIGN = -1, -2, -3, -4, -5
 ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_HIP = -6, -7, -8, -9, -100
-OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32, OPT_HOUSEHOLDER = 1, 2, 4, 16
+OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32, OPT_HOUSEHOLDER, OPT_SPECTRAL_SHIFT = 1, 2, 4, 16, 32
 OPT_CHUNKS_SHIFT = 8
 
 
@@ -37,7 +37,8 @@ PHASES = ("init", "f32_product", "f32_qr", "f32_backproject", "f64_product", "f6
           "norms", "update", "flags")
 
 EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_adamw_step",
-           "dion_lion_step", "dion_strerror", "dion_version")
+           "dion_lion_step", "dion_lambda_max_workspace_size", "dion_lambda_max_batched", "dion_strerror",
+           "dion_version")
 
 
 class DionError(RuntimeError):
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
     lib.dion_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, i32, i32, vp]
     lib.dion_lion_step.restype = ctypes.c_int
     lib.dion_lion_step.argtypes = [vp, vp, vp, i64, f32, f32, f32, f32, i32, i32, vp]
+    lib.dion_lambda_max_workspace_size.restype = ctypes.c_size_t
+    lib.dion_lambda_max_workspace_size.argtypes = [i64, i64, i32]
+    lib.dion_lambda_max_batched.restype = ctypes.c_int
+    lib.dion_lambda_max_batched.argtypes = [vp, i64, i64, vp, i32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.dion_strerror.restype = ctypes.c_char_p
     lib.dion_strerror.argtypes = [ctypes.c_int]
     lib.dion_version.restype = ctypes.c_int
@@ -121,3 +126,14 @@ def lion_step_raw(param: int, grad: int, exp_avg: int, n: int, lr: float, beta1:
     """dion_lion_step with integer addresses; returns the status code."""
     return int(load().dion_lion_step(param or None, grad or None, exp_avg or None, n, lr, beta1, beta2,
                                      weight_decay, p_dtype, g_dtype, stream or None))
+
+
+def lambda_max_workspace_size(r: int, batch: int, k: int) -> int:
+    return int(load().dion_lambda_max_workspace_size(r, batch, k))
+
+
+def lambda_max_raw(W: int, r: int, batch: int, V0: int, k: int, iters: int, lam: int, workspace: int,
+                   workspace_bytes: int, stream: int) -> int:
+    """dion_lambda_max_batched with integer addresses; returns the status code."""
+    return int(load().dion_lambda_max_batched(W or None, r, batch, V0 or None, k, iters, lam or None,
+                                              workspace or None, workspace_bytes, stream or None))

@@ -187,6 +187,33 @@ def adamw_step_(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, 
         raise _lib.DionError(st, "dion_adamw_step")
 
 
+def lambda_max_(W: torch.Tensor, k: int = 32, iters: int = 10, V0: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    """Multi-power-iteration estimate of lambda_max for each symmetric PSD matrix of the fp64
+    stack W [b, r, r] (dion_lambda_max_batched; only the lower triangle is read).  V0 [b, r, k]
+    fp64 or None for the library's start vectors.  Returns (or fills) fp64 [b] on W's device."""
+    if not isinstance(W, torch.Tensor) or W.device.type != "cuda" or W.dtype != torch.float64 or W.dim() != 3 \
+            or W.shape[1] != W.shape[2] or not W.is_contiguous():
+        raise ValueError("W must be a contiguous fp64 GPU tensor [b, r, r]")
+    b, r = int(W.shape[0]), int(W.shape[1])
+    if V0 is not None:
+        if V0.dtype != torch.float64 or tuple(V0.shape) != (b, r, k) or not V0.is_contiguous() or V0.device != W.device:
+            raise ValueError(f"V0 must be a contiguous fp64 tensor [{b}, {r}, {k}] on W's device")
+    if out is None:
+        out = torch.empty(b, dtype=torch.float64, device=W.device)
+    elif out.dtype != torch.float64 or out.numel() != b or not out.is_contiguous() or out.device != W.device:
+        raise ValueError("out must be a contiguous fp64 tensor of b elements on W's device")
+    nbytes = _lib.lambda_max_workspace_size(r, b, k)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(W.device)
+    st = _lib.lambda_max_raw(W.data_ptr(), r, b, 0 if V0 is None else V0.data_ptr(), int(k), int(iters),
+                             out.data_ptr(), ws.data_ptr(), nbytes, int(stream.cuda_stream))
+    if st != _lib.OK:
+        raise _lib.DionError(st, "dion_lambda_max_batched")
+    return out
+
+
 def lion_step_(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, lr: float, beta1: float = 0.9,
                beta2: float = 0.99, weight_decay: float = 0.0, *, stream=None) -> None:
     """One Lion step (dion_lion_step) on a contiguous tensor of any shape, in place."""

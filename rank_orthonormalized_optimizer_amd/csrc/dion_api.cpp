@@ -44,9 +44,10 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64
     if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
         return DION_ERR_DTYPE;
     const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 | DION_OPT_HOUSEHOLDER |
-                           (15u << DION_OPT_CHUNKS_SHIFT);
+                           DION_OPT_SPECTRAL_SHIFT | (15u << DION_OPT_CHUNKS_SHIFT);
     if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)) ||
-        ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)))
+        ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)) ||
+        ((options & DION_OPT_SPECTRAL_SHIFT) && (options & DION_OPT_FORCE_F32)))
         return DION_ERR_OPTION;
     dion::Plan p;
     if (!dion::make_plan(m, n, batch, rank, &p)) return DION_ERR_SHAPE;
@@ -124,14 +125,45 @@ int dion_lion_step(void* param, const void* grad, float* exp_avg, int64_t n, flo
     return e ? DION_ERR_HIP - e : DION_OK;
 }
 
+size_t dion_lambda_max_workspace_size(int64_t r, int64_t batch, int32_t k) {
+    if (r < 1 || r > ((int64_t)1 << 24) || batch < 0 || batch > 65535 || k < 1 || k > dion::kMpiMaxPool) return 0;
+    return (size_t)batch * (size_t)(2 * r * k + 2) * sizeof(double);
+}
+
+int dion_lambda_max_batched(const double* W, int64_t r, int64_t batch, const double* V0, int32_t k, int32_t iters,
+                            double* lambda, void* workspace, size_t workspace_bytes, void* stream) {
+    if (r < 1 || r > ((int64_t)1 << 24) || batch < 0 || batch > 65535 || k < 1 || k > dion::kMpiMaxPool ||
+        (double)r * (double)r * (double)batch > 1.0e15)
+        return DION_ERR_SHAPE;
+    if (iters < 0 || iters > dion::kMpiMaxIters) return DION_ERR_HYPER;
+    if (batch == 0) return DION_OK;
+    if (!W || !lambda || !workspace) return DION_ERR_NULL;
+    if ((((uintptr_t)W | (uintptr_t)V0 | (uintptr_t)lambda) & 7u) || ((uintptr_t)workspace & 255u)) return DION_ERR_ALIGN;
+    const size_t need = dion_lambda_max_workspace_size(r, batch, k);
+    if (workspace_bytes < need) return DION_ERR_WORKSPACE;
+    const double b = (double)batch;
+    const Range rs[4] = {span(lambda, b * 8), span(workspace, (double)need), span(W, b * r * r * 8),
+                         span(V0, V0 ? b * r * k * 8 : 0.0)};
+    for (int i = 0; i < 2; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    dion::MpiArgs a{};
+    a.W = W; a.r = r; a.k = k; a.V0 = V0;
+    a.ws = (double*)workspace; a.ws_stride = 2 * r * k + 2;
+    a.lam = lambda; a.lam_stride = 1;
+    a.st = nullptr;
+    const int e = dion::run_lambda_max(a, batch, iters, stream);
+    return e ? DION_ERR_HIP - e : DION_OK;
+}
+
 const char* dion_strerror(int status) {
     switch (status) {
         case DION_OK: return "success";
         case DION_ERR_NULL: return "a required pointer is NULL";
         case DION_ERR_SHAPE: return "invalid shape (m, n >= 1, batch >= 0) or size overflow";
         case DION_ERR_RANK: return "rank outside [0, min(m, n)]";
-        case DION_ERR_HYPER: return "invalid hyper-parameter (mu, betas in [0,1), finite lr and decay, finite eps >= 0, step >= 1)";
-        case DION_ERR_ALIGN: return "misaligned pointer (16 bytes; workspace 256 bytes)";
+        case DION_ERR_HYPER: return "invalid hyper-parameter (mu, betas in [0,1), finite lr and decay, finite eps >= 0, step >= 1, iterations 0..64)";
+        case DION_ERR_ALIGN: return "misaligned pointer (16 bytes, 8 for fp64 arrays; workspace 256 bytes)";
         case DION_ERR_OVERLAP: return "overlapping buffers";
         case DION_ERR_WORKSPACE: return "workspace smaller than dion_workspace_size()";
         case DION_ERR_DTYPE: return "unsupported dtype (DION_F32 or DION_BF16)";

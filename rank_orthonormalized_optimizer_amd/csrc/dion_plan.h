@@ -24,6 +24,13 @@ enum : int {
 // Partial sums of squares per matrix written by the near-identity test (fixed-order reduction).
 constexpr int kNearIdParts = 256;
 
+// Multi-power-iteration estimate of the largest eigenvalue: pool size limit, and the pool size and
+// iteration count the step uses for the shift of its shifted CholeskyQR pass.
+constexpr int kMpiMaxPool = 32;
+constexpr int kMpiMaxIters = 64;
+constexpr int kShiftPool = 32;
+constexpr int kShiftIters = 10;
+
 struct Plan {
     int64_t m, n, b, r;
     int64_t nblk;      // number of rank column blocks
@@ -32,10 +39,10 @@ struct Plan {
     int64_t gsplit6;   // K-splits of the fp32 Gram products (split-bf16 kernel, 128 x 128 tiles)
     int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
     // byte offsets into the workspace (all 256-byte aligned)
-    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart;
+    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw;
     size_t total;
     // bytes per matrix of each region (a region is [batch][...] and contiguous)
-    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart;
+    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, spw;
 };
 
 // The sub-plan of matrices [c0, c0 + cb): same sizes, region offsets advanced to matrix c0.
@@ -46,6 +53,7 @@ inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
     q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart; q.gpart += c * p.sgpart;
+    q.pw += c * p.spw;
     return q;
 }
 
@@ -114,12 +122,15 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     const double gp32 = q.gsplit6 > 1 ? (double)q.gsplit6 * r * r * 4 : 0.0;
     const double gpm = gp64 > gp32 ? gp64 : gp32;
     q.gpart = take(B * gpm);               // Gram partials (either chain)
+    const double pw = (2.0 * r * kShiftPool + 2) * 8;
+    q.pw = take(B * pw);                   // spectral-shift pool: two r x 32 fp64 buffers, trace, estimate
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
     q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = kNearIdParts * 8;
     q.sW = q.sL = q.sTf = (size_t)(r * r * 8); q.sTd = (size_t)(q.nblk * kNB * kNB * 8);
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
     q.sgpart = (size_t)gpm;
+    q.spw = (size_t)pw;
     *p = q;
     return true;
 }
@@ -128,6 +139,26 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
 int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
              float mu, float lr, float eps, int x_bf16, int g_bf16,
              char* ws, int32_t* flags, uint32_t options, void* stream, void* const* events);
+
+// Multi-power-iteration estimate of lambda_max for a stack of symmetric PSD matrices (only the
+// lower triangle of W is read).  Per matrix bz: pool and trace in ws + bz * ws_stride (doubles:
+// two r x k buffers, then the trace), the estimate written to lam[bz * lam_stride].  V0 is
+// [b][r][k] or null (SplitMix64 start vectors); st null runs every matrix, else only those with
+// (st[bz] & st_mask) == st_val.
+struct MpiArgs {
+    const double* W;
+    int64_t r;
+    int k;
+    const double* V0;
+    double* ws;
+    int64_t ws_stride;
+    double* lam;
+    int64_t lam_stride;
+    const int* st;
+    int st_mask, st_val;
+};
+// Enqueues 1 + (iters + 1) + 1 launches; returns a hipError_t value.
+int run_lambda_max(const MpiArgs& a, int64_t b, int iters, void* stream);
 
 // Element-wise optimizers (arguments already validated).  Return a hipError_t value.
 int run_adamw(void* p, const void* g, float* m, float* v, int64_t n, int64_t t, float lr, float b1, float b2,

@@ -496,16 +496,20 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(PotrfArgs p) {
     diag_block<T>(p, bz, sm);
 }
 
-// L = W (+ s I), s = c_shift * trace(W) when shifting.
+// L = W (+ s I) when shifting: s = c_shift * lam[bz * lam_stride] (an estimate of lambda_max(W))
+// if lam is set, else s = c_shift * trace(W).
 template <typename T>
 __global__ __launch_bounds__(256) void copy_shift_kernel(const T* W, T* L, int64_t r, const int* st, int st_mask,
-                                                         int st_val, int shift, double c_shift) {
+                                                         int st_val, int shift, double c_shift, const double* lam,
+                                                         int64_t lam_stride) {
     const int bz = blockIdx.y;
     if ((st[bz] & st_mask) != st_val) return;
     W += bz * r * r;
     L += bz * r * r;
     T sv = 0;
-    if (shift) {
+    if (shift && lam) {
+        sv = (T)(c_shift * lam[bz * lam_stride]);
+    } else if (shift) {
         __shared__ double red[256];
         double tr = 0;
         for (int64_t i = threadIdx.x; i < r; i += 256) tr += (double)W[i * r + i];
@@ -1066,6 +1070,10 @@ struct ChainCtx {
     hipStream_t s;
     hipEvent_t gate = nullptr;   // recorded once, after the chunk's first product (staggered chunks)
     bool* gated = nullptr;
+    // shifted passes: s = c_shift * lam[b * lam_stride] (the multi-power-iteration estimate of
+    // lambda_max(W)) when set, else s = c_shift * trace(W)
+    const double* lam = nullptr;
+    int64_t lam_stride = 0;
     hipError_t open_gate() const {
         if (!gate || *gated) return hipSuccess;
         *gated = true;
@@ -1187,7 +1195,8 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
         const double c_shift = 11.0 * ((double)m * r + (double)r * (r + 1)) * u;
         dim3 grid(grid_1d(r * r, 1024), (unsigned)b);
-        hipLaunchKernelGGL((copy_shift_kernel<T>), grid, dim3(256), 0, c.s, W, L, r, c.st, mask, val, shift, c_shift);
+        hipLaunchKernelGGL((copy_shift_kernel<T>), grid, dim3(256), 0, c.s, W, L, r, c.st, mask, val, shift, c_shift,
+                           c.lam, c.lam_stride);
         DION_TRY(hipGetLastError());
     }
     for (int64_t jb = 0; jb < p.nblk; ++jb) {
@@ -1358,6 +1367,8 @@ struct CholInvArgs {
     double tau;
     int fail_bit, tau_bit, shift;
     double c_shift;
+    const double* lam;   // shift estimate per matrix (lam[bz * lam_stride]), or null: trace(W)
+    int64_t lam_stride;
     // second-pass use: the near-identity partial sums of ||P^T P - I||_F^2 ([b][kNearIdParts],
     // nparts used); a matrix whose norm is <= ntau keeps its first-order T and returns
     const double* npart;
@@ -1468,9 +1479,11 @@ __global__ __launch_bounds__(256) void cholinv_kernel(CholInvArgs a) {
     T* Y = (T*)a.Y + bz * rr;
     T* Td = (T*)a.Td + bz * nblk * kNB * kNB;
     const bool vr = (r % 4) == 0;
-    // L = W (+ s I), s = c_shift trace(W)
+    // L = W (+ s I), s = c_shift lambda_hat (the estimate, when given) or c_shift trace(W)
     T sv = T(0);
-    if (a.shift) {
+    if (a.shift && a.lam) {
+        sv = (T)(a.c_shift * a.lam[bz * a.lam_stride]);
+    } else if (a.shift) {
         double tr = 0;
         for (int64_t i = threadIdx.x; i < r; i += 256) tr += (double)W[i * r + i];
         red[threadIdx.x] = tr;
@@ -1614,6 +1627,7 @@ static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int f
     a.tau = tau; a.fail_bit = fail_bit; a.tau_bit = tau_bit; a.shift = shift;
     const double u = sizeof(T) == 8 ? 1.1102230246251565e-16 : 5.9604644775390625e-08;
     a.c_shift = 11.0 * ((double)p.m * p.r + (double)p.r * (p.r + 1)) * u;
+    a.lam = c.lam; a.lam_stride = c.lam_stride;
     a.npart = npart; a.nparts = nparts; a.ntau = ntau;
     hipLaunchKernelGGL((cholinv_kernel<T>), dim3((unsigned)p.b), dim3(256), 0, c.s, a);
     return (int)hipGetLastError();
@@ -2080,7 +2094,7 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
 
 template <typename T>
 static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf16, const float* Q,
-                     bool force32, void* const* ev, bool householder = false) {
+                     bool force32, void* const* ev, bool householder = false, bool spectral = false) {
     // ev: events marking the starts of the chain's three phases (product, QR, back-projection)
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], c.s) : hipSuccess; };
     const Plan& p = *c.p;
@@ -2121,7 +2135,19 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     // and the marked matrices factor W + s I instead (W is kept by the factorization)
     if ((e = gram<T>(c, P, A64 | F, A64))) return e;
     if ((e = factor_invert<T>(c, A64 | SH | F, A64, kTau64, SH, SH, 0, false))) return e;
-    if ((e = factor_invert<T>(c, A64 | SH | F, A64 | SH, 0.0, F, 0, 1, true))) return e;
+    ChainCtx cs = c;
+    if (spectral) {   // the shift from a multi-power-iteration estimate of lambda_max(W), not trace(W)
+        double* pw = (double*)(c.ws + p.pw);
+        const int64_t stride = (int64_t)(p.spw / sizeof(double));
+        MpiArgs ma{};
+        ma.W = (const double*)(c.ws + p.W); ma.r = p.r; ma.k = kShiftPool; ma.V0 = nullptr;
+        ma.ws = pw; ma.ws_stride = stride;
+        ma.lam = pw + 2 * p.r * kShiftPool + 1; ma.lam_stride = stride;
+        ma.st = c.st; ma.st_mask = A64 | SH | F; ma.st_val = A64 | SH;
+        if ((e = run_lambda_max(ma, p.b, kShiftIters, c.s))) return e;
+        cs.lam = ma.lam; cs.lam_stride = stride;
+    }
+    if ((e = factor_invert<T>(cs, A64 | SH | F, A64 | SH, 0.0, F, 0, 1, true))) return e;
     if ((e = apply<T>(c, P, Pb, A64 | F, A64))) return e;
     // pass 2
     if ((e = reortho_pass<T>(c, Pb, P, A64 | F, A64, kNearId64, F))) return e;
@@ -2212,7 +2238,8 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
     if (force64 && ev)
         for (int i = DION_PHASE_F32_PRODUCT; i <= DION_PHASE_F32_BACKPROJECT; ++i) DION_TRY(mark(i));
     if (!force32 && (e = run_chain<double>(c, M, G, g_bf16, Q, force32, ev ? ev + DION_PHASE_F64_PRODUCT : nullptr,
-                                           (options & DION_OPT_HOUSEHOLDER) != 0)))
+                                           (options & DION_OPT_HOUSEHOLDER) != 0,
+                                           (options & DION_OPT_SPECTRAL_SHIFT) != 0)))
         return e;
     if (force32 && ev)
         for (int i = DION_PHASE_F64_PRODUCT; i <= DION_PHASE_F64_BACKPROJECT; ++i) DION_TRY(mark(i));

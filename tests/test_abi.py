@@ -31,6 +31,8 @@ def test_header_enums_match_binding():
     assert vals["DION_F32"] == _lib.F32 and vals["DION_BF16"] == _lib.BF16
     assert vals["DION_OPT_STICKY_F64"] == _lib.OPT_STICKY_F64 and vals["DION_OPT_FORCE_F64"] == _lib.OPT_FORCE_F64
     assert vals["DION_OPT_FORCE_F32"] == _lib.OPT_FORCE_F32
+    assert vals["DION_OPT_HOUSEHOLDER"] == _lib.OPT_HOUSEHOLDER
+    assert vals["DION_OPT_SPECTRAL_SHIFT"] == _lib.OPT_SPECTRAL_SHIFT
     assert vals["DION_FLAG_F64"] == _lib.FLAG_F64 and vals["DION_FLAG_NONFINITE"] == _lib.FLAG_NONFINITE
     assert vals["DION_NUM_PHASES"] == _lib.NUM_PHASES == len(_lib.PHASES)
     for k, v in vals.items():
@@ -89,7 +91,8 @@ def call(**kw):
     (dict(options=_lib.OPT_FORCE_F32 | _lib.OPT_FORCE_F64), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_HOUSEHOLDER | _lib.OPT_FORCE_F32), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_HOUSEHOLDER, m=4097, n=4097, batch=1, rank=4097), _lib.ERR_OPTION),
-    (dict(options=32), _lib.ERR_OPTION),
+    (dict(options=64), _lib.ERR_OPTION),
+    (dict(options=_lib.OPT_SPECTRAL_SHIFT | _lib.OPT_FORCE_F32), _lib.ERR_OPTION),
     (dict(X=0), _lib.ERR_NULL),
     (dict(Q=0), _lib.ERR_NULL),
     (dict(workspace=0), _lib.ERR_NULL),
@@ -174,3 +177,45 @@ def test_lion_invalid_calls_rejected_on_host(kw, status):
 def test_elementwise_empty_is_a_noop():
     assert adamw(n=0, param=0, grad=0, exp_avg=0, exp_avg_sq=0) == _lib.OK
     assert lion(n=0, param=0, grad=0, exp_avg=0) == _lib.OK
+
+
+def lam(**kw):
+    a = dict(W=BASE, r=256, batch=4, V0=0, k=32, iters=10, lam=BASE + 64 * MB, workspace=BASE + 128 * MB,
+             workspace_bytes=_lib.lambda_max_workspace_size(256, 4, 32), stream=0)
+    a.update(kw)
+    return _lib.lambda_max_raw(**a)
+
+
+def test_lambda_max_workspace_size():
+    assert _lib.lambda_max_workspace_size(256, 4, 32) == 4 * (2 * 256 * 32 + 2) * 8
+    assert _lib.lambda_max_workspace_size(7, 3, 5) == 3 * (2 * 7 * 5 + 2) * 8
+    assert _lib.lambda_max_workspace_size(256, 0, 32) == 0
+    for bad in ((0, 4, 32), (256, -1, 32), (256, 4, 0), (256, 4, 33), (256, 65536, 1)):
+        assert _lib.lambda_max_workspace_size(*bad) == 0, bad
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=0), _lib.ERR_SHAPE),
+    (dict(batch=-1), _lib.ERR_SHAPE),
+    (dict(batch=65536), _lib.ERR_SHAPE),
+    (dict(k=0), _lib.ERR_SHAPE),
+    (dict(k=33), _lib.ERR_SHAPE),
+    (dict(iters=-1), _lib.ERR_HYPER),
+    (dict(iters=65), _lib.ERR_HYPER),
+    (dict(W=0), _lib.ERR_NULL),
+    (dict(lam=0), _lib.ERR_NULL),
+    (dict(workspace=0), _lib.ERR_NULL),
+    (dict(W=BASE + 4), _lib.ERR_ALIGN),
+    (dict(V0=BASE + 32 * MB + 12), _lib.ERR_ALIGN),
+    (dict(workspace=BASE + 128 * MB + 64), _lib.ERR_ALIGN),
+    (dict(workspace_bytes=1000), _lib.ERR_WORKSPACE),
+    (dict(lam=BASE + 8), _lib.ERR_OVERLAP),                 # inside W
+    (dict(lam=BASE + 128 * MB + 4096), _lib.ERR_OVERLAP),   # inside the workspace
+    (dict(V0=BASE + 128 * MB), _lib.ERR_OVERLAP),           # start vectors in the workspace
+])
+def test_lambda_max_invalid_calls_rejected_on_host(kw, status):
+    assert lam(**kw) == status
+
+
+def test_lambda_max_empty_batch_is_a_noop():
+    assert lam(batch=0, W=0, lam=0, workspace=0, workspace_bytes=0) == _lib.OK

@@ -217,16 +217,22 @@ def test_householder_fallback(cuda, wid):
     check(rep, tol_for(wl))
 
 
+@pytest.mark.parametrize("spectral", [False, True])
 @pytest.mark.parametrize("force64", [False, True])
-def test_shifted_first_pass(cuda, force64):
+def test_shifted_first_pass(cuda, force64, spectral):
     """8 decades of spectrum: the fp64 chain's plain Cholesky of P0^T P0 breaks down (host fp64
     Cholesky fails too) and the shifted first pass plus two plain passes take over; shifted
-    CholeskyQR3 in fp64 on the host stays within 4e-9 of the oracle's P Q^T on these inputs."""
+    CholeskyQR3 in fp64 on the host stays within 4e-9 of the oracle's P Q^T on these inputs.
+    With the spectral option the shift comes from the multi-power-iteration estimate of
+    lambda_max(P0^T P0) instead of its trace; the passes must still succeed without the
+    Householder last resort."""
     import dataclasses
     import rank_orthonormalized_optimizer_amd as dion
     wl = dataclasses.replace(W.SMALL[5], grad_args={"decades": 8.0}, name="shifted-8")
-    rep = run_teacher_forced(wl, cuda, options=dion.OPT_FORCE_F64 if force64 else 0, steps=2)
+    opts = (dion.OPT_FORCE_F64 if force64 else 0) | (dion.OPT_SPECTRAL_SHIFT if spectral else 0)
+    rep = run_teacher_forced(wl, cuda, options=opts, steps=2)
     for _, t, _, flags in rep:
         if t == 1:
             assert np.all(flags & dion.FLAG_SHIFTED), flags
+        assert not np.any(flags & (dion.FLAG_HOUSEHOLDER | dion.FLAG_NONFINITE)), flags
     check(rep, tol_for(wl))

@@ -146,3 +146,16 @@ def test_planted_mistake_is_caught(bad, pins):
         except AssertionError:
             caught += 1
     assert caught > 0, f"{bad.__name__} passed every pin"
+
+
+def test_start_vector_stream():
+    """The counter-based start vectors: SplitMix64 seeded with 0 begins 0xe220a8397b1dcdaf,
+    0x6e789e6aa1b965f4, 0x06c45d188009454f (its published reference outputs), and the vectors
+    are 2u - 1 of the top 53 bits, row-major over (matrix, row, vector)."""
+    import workloads as W
+    z = W.splitmix64(np.array([1, 2, 3], dtype=np.uint64))
+    assert [int(x) for x in z] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    v = W.splitmix_start_vectors(2, 3, 4)
+    assert v[0, 0, 0] == 2.0 * (0xE220A8397B1DCDAF >> 11) / 2.0 ** 53 - 1.0
+    assert v[1, 2, 3] == 2.0 * (int(W.splitmix64(np.array([24], dtype=np.uint64))[0]) >> 11) / 2.0 ** 53 - 1.0
+    assert np.all(np.abs(v) < 1.0)

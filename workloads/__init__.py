@@ -251,3 +251,46 @@ def make_grad(wl: Workload, gi: int, step: int, seed: int = 0) -> np.ndarray:
     else:
         raise ValueError(f"unknown gradient recipe {kind!r}")
     return out
+
+
+# ----------------------------------------------------------------------------
+# start vectors of the multi-power-iteration estimate (a counter-based stream)
+# ----------------------------------------------------------------------------
+_GOLDEN64 = 0x9E3779B97F4A7C15
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(n: np.ndarray) -> np.ndarray:
+    """Output number n (n >= 1) of SplitMix64 seeded with 0 (Steele, Lea and Flood, "Fast
+    Splittable Pseudorandom Number Generators", 2014): the state n * 0x9E3779B97F4A7C15
+    (mod 2^64) through the variant-13 finalizer.  Vectorized over uint64 counters."""
+    z = np.asarray(n, dtype=np.uint64) * np.uint64(_GOLDEN64)
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def splitmix_start_vectors(batch: int, r: int, k: int) -> np.ndarray:
+    """The library's default start vectors of the lambda_max estimate, [batch, r, k] fp64:
+    entry (b, i, j) is 2u - 1 with u the top 53 bits of SplitMix64 output b*r*k + i*k + j + 1
+    over 2^53 (exact in fp64)."""
+    idx = np.arange(batch * r * k, dtype=np.uint64) + np.uint64(1)
+    with np.errstate(over="ignore"):
+        z = splitmix64(idx)
+    u = (z >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    return (2.0 * u - 1.0).reshape(batch, r, k)
+
+
+def psd_stack(batch: int, r: int, seed: int, kind: str = "gram", decades: float = 6.0) -> np.ndarray:
+    """Symmetric PSD test matrices [batch, r, r] fp64: "gram" = A^T A with A (r + 8) x r Gaussian
+    (a Gram matrix like P0^T P0), "spectrum" = U diag(10^(-decades i / r)) U^T with U Haar."""
+    out = np.empty((batch, r, r))
+    for b in range(batch):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, r, b, len(kind)])))
+        if kind == "gram":
+            A = rng.standard_normal((r + 8, r))
+            out[b] = A.T @ A
+        else:
+            U = _haar(rng, r)
+            out[b] = (U * 10.0 ** (-decades * np.arange(r) / r)) @ U.T
+    return out
