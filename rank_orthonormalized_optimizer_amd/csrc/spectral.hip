@@ -17,7 +17,7 @@
 //
 // Kernels: one init launch (the pool, from the caller's vectors or a SplitMix64 counter stream,
 // and the trace), t + 1 product launches over 64-row blocks (W tiles mirrored from the lower
-// triangle through LDS, the pool tile broadcast from LDS, fp64 FMAs), one finish launch per
+// triangle through LDS, fp64 matrix-core products with the pool), one finish launch per
 // matrix (fixed-order dot products and the pool's maximum).  Every launch returns at once for a
 // matrix whose state word does not match, so the Dion step can run it for the shifted matrices
 // only.
@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include "dion_plan.h"
+#include "gemm_mfma.hpp"
 
 namespace dion {
 
@@ -67,8 +68,20 @@ __global__ __launch_bounds__(256) void mpi_init_kernel(MpiArgs a) {
     if (blockIdx.x == 0) {
         __shared__ double red[256];
         const double* W = a.W + bz * a.r * a.r;
+        const int64_t r = a.r;
         double tr = 0;
-        for (int64_t i = threadIdx.x; i < a.r; i += 256) tr += W[i * a.r + i];
+        // eight diagonal loads in flight per thread (clamped addresses, zero outside)
+        for (int64_t i0 = threadIdx.x; i0 < r; i0 += 256 * 8) {
+            double d[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t i = i0 + 256 * q;
+                const double x = W[(i < r ? i : 0) * (r + 1)];
+                d[q] = i < r ? x : 0.0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) tr += d[q];
+        }
         red[threadIdx.x] = tr;
         __syncthreads();
         for (int w = 128; w > 0; w >>= 1) {
@@ -80,7 +93,14 @@ __global__ __launch_bounds__(256) void mpi_init_kernel(MpiArgs a) {
 }
 
 // V_out[rows of this block] = W V_in / trace(W), for the 64 rows R0.. of W; the pool buffer
-// `src` is read and the other one written.
+// `src` is read and the other one written.  Each wave multiplies 16 rows by the 32 pool columns
+// on the fp64 matrix cores (two 16 x 16 blocks, v_mfma_f64_16x16x4, k = 4 s + lane / 16 at
+// step s).  The next column tile of W and of the pool is loaded into registers while the
+// current one is multiplied from LDS (loads branch-free: addresses clamped into the matrix,
+// values selected to zero outside it), so each tile's HBM latency overlaps the previous tile's
+// matrix-core work.  LDS pitches 66 (W) and 48 (pool) doubles put each half-wave's fragment
+// reads in distinct banks.  (Loading each wave's W fragments straight into registers, without
+// LDS, measured 13% slower: below the diagonal a fragment load then touches 16 rows of W.)
 __global__ __launch_bounds__(256) void mpi_product_kernel(MpiArgs a, int src) {
     const int bz = blockIdx.y;
     if (!owned(a, bz)) return;
@@ -92,47 +112,84 @@ __global__ __launch_bounds__(256) void mpi_product_kernel(MpiArgs a, int src) {
     double* Vout = base + (src ? 0 : rk);
     const double tau = base[2 * rk];
     const double scale = tau > 0.0 ? 1.0 / tau : 0.0;
-    __shared__ double Wt[kRows][kRows + 1];
-    __shared__ double Vt[kRows][kMpiMaxPool];
-    const int tid = threadIdx.x, row = tid & (kRows - 1), j0 = (tid >> 6) * 8;
+    constexpr int kWPitch = kRows + 2, kVPitch = kMpiMaxPool + 16;
+    __shared__ double Wt[kRows][kWPitch];
+    __shared__ double Vt[kRows][kVPitch];
+    constexpr int kWPer = kRows * kRows / 256, kVPer = kRows * kMpiMaxPool / 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
     const int64_t R0 = (int64_t)blockIdx.x * kRows;
-    double acc[8];
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0;
     const int64_t ntile = (r + kRows - 1) / kRows;
-    for (int64_t cb = 0; cb < ntile; ++cb) {
+    double wr[kWPer], vr[kVPer];
+    // element (gi, gc) of the symmetric W from the lower triangle: W[gi][gc] if gc <= gi, else
+    // W[gc][gi]; threads run along the stored rows so the loads coalesce either way
+    auto load_tile = [&](int64_t cb) {
         const int64_t C0 = cb * kRows;
-        __syncthreads();
-        // element (gi, gc) of the symmetric W from the lower triangle: W[gi][gc] if gc <= gi, else
-        // W[gc][gi]; threads run along the stored rows so the loads coalesce either way
-        for (int e = tid; e < kRows * kRows; e += 256) {
-            int i, c;
-            if (C0 <= R0) { i = e >> 6; c = e & (kRows - 1); }
-            else { c = e >> 6; i = e & (kRows - 1); }
+        const bool lower = C0 <= R0;
+#pragma unroll
+        for (int q = 0; q < kWPer; ++q) {
+            const int e = tid + 256 * q;
+            const int i = lower ? (e >> 6) : (e & (kRows - 1));
+            const int c = lower ? (e & (kRows - 1)) : (e >> 6);
             const int64_t gi = R0 + i, gc = C0 + c;
-            double w = 0.0;
-            if (gi < r && gc < r) w = gc <= gi ? W[gi * r + gc] : W[gc * r + gi];
-            Wt[i][c] = w;
+            const bool ok = gi < r && gc < r;
+            const int64_t hi = ok ? (gc <= gi ? gi : gc) : 0, lo = ok ? (gc <= gi ? gc : gi) : 0;
+            const double w = W[hi * r + lo];
+            wr[q] = ok ? w : 0.0;
         }
-        for (int e = tid; e < kRows * kMpiMaxPool; e += 256) {
+#pragma unroll
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + 256 * q;
             const int c = e / kMpiMaxPool, j = e % kMpiMaxPool;
             const int64_t gc = C0 + c;
-            Vt[c][j] = (gc < r && j < k) ? Vin[gc * k + j] : 0.0;
+            const bool ok = gc < r && j < k;
+            const double v = Vin[ok ? gc * k + j : 0];
+            vr[q] = ok ? v : 0.0;
+        }
+    };
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+    load_tile(0);
+    for (int64_t cb = 0; cb < ntile; ++cb) {
+        const bool lower = cb * kRows <= R0;
+        __syncthreads();   // the previous tile's products are done with the LDS tiles
+#pragma unroll
+        for (int q = 0; q < kWPer; ++q) {
+            const int e = tid + 256 * q;
+            const int i = lower ? (e >> 6) : (e & (kRows - 1));
+            const int c = lower ? (e & (kRows - 1)) : (e >> 6);
+            Wt[i][c] = wr[q];
+        }
+#pragma unroll
+        for (int q = 0; q < kVPer; ++q) {
+            const int e = tid + 256 * q;
+            Vt[e / kMpiMaxPool][e % kMpiMaxPool] = vr[q];
         }
         __syncthreads();
-        for (int c = 0; c < kRows; ++c) {
-            const double w = Wt[row][c];
-            for (int q = 0; q < 8; ++q) acc[q] = fma(w, Vt[c][j0 + q], acc[q]);
+        load_tile(cb + 1 < ntile ? cb + 1 : cb);   // the last tile reloads itself: no branch on the loads
+#pragma unroll
+        for (int st = 0; st < kRows / 4; ++st) {
+            const int kk = 4 * st + lk;
+            const double af = Wt[16 * wave + lr][kk];
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(af, Vt[kk][lr], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(af, Vt[kk][16 + lr], acc1, 0, 0, 0);
         }
     }
-    const int64_t gi = R0 + row;
-    if (gi < r)
-        for (int q = 0; q < 8; ++q)
-            if (j0 + q < k) Vout[gi * k + j0 + q] = acc[q] * scale;
+    // D[row][col] of a 16 x 16 block: lane l, element v holds row l / 16 + 4 v, column l % 16
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t gi = R0 + 16 * wave + lk + 4 * v;
+        if (gi < r) {
+            if (lr < k) Vout[gi * k + lr] = acc0[v] * scale;
+            if (16 + lr < k) Vout[gi * k + 16 + lr] = acc1[v] * scale;
+        }
+    }
 }
 
 // lambda_hat = max_j trace(W) (V_t . V_t+1)_j / (V_t . V_t)_j over the pool (0 for a zero
-// vector); `last` is the buffer the last product wrote (V_t+1).
-__global__ __launch_bounds__(256) void mpi_finish_kernel(MpiArgs a, int last) {
+// vector); `last` is the buffer the last product wrote (V_t+1).  1024 threads: column j = tid % 32,
+// row group g = tid / 32 takes rows g, g + 32, ... four at a time; the 32 groups' partial sums are
+// added in group order.
+__global__ __launch_bounds__(1024) void mpi_finish_kernel(MpiArgs a, int last) {
     const int bz = blockIdx.x;
     if (!owned(a, bz)) return;
     const int64_t r = a.r, rk = r * a.k;
@@ -141,21 +198,31 @@ __global__ __launch_bounds__(256) void mpi_finish_kernel(MpiArgs a, int last) {
     const double* V1 = base + (last ? rk : 0);
     const double* V0 = base + (last ? 0 : rk);
     const double tau = base[2 * rk];
-    __shared__ double sn[256], sd[256];
+    __shared__ double sn[1024], sd[1024];
     const int j = threadIdx.x & 31, g = threadIdx.x >> 5;
     double num = 0.0, den = 0.0;
     if (j < k)
-        for (int64_t i = g; i < r; i += 8) {
-            const double x = V0[i * k + j];
-            num = fma(x, V1[i * k + j], num);
-            den = fma(x, x, den);
+        for (int64_t i0 = g; i0 < r; i0 += 32 * 4) {
+            double x[4], y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = i0 + 32 * q;
+                const int64_t o = (i < r ? i : 0) * k + j;
+                x[q] = i < r ? V0[o] : 0.0;
+                y[q] = i < r ? V1[o] : 0.0;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                num = fma(x[q], y[q], num);
+                den = fma(x[q], x[q], den);
+            }
         }
     sn[threadIdx.x] = num;
     sd[threadIdx.x] = den;
     __syncthreads();
     if (threadIdx.x < 32) {
         double n = 0.0, d = 0.0;
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 32; ++q) {
             n += sn[q * 32 + j];
             d += sd[q * 32 + j];
         }
@@ -177,7 +244,7 @@ int run_lambda_max(const MpiArgs& a, int64_t b, int iters, void* stream) {
     for (int i = 1; i <= iters + 1; ++i)
         hipLaunchKernelGGL(mpi_product_kernel, dim3((unsigned)((a.r + kRows - 1) / kRows), (unsigned)b), dim3(256), 0,
                            s, a, (i - 1) & 1);
-    hipLaunchKernelGGL(mpi_finish_kernel, dim3((unsigned)b), dim3(256), 0, s, a, (iters + 1) & 1);
+    hipLaunchKernelGGL(mpi_finish_kernel, dim3((unsigned)b), dim3(1024), 0, s, a, (iters + 1) & 1);
     return (int)hipGetLastError();
 }
 
