@@ -148,7 +148,7 @@ int dion_lambda_max_batched(const double* W, int64_t r, int64_t batch, const dou
         for (int j = i + 1; j < 4; ++j)
             if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
     dion::MpiArgs a{};
-    a.W = W; a.r = r; a.k = k; a.V0 = V0;
+    a.W = W; a.r = r; a.k = k; a.V0 = V0; a.first = 0;
     a.ws = (double*)workspace; a.ws_stride = 2 * r * k + 2;
     a.lam = lambda; a.lam_stride = 1;
     a.st = nullptr;

@@ -38,6 +38,7 @@ struct Plan {
     int64_t gsplit;    // K-splits of the fp64 Gram products (partials reduced in fixed order)
     int64_t gsplit6;   // K-splits of the fp32 Gram products (split-bf16 kernel, 128 x 128 tiles)
     int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
+    int64_t c0;        // index of the first matrix (0, or a chunk's offset in the whole stack)
     // byte offsets into the workspace (all 256-byte aligned)
     size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw;
     size_t total;
@@ -49,6 +50,7 @@ struct Plan {
 inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     Plan q = p;
     q.b = cb;
+    q.c0 = p.c0 + c0;
     const size_t c = (size_t)c0;
     q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
@@ -143,13 +145,15 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
 // Multi-power-iteration estimate of lambda_max for a stack of symmetric PSD matrices (only the
 // lower triangle of W is read).  Per matrix bz: pool and trace in ws + bz * ws_stride (doubles:
 // two r x k buffers, then the trace), the estimate written to lam[bz * lam_stride].  V0 is
-// [b][r][k] or null (SplitMix64 start vectors); st null runs every matrix, else only those with
-// (st[bz] & st_mask) == st_val.
+// [b][r][k] or null (SplitMix64 start vectors, counted from matrix index first + bz, so that a
+// matrix gets the same vectors whichever chunk it runs in); st null runs every matrix, else only
+// those with (st[bz] & st_mask) == st_val.
 struct MpiArgs {
     const double* W;
     int64_t r;
     int k;
     const double* V0;
+    int64_t first;
     double* ws;
     int64_t ws_stride;
     double* lam;

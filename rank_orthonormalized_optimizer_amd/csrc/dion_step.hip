@@ -2140,7 +2140,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
         double* pw = (double*)(c.ws + p.pw);
         const int64_t stride = (int64_t)(p.spw / sizeof(double));
         MpiArgs ma{};
-        ma.W = (const double*)(c.ws + p.W); ma.r = p.r; ma.k = kShiftPool; ma.V0 = nullptr;
+        ma.W = (const double*)(c.ws + p.W); ma.r = p.r; ma.k = kShiftPool; ma.V0 = nullptr; ma.first = p.c0;
         ma.ws = pw; ma.ws_stride = stride;
         ma.lam = pw + 2 * p.r * kShiftPool + 1; ma.lam_stride = stride;
         ma.st = c.st; ma.st_mask = A64 | SH | F; ma.st_val = A64 | SH;
@@ -2154,7 +2154,9 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
     // pass 3, only after a shifted first pass
     if ((e = reortho_pass<T>(c, P, Pb, A64 | SH | F, A64 | SH, kNearId64, F))) return e;
     {
-        dim3 grid(grid_1d(p.m * p.r, 1024), (unsigned)p.b);
+        // rare copies (failed or shifted matrices only): few workgroups per matrix, so that the
+        // launch costs little when no matrix needs it
+        dim3 grid(grid_1d(p.m * p.r, 128), (unsigned)p.b);
         // Where a pass broke down, P still holds P0 times an upper-triangular matrix (the passes
         // before the failing one), whose Q-factor is that of P0: Householder QR of a copy in Pb,
         // the Q-factor written back to P

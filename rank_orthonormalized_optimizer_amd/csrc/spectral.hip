@@ -49,7 +49,7 @@ __device__ __forceinline__ bool owned(const MpiArgs& a, int bz) {
 }
 
 // The pool V_0 (caller's vectors, or 2u - 1 with u the top 53 bits of SplitMix64 output
-// bz*r*k + i*k + j + 1) and trace(W), fixed-order.
+// (first + bz)*r*k + i*k + j + 1) and trace(W), fixed-order.
 __global__ __launch_bounds__(256) void mpi_init_kernel(MpiArgs a) {
     const int bz = blockIdx.y;
     if (!owned(a, bz)) return;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void mpi_init_kernel(MpiArgs a) {
         if (a.V0) {
             v = a.V0[bz * rk + idx];
         } else {
-            const uint64_t z = splitmix64_at((uint64_t)(bz * rk + idx) + 1);
+            const uint64_t z = splitmix64_at((uint64_t)((a.first + bz) * rk + idx) + 1);
             v = (double)(z >> 11) * 0x1.0p-53 * 2.0 - 1.0;
         }
         V[idx] = v;

@@ -68,3 +68,30 @@ def test_mixed_optimizer_steps(cuda, other):
             assert rel(got, th) <= 1e-4, (t, i)
             assert rel(to_numpy(opt.state[i][0]).astype(np.float64), mm) <= 1e-5, (t, i)
             assert tuple(params[i].shape) == SHAPES[i]
+
+
+def test_mixed_optimizer_bf16(cuda):
+    """bf16 weights: the 2-D ones go to Dion with bf16 X (fp32 M and Q), the rest to AdamW with a
+    bf16 parameter; one step against the oracles at the bf16 bar (2e-2 on the parameters)."""
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    from tests.test_gpu_elementwise import _store, _up
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([22])))
+    shapes = [(64, 96), (64, 96), (33,)]
+    host = [_store(0.02 * rng.standard_normal(s), "bf16") for s in shapes]
+    params = [torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(cuda) for h in host]
+    opt = dion.MixedDion(params, lr=0.01, mu=0.95, other="adamw", other_lr=1e-3, betas=(0.9, 0.999),
+                         weight_decay=0.0)
+    gh = [_store(1e-2 * rng.standard_normal(s), "bf16") for s in shapes]
+    grads = [torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(cuda) for h in gh]
+    (idx, st), = opt.groups
+    M0, Q0 = to_numpy(st.M).astype(np.float64), to_numpy(st.Q).astype(np.float64)
+    print("[mixed] bf16 step", flush=True)
+    opt.step(grads)
+    torch.cuda.synchronize()
+    for k, i in enumerate(idx):
+        o = dion_step(_up(host[i]), _up(gh[i]), M0[k], Q0[k], 0.95, _f32(0.01), 1e-8)
+        assert rel(_up(to_numpy(params[i])), o["X"]) <= 2e-2, i
+    th, _, _ = adamw_step(_up(host[2]), _up(gh[2]), np.zeros(33), np.zeros(33), 1, _f32(1e-3), _f32(0.9),
+                          _f32(0.999), _f32(1e-8), 0.0)
+    assert rel(_up(to_numpy(params[2])), th) <= 2e-2

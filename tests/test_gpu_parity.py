@@ -236,3 +236,28 @@ def test_shifted_first_pass(cuda, force64, spectral):
             assert np.all(flags & dion.FLAG_SHIFTED), flags
         assert not np.any(flags & (dion.FLAG_HOUSEHOLDER | dion.FLAG_NONFINITE)), flags
     check(rep, tol_for(wl))
+
+
+def test_spectral_shift_chunks_bitwise(cuda):
+    """The spectral shift's pool lives in per-matrix workspace slices: splitting the stack into
+    concurrent chunks must not change a bit of the shifted step."""
+    import dataclasses
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    from rank_orthonormalized_optimizer_amd._lib import opt_chunks
+    wl = dataclasses.replace(W.SMALL[5], grad_args={"decades": 8.0}, name="shifted-8-chunks")
+    g = wl.groups[0]
+    X, M, Q = W.make_state(wl, 0)
+    G = to_torch(W.make_grad(wl, 0, 1), cuda)
+    outs = []
+    for nc in (1, 2):
+        Xd, Md, Qd = to_torch(X, cuda), to_torch(M, cuda), to_torch(Q, cuda)
+        flags = torch.zeros(g.batch, dtype=torch.int32, device=cuda)
+        print(f"[parity] spectral shift chunks={nc}", flush=True)
+        dion.step_(Xd, G, Md, Qd, g.rank, wl.mu, wl.lr, wl.eps, flags=flags,
+                   options=dion.OPT_FORCE_F64 | dion.OPT_SPECTRAL_SHIFT | opt_chunks(nc))
+        torch.cuda.synchronize()
+        outs.append((to_numpy(Xd), to_numpy(Md), to_numpy(Qd), to_numpy(flags)))
+    assert np.all(outs[0][3] & dion.FLAG_SHIFTED)
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
