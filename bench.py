@@ -225,7 +225,10 @@ def spectral_block(dev, stream, reps: int = 10, with_cpu: bool = True) -> dict:
                 "calls_per_s": 1e3 / ms_full, "product_launch_ms": prod_ms,
                 "roofline": {"bound": "alu", "kernel": "mpi_product_kernel", "achieved": tf,
                              "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s", "frac": tf / PEAK_TFLOPS["f64"],
-                             "flops_per_launch": flops}}
+                             "flops_per_launch": flops,
+                             "traffic": measured_traffic(f"spectral-{b}x{r}x{r}", "mpi_product_kernel"),
+                             "traffic_unit": "bytes/launch",
+                             "algorithmic_bytes_per_launch": b * (8.0 * r * r + 16.0 * r * SPECTRAL_K)}}
         if with_cpu:
             from oracle.spectral_oracle import lambda_max_estimate
             import workloads as W
