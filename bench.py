@@ -8,6 +8,11 @@ with low-rank-plus-noise gradients (see workloads/).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
 
+The K timed steps run twice: eagerly (one host launch per kernel, with the library's phase
+events) and as replays of the same steps captured in HIP graphs (one graph per resident
+gradient).  The replays set the value; both times are reported ("eager_ms_per_step",
+"graph_ms_per_step"), and --eager times the eager steps only.
+
 Metric: updates/s (steps per second over the whole workload), with the
 effective parameter bandwidth (algorithmic bytes / step time) and its share of
 the 8 TB/s HBM peak alongside.  The "roofline" entry times the dominant kernel
@@ -257,6 +262,9 @@ def main() -> int:
                     help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
     ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager steps only (default: also capture them as HIP graphs and time the replays, "
+                         "which set the reported value)")
     ap.add_argument("--no-elementwise", action="store_true",
                     help="skip the AdamW / Lion measurement (the parameters Dion does not take)")
     ap.add_argument("--elementwise-only", action="store_true",
@@ -359,7 +367,42 @@ def main() -> int:
     enqueue = time.perf_counter() - w0
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = t0.elapsed_time(t1) / args.steps
+    eager_ms = t0.elapsed_time(t1) / args.steps
+    ms, launch, graph_ms = eager_ms, "eager", None
+    if not args.eager:
+        # The same steps captured once per resident gradient as HIP graphs and replayed: the
+        # kernels and their arguments are those of the eager steps (options as the host hint has
+        # settled them), so only the host's launch overhead between kernels goes away.
+        ng = max(len(s_["G"]) for s_ in stacks)
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(stream)
+        graphs = []
+        for j in range(ng):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                gph.capture_begin()
+                for s_ in stacks:
+                    g_ = s_["g"]
+                    o = opts if s_["hint"] is None else s_["hint"].options(opts)
+                    dion.step_(s_["X"], s_["G"][j % len(s_["G"])], s_["M"], s_["Q"], g_.rank, wl.mu, wl.lr, wl.eps,
+                               workspace=s_["ws"], flags=s_["flags"], options=o, stream=cap)
+                gph.capture_end()
+            graphs.append(gph)
+        stream.wait_stream(cap)
+        for k in range(2):
+            graphs[(args.warmup + args.steps + k) % ng].replay()
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for k in range(args.steps):
+            graphs[(args.warmup + args.steps + 2 + k) % ng].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        ms, launch = graph_ms, "hip_graph"
+        del graphs
 
     # per-phase device times, averaged over the timed steps (summed over stacks)
     phase_ms = {p: 0.0 for p in PHASES}
@@ -420,7 +463,10 @@ def main() -> int:
         "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,
         "matrices": nmat, "fp64_chain_matrices": n64, "nonfinite_matrices": nbad,
         "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
-        "wall_s_timed_region": wall,
+        "launch": launch,
+        "eager_ms_per_step": eager_ms,
+        "graph_ms_per_step": graph_ms,
+        "wall_s_timed_region_eager": wall,
         "host_enqueue_ms_per_step": 1000.0 * enqueue / args.steps,
         "roofline": {"bound": "mfma", "kernel": dom, "what": what, "dtype": dt_,
                      "achieved": achieved, "peak": PEAK_TFLOPS[dt_], "unit": "TFLOP/s",
