@@ -148,6 +148,36 @@ class DionStack:
         return self.workspace[:4 * n].view(torch.float32).view(self.batch, self.m, self.rank)
 
 
+class GraphedStep:
+    """One DionStack step captured in a HIP graph for fixed tensors, replayed by ``replay()``.
+
+    The step's kernels and arguments are those of ``stack.step(X, G)`` at capture time
+    (including the options the host hint has settled on), so a replay gives bitwise the result
+    of an eager step on the same inputs, without the host launching each kernel.  ``G`` is read
+    at replay time: refill it in place between replays.  Capture after at least one eager step
+    (the sticky flags and the hint settle there); recapture if the options should change.
+    """
+
+    def __init__(self, stack: "DionStack", X: torch.Tensor, G: torch.Tensor):
+        self.stack, self.X, self.G = stack, X, G
+        dev = stack.flags.device
+        opts = stack.hint.options(stack.options) if stack.hint is not None else stack.options
+        cur = torch.cuda.current_stream(dev)
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(cur)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            self.graph.capture_begin()
+            step_(X, G, stack.M, stack.Q, stack.rank, stack.mu, stack.lr, stack.eps, workspace=stack.workspace,
+                  flags=stack.flags, options=opts, stream=cap)
+            self.graph.capture_end()
+        cur.wait_stream(cap)
+
+    def replay(self) -> None:
+        """Enqueue the captured step on torch's current stream."""
+        self.graph.replay()
+
+
 def group_matrices(params) -> "OrderedDict[tuple, list]":
     """Group 2-D tensors by (shape, dtype) into stackable lists; reject anything else.
 

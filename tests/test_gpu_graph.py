@@ -59,3 +59,31 @@ def test_graph_replay_bitwise_equals_eager(cuda, wid):
         assert float(junk) == float(junk)
         for a, b in ((Xa, Xb), (Ma, Mb), (Qa, Qb), (Fa, Fb)):
             assert np.array_equal(to_numpy(a), to_numpy(b)), (wid, t)
+
+
+def test_graphed_step_api(cuda):
+    """api.GraphedStep: a DionStack step captured once and replayed with a refilled gradient buffer
+    equals the DionStack's eager steps bit for bit."""
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.SMALL[2]
+    g = wl.groups[0]
+    X, _, _ = W.make_state(wl, 0)
+    grads = [to_torch(W.make_grad(wl, 0, t), cuda) for t in range(1, 5)]
+    sa = dion.DionStack(g.batch, g.m, g.n, rank=g.rank, mu=wl.mu, lr=wl.lr, eps=wl.eps, device=cuda)
+    sb = dion.DionStack(g.batch, g.m, g.n, rank=g.rank, mu=wl.mu, lr=wl.lr, eps=wl.eps, device=cuda)
+    Xa, Xb = to_torch(X, cuda), to_torch(X, cuda)
+    for t in (0, 1):   # two eager steps on both: flags and the host hint settle
+        sa.step(Xa, grads[t])
+        sb.step(Xb, grads[t])
+    torch.cuda.synchronize()
+    gbuf = grads[2].clone()
+    gs = dion.GraphedStep(sb, Xb, gbuf)
+    for t in (2, 3):
+        print(f"[graph] GraphedStep step {t + 1}", flush=True)
+        sa.step(Xa, grads[t])
+        gbuf.copy_(grads[t])
+        gs.replay()
+        torch.cuda.synchronize()
+        for a, b in ((Xa, Xb), (sa.M, sb.M), (sa.Q, sb.Q), (sa.flags, sb.flags)):
+            assert np.array_equal(to_numpy(a), to_numpy(b)), t
