@@ -16,15 +16,18 @@ from tests.harness import to_numpy, to_torch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3])
-def test_graph_replay_bitwise_equals_eager(cuda, wid):
+@pytest.mark.parametrize("wid,chunks", [(1, 1), (2, 1), (3, 1), (2, 3)])
+def test_graph_replay_bitwise_equals_eager(cuda, wid, chunks):
+    """chunks > 1 runs the stack on the library's internal streams (fork/join by events), which
+    the capture records as parallel branches."""
     import torch
     import rank_orthonormalized_optimizer_amd as dion
+    from rank_orthonormalized_optimizer_amd._lib import opt_chunks
     wl = W.SMALL[wid]
     g = wl.groups[0]
     X, M, Q = W.make_state(wl, 0)
     grads = [to_torch(W.make_grad(wl, 0, t), cuda) for t in range(1, 5)]
-    opts = dion.OPT_STICKY_F64
+    opts = dion.OPT_STICKY_F64 | opt_chunks(chunks)
 
     def state():
         return (to_torch(X, cuda), to_torch(M, cuda), to_torch(Q, cuda),
