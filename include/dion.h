@@ -96,7 +96,8 @@ enum {
                                  skip the fp32 attempt and go straight to the fp64 chain */
     DION_OPT_FORCE_F64 = 2,   /* every matrix uses the fp64 chain */
     DION_OPT_FORCE_F32 = 4,   /* never fall back; an fp32 breakdown is reported as
-                                 DION_FLAG_NONFINITE and its results are undefined */
+                                 DION_FLAG_NONFINITE and that matrix takes the rank-0 step
+                                 (see DION_FLAG_NONFINITE) */
     DION_OPT_HOUSEHOLDER = 16, /* the fp64 chain orthonormalizes P0 by its last-resort Householder
                                  QR instead of CholeskyQR (with DION_OPT_FORCE_F64: every
                                  matrix); not with DION_OPT_FORCE_F32, rank <= 4096.  The
@@ -115,7 +116,10 @@ enum {
 /* per-matrix `flags` bits written by the step (device int32 [batch]) */
 enum {
     DION_FLAG_F64 = 1,        /* this step's P and R came from the fp64 chain */
-    DION_FLAG_NONFINITE = 2,  /* a NaN/Inf was met, or the factorization broke down */
+    DION_FLAG_NONFINITE = 2,  /* a NaN/Inf was met, or the factorization broke down with no
+                                 fallback left (DION_OPT_FORCE_F32, or rank > 4096 where the
+                                 Householder QR does not reach): such a matrix gets M <- M + G and
+                                 keeps X and Q unchanged, and its P in the workspace is undefined */
     DION_FLAG_SHIFTED = 4,    /* the fp64 chain needed the shifted first pass */
     DION_FLAG_HOUSEHOLDER = 8 /* P came from the fp64 Householder QR (the CholeskyQR passes broke
                                  down, or DION_OPT_HOUSEHOLDER) */

@@ -49,6 +49,16 @@ constexpr double kTau64 = 1.0e7;
 // <= 4e-12) and S up to F^3 (truncation eps^4 <= 1e-12); beyond, the Cholesky pass.
 constexpr double kNearId32 = 1.0e-4;
 constexpr double kNearId64 = 1.0e-6;
+// Diagonal-ratio limit of a re-orthonormalization pass's Cholesky regime.  After a plain first
+// pass accepted under kTau32 / kTau64, P1^T P1 is I + O(kappa^2 u) and the ratio stays near 1;
+// after the shifted first pass kappa(P1) ~ sqrt(c_shift r) kappa(P0), which reached 5.6e4 on the
+// full-rank 4096^2 stack (CPU emulation of its first step) and a few 1e4 on 8-decade spectra.
+// A P0 that is singular to working precision (duplicate or zero columns) leaves P1 singular too,
+// and its Cholesky then either fails or shows a ratio near u^-1/2 (1e8 in fp64): above the limit
+// the pass counts as broken down, and the matrix goes on to the next fallback (fp32: the fp64
+// chain; fp64: the Householder QR).
+constexpr double kTauRe32 = 1.0e3;
+constexpr double kTauRe64 = 1.0e6;
 
 // ---------------------------------------------------------------------------
 // generic batched GEMM:  C = alpha * A B + beta * C
@@ -615,6 +625,7 @@ __device__ __forceinline__ void row4(const double* p64src, float* p32, int64_t o
 __global__ __launch_bounds__(256) void next_q_kernel(const double* R64, float* R32, const double* cs, float* Q,
                                                      int64_t n, int64_t r, const int* st) {
     const int bz = blockIdx.y;
+    if (st[bz] & ST_FAIL) return;   // no factor: Q stays as it was
     const bool p64 = (st[bz] & ST_PATH64) != 0, vec = (r % 4) == 0;
     const int64_t nr = n * r, gpr = (r + 3) / 4, groups = n * gpr;
     const double* c = cs + bz * r;
@@ -652,10 +663,27 @@ __global__ __launch_bounds__(256) void round_p_kernel(const double* P64, float* 
 struct UpdArgs {
     const float* P; const float* R; const float* Q;   // fp32 [b][rows][r], k contiguous
     float* M; const void* G; void* X;
+    const int* st;                                    // per-matrix state words
     int m, n, r, kp;                                  // kp: r rounded up to whole 32-k slabs
     bool vec;                                         // r % 4 == 0: 16-byte row loads
     float one_minus_mu, lr_s;
 };
+
+// The tile of a matrix whose orthonormalization broke down with no fallback left (ST_FAIL):
+// there is no factor to update with, so the step is the rank-0 one, M <- M + G, X untouched.
+template <int BM, int BN, bool G_BF16>
+__device__ void failed_tile(const UpdArgs& u, int bz, int m0, int n0) {
+    const int64_t mn = (int64_t)u.m * u.n;
+    for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
+        const int row = m0 + idx / BN, col = n0 + idx % BN;
+        if (row >= u.m || col >= u.n) continue;
+        const int64_t off = bz * mn + (int64_t)row * u.n + col;
+        float g;
+        if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
+        else g = ((const float*)u.G)[off];
+        u.M[off] += g;
+    }
+}
 
 // One BM x BN tile of M and X per workgroup of WGM x WGN waves: both rank-kp products on the
 // bf16 matrix cores in the six-term split form (fp32 accuracy), sharing the P fragments, then
@@ -670,6 +698,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
     static_assert(FM * WGM * 16 == BM && FN * WGN * 16 == BN, "whole MFMA blocks per wave");
     const TileId tid = xcd_tile_id();
     const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
+    if (u.st[bz] & ST_FAIL) {
+        failed_tile<BM, BN, G_BF16>(u, bz, m0, n0);
+        return;
+    }
     __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][3][BM * BK];   // P h m l
     __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][6][BN * BK];   // R h m l | Q h m l
     const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
@@ -797,6 +829,10 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     constexpr int BM = 128, BN = 64, PA = BM * kSplitK, PB = BN * kSplitK, FM = 4, FN = 2;
     const TileId tid = xcd_tile_id();
     const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
+    if (u.st[bz] & ST_FAIL) {
+        failed_tile<BM, BN, G_BF16>(u, bz, m0, n0);
+        return;
+    }
     __shared__ __attribute__((aligned(16))) uint16_t lds[3 * PA + 6 * PB];   // P h m l | R h m l | Q h m l
     const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
     const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
@@ -1734,6 +1770,7 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
     const int64_t r = p.r, b = p.b;
     T* W = (T*)(c.ws + p.W);
     double* part = (double*)(c.ws + p.emax);
+    const double tau_re = sizeof(T) == 8 ? kTauRe64 : kTauRe32;
     int e;
     if ((e = gram<T>(c, Pin, mask, val, false))) return e;
     {
@@ -1750,7 +1787,8 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
         if (p.nblk <= kFusedMaxBlocks) {
             // matrices far from orthonormal: a full Cholesky pass (W is untouched), T = L^-1, in
             // the fused factorization, which makes the regime test itself
-            if ((e = factor_invert<T>(c, mask, val, 0.0, fail_bit, 0, 0, true, part, (int)nparts, tau))) return e;
+            if ((e = factor_invert<T>(c, mask, val, tau_re, fail_bit, fail_bit, 0, true, part, (int)nparts, tau)))
+                return e;
             return apply<T>(c, Pin, Pout, mask, val);
         }
         hipLaunchKernelGGL(near_id_decide_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, (const double*)part,
@@ -1758,7 +1796,7 @@ static int reortho_pass(const ChainCtx& c, const T* Pin, T* Pout, int mask, int 
         DION_TRY(hipGetLastError());
     }
     const int cmask = mask | ST_CHOL2, cval = val | ST_CHOL2;
-    if ((e = factor_invert<T>(c, cmask, cval, 0.0, fail_bit, 0, 0, true))) return e;
+    if ((e = factor_invert<T>(c, cmask, cval, tau_re, fail_bit, fail_bit, 0, true))) return e;
     return apply<T>(c, Pin, Pout, mask, val);
 }
 
@@ -2185,6 +2223,7 @@ static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, f
     u.R = (const float*)(ws + p.R32);
     u.Q = Q;
     u.M = M; u.G = G; u.X = X;
+    u.st = (const int*)(ws + p.st);
     u.m = (int)p.m; u.n = (int)p.n; u.r = (int)p.r; u.kp = (int)p.kp;
     u.vec = (p.r % 4) == 0;
     u.one_minus_mu = 1.0f - mu;

@@ -6,7 +6,9 @@ pins are properties the published rules fix, none of them a retyping of the
 update:
 
   AdamW  first step from zero moments: the move is lr * g / (|g| + eps) whatever the
-         betas (the bias corrections cancel exactly); under a constant gradient every
+         betas (the bias corrections cancel exactly), and with decay the decoupled rule
+         gives theta (1 - lr wd) - lr g / (|g| + eps), the decay taken on the weight as it
+         was before the step; under a constant gradient every
          later step moves by the same amount (the corrected moments stay g and g^2);
          a zero gradient from zero moments only decays; the moments are geometric
          blends with weights (1 - beta)
@@ -59,6 +61,17 @@ def pin_adamw_decay_only(adamw=E.adamw_step):
     assert np.array_equal(th, theta * (1 - 0.1 * 0.5)) and not m.any() and not v.any()
 
 
+def pin_adamw_first_step_with_decay(adamw=E.adamw_step):
+    """Decay and gradient both non-zero: the decoupled decay multiplies the weight as it was
+    before the step, so step 1 from zero moments lands on theta (1 - lr wd) - lr g / (|g| + eps);
+    decaying the stepped weight instead is off by lr wd times the move."""
+    theta, g = _draw(129, 7)
+    for lr, wd in ((0.1, 0.5), (1e-3, 0.1)):
+        th, m, v = adamw(theta, g, np.zeros_like(g), np.zeros_like(g), 1, lr, 0.9, 0.999, 1e-8, wd)
+        want = theta * (1 - lr * wd) - lr * g / (np.abs(g) + 1e-8)
+        assert np.allclose(th, want, rtol=0, atol=1e-15), (lr, wd)
+
+
 def pin_lion_unit_moves(lion=E.lion_step):
     theta, g = _draw(301, 4)
     g[::7] = 0.0
@@ -86,8 +99,8 @@ def pin_lion_momentum(lion=E.lion_step):
         assert np.allclose(m, g * (1 - b2 ** k), rtol=1e-12, atol=0), k
 
 
-PINS = [pin_adamw_first_step, pin_adamw_constant_gradient, pin_adamw_decay_only, pin_lion_unit_moves,
-        pin_lion_momentum]
+PINS = [pin_adamw_first_step, pin_adamw_first_step_with_decay, pin_adamw_constant_gradient, pin_adamw_decay_only,
+        pin_lion_unit_moves, pin_lion_momentum]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -111,6 +124,11 @@ def _adamw_swapped_betas(theta, g, m, v, t, lr, b1, b2, eps, wd):
     return E.adamw_step(theta, g, m, v, t, lr, b2, b1, eps, wd)
 
 
+def _adamw_decay_after_step(theta, g, m, v, t, lr, b1, b2, eps, wd):
+    th, m2, v2 = E.adamw_step(theta, g, m, v, t, lr, b1, b2, eps, 0.0)
+    return th * (1 - lr * wd), m2, v2
+
+
 def _lion_momentum_direction(theta, g, m, lr, b1, b2, wd):
     theta2, m2 = E.lion_step(theta, g, m, lr, b1, b2, wd)
     return theta * (1 - lr * wd) - lr * np.sign(m2), m2
@@ -124,6 +142,7 @@ def _lion_swapped_betas(theta, g, m, lr, b1, b2, wd):
     (_adamw_no_bias_correction, [pin_adamw_first_step, pin_adamw_constant_gradient]),
     (_adamw_coupled_decay, [pin_adamw_decay_only]),
     (_adamw_swapped_betas, [pin_adamw_first_step, pin_adamw_constant_gradient]),
+    (_adamw_decay_after_step, [pin_adamw_first_step_with_decay]),
     (_lion_momentum_direction, [pin_lion_unit_moves]),
     (_lion_swapped_betas, [pin_lion_momentum, pin_lion_unit_moves]),
 ])

@@ -1,33 +1,42 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times,
+through every step of each workload's sequence (steady state: warm-started Q', M != 0).
 
 The oracle recomputes sampled matrices of every stack one by one (teacher-forced:
-from the exact pre-step state bits the GPU used); properties that hold at any
-size are checked on every matrix on the GPU in fp64 (torch used as a checker only):
+from the exact pre-step state bits the GPU used), with the update checks of the
+harness (dM, dX, and X' element by element against the GPU's own P and Q');
+properties that hold at any size are checked on every matrix on the GPU in fp64
+(torch used as a checker only):
   * P^T P = I for the orthonormal factor left in the workspace,
   * full rank (r = min(m, n)): M' = mu B exactly in exact arithmetic,
   * no matrix flagged non-finite.
+Free-running errors (the first sampled matrix also stepped by the oracle from its own
+fp64 state, never reset to the GPU's) are printed beside the teacher-forced ones and
+not judged: the pages give no multi-step trajectory to pin them to.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import compare_step, to_numpy, to_torch, tol_for
+from oracle import dion_step
+from tests.harness import check_errs, compare_step, rel, to_numpy, to_torch, tol_for
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run(wl, device, steps, sample):
+def _run(wl, device, steps, samples):
     import torch
     import rank_orthonormalized_optimizer_amd as dion
     out = []
     for gi, g in enumerate(wl.groups):
         print(f"[fullsize] {wl.name} group {gi} {g}: inputs", flush=True)
         X, M, Q = W.make_state(wl, gi)
+        idx = sorted(set(i for i in samples(g.batch) if 0 <= i < g.batch))
+        f0 = idx[0]
+        free = {"X": W.to_f64(X[f0], wl.x_dtype), "M": M[f0].astype(np.float64), "Q": Q[f0].astype(np.float64)}
         Xd, Md, Qd = to_torch(X, device), to_torch(M, device), to_torch(Q, device)
         del X, M, Q
         flags = torch.zeros(g.batch, dtype=torch.int32, device=device)
         ws = dion.api.workspace_for(g.m, g.n, g.batch, g.rank, device)
-        idx = sorted(set([0, g.batch - 1][:sample]))
         for t in range(1, steps + 1):
             G = W.make_grad(wl, gi, t)
             Gd = to_torch(G, device)
@@ -40,23 +49,35 @@ def _run(wl, device, steps, sample):
             P = ws[:4 * g.batch * g.m * g.rank].view(torch.float32).view(g.batch, g.m, g.rank)
             # properties on every matrix
             orth = 0.0
+            eye = torch.eye(g.rank, dtype=torch.float64, device=device)
             for i in range(g.batch):
                 Pi = P[i].double()
-                orth = max(orth, float((Pi.T @ Pi - torch.eye(g.rank, dtype=torch.float64, device=device))
-                                       .abs().max()))
+                orth = max(orth, float((Pi.T @ Pi - eye).abs().max()))
+            del eye
             fr = None
             if Bpre is not None:
                 fr = max(float(torch.linalg.norm(Md[i].double() - wl.mu * Bpre[i]) / torch.linalg.norm(Bpre[i]))
                          for i in range(g.batch))
+                del Bpre
             fl = to_numpy(flags)
             post = {"X": to_numpy(Xd[idx]), "M": to_numpy(Md[idx]), "Q": to_numpy(Qd[idx]), "P": to_numpy(P[idx])}
             print(f"[fullsize] {wl.name} group {gi} step {t}: oracle on matrices {idx}", flush=True)
             errs = compare_step(wl, pre, post, G[idx], g.rank)
-            out.append(dict(group=gi, step=t, errs=errs, orth=orth, fullrank_M=fr, flags=fl))
+            # free-running: the oracle's own trajectory for matrix f0
+            fo = dion_step(free["X"], W.to_f64(G[f0], wl.g_dtype), free["M"], free["Q"], wl.mu, wl.lr, wl.eps)
+            free = {"X": fo["X"], "M": fo["M"], "Q": fo["Q"]}
+            k0 = idx.index(f0)
+            P0 = post["P"][k0].astype(np.float64)
+            freerun = {"PQ": rel(P0 @ post["Q"][k0].astype(np.float64).T, fo["P"] @ fo["Q"].T),
+                       "M": rel(post["M"][k0].astype(np.float64), fo["M"]),
+                       "X": rel(W.to_f64(post["X"][k0], wl.x_dtype), fo["X"])}
+            out.append(dict(group=gi, step=t, errs=errs, orth=orth, fullrank_M=fr, flags=fl, free=freerun))
             print(f"[fullsize]   orth={orth:.2e} fullrank_M={fr} flags={np.unique(fl).tolist()} "
-                  f"errs={[{k: round(v, 9) for k, v in e.items() if k != 'rank_deficient'} for e in errs]}",
-                  flush=True)
+                  f"teacher-forced={[{k: v for k, v in e.items() if k != 'rank_deficient'} for e in errs]} "
+                  f"free-running(matrix {f0})={freerun}", flush=True)
             del Gd, G
+        del Xd, Md, Qd, ws, flags
+        torch.cuda.empty_cache()
     return out
 
 
@@ -68,21 +89,35 @@ def _check(wl, res):
         if r["fullrank_M"] is not None:
             assert r["fullrank_M"] <= tol, r
         for e in r["errs"]:
-            for k in ("PQ", "M", "X"):
-                assert e[k] <= tol, (r["group"], r["step"], k, e[k])
+            check_errs(e, tol, f"group {r['group']} step {r['step']}")
 
 
-@pytest.mark.parametrize("wid,steps,sample", [(1, 3, 1), (2, 2, 2), (4, 1, 1)])
-def test_full_size(cuda, wid, steps, sample):
-    wl = W.get(wid)
-    _check(wl, _run(wl, cuda, steps, sample))
+def test_full_size_single_matrix(cuda):
+    """256 x 512, r = 32: all ten steps."""
+    wl = W.get(1)
+    _check(wl, _run(wl, cuda, wl.steps, lambda b: [0]))
+
+
+def test_full_size_attention_stack(cuda):
+    """24 x 1024^2, r = 256: all five steps, three matrices sampled."""
+    wl = W.get(2)
+    _check(wl, _run(wl, cuda, wl.steps, lambda b: [0, b // 2, b - 1]))
 
 
 def test_full_size_bf16_llama_stack(cuda):
+    """64 x 2048^2, 32 x 5632 x 2048, 16 x 2048 x 5632 (bf16 X, G), r = 256: all three steps."""
     wl = W.get(3)
-    _check(wl, _run(wl, cuda, 1, 1))
+    _check(wl, _run(wl, cuda, wl.steps, lambda b: [0, b - 1]))
+
+
+def test_full_size_mlp_matrix(cuda):
+    """8192 x 28672, r = 512: all three steps."""
+    wl = W.get(4)
+    _check(wl, _run(wl, cuda, wl.steps, lambda b: [0]))
 
 
 def test_full_size_full_rank(cuda):
+    """8 x 4096^2 at full rank: all three steps, first and last matrix against the oracle,
+    P^T P = I and M' = mu B on all eight."""
     wl = W.get(5)
-    _check(wl, _run(wl, cuda, 1, 1))
+    _check(wl, _run(wl, cuda, wl.steps, lambda b: [0, b - 1]))

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import compare_step, to_numpy, to_torch, tol_for
+from tests.harness import TOL_KEYS, check_errs, compare_step, to_numpy, to_torch, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +41,12 @@ def check(report, tol):
     worst = {}
     for gi, t, errs, flags in report:
         for i, e in enumerate(errs):
-            assert not (flags[i] & 2), f"group {gi} step {t} matrix {i}: non-finite flag"
-            for k in ("PQ", "M", "X"):
+            where = f"group {gi} step {t} matrix {i}"
+            assert not (flags[i] & 2), f"{where}: non-finite flag"
+            for k in TOL_KEYS + ("Xband",):
                 if k in e:
                     worst[k] = max(worst.get(k, 0.0), e[k])
-                    assert e[k] <= tol, f"group {gi} step {t} matrix {i}: {k} rel err {e[k]:.3e} > {tol}"
+            check_errs(e, tol, where)
             if "orth" in e:
                 assert e["orth"] <= 1e-4, f"group {gi} step {t} matrix {i}: |P^T P - I| = {e['orth']:.3e}"
     print("worst", worst, flush=True)
