@@ -87,6 +87,8 @@ enum {
     DION_ERR_DTYPE = -8,      /* x_dtype or g_dtype not a dion_dtype */
     DION_ERR_OPTION = -9,     /* unknown option bit, contradictory options, or
                                  DION_OPT_HOUSEHOLDER with rank > 4096 */
+    DION_ERR_SCRATCH = -10,   /* dion_step_batched_noalloc: the stack needs more than the
+                                 DION_NOALLOC_SCRATCH_BYTES of built-in scratch */
     DION_ERR_HIP = -100       /* -100 - hipError_t for a failed HIP call */
 };
 
@@ -187,6 +189,29 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q,
                                void* workspace, size_t workspace_bytes,
                                int32_t* flags, uint32_t options, void* stream,
                                void* const* events);
+
+/*
+ * dion_step_batched without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, step, results and status codes as dion_step_batched, minus the workspace; the
+ * scratch is a static device array of DION_NOALLOC_SCRATCH_BYTES built into the library, one per
+ * GPU, held until the process ends.  Nothing is allocated by the call.
+ *   - DION_ERR_SCRATCH (checked on the host before anything is enqueued) when
+ *     dion_workspace_size(m, n, batch, rank) exceeds DION_NOALLOC_SCRATCH_BYTES;
+ *   - the stack runs as one chunk on `stream`: chunk option bits above 1 give DION_ERR_OPTION;
+ *   - every call on a GPU shares that GPU's scratch: calls that may overlap on one GPU (other
+ *     streams, other threads) race and must be ordered by the caller;
+ *   - the first call on a device looks up the scratch's device address (hipGetSymbolAddress);
+ *     make that first call outside graph capture.
+ *   - P is not returned (dion_step_batched leaves it in its workspace).
+ * The scratch's contents on entry do not matter: nothing in it has to start at zero.
+ */
+#define DION_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dion_step_batched_noalloc(void* X, const void* G, float* M, float* Q,
+                              int64_t m, int64_t n, int64_t batch, int64_t rank,
+                              float mu, float lr, float eps,
+                              int x_dtype, int g_dtype,
+                              int32_t* flags, uint32_t options, void* stream);
 
 /*
  * The parameters Dion does not take.  The rivista.ai page (the paragraph

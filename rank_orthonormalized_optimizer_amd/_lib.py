@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdion_mi3
 F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_HYPER, ERR_ALIGN = -1, -2, -3, -4, -5
-ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_HIP = -6, -7, -8, -9, -100
+ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_SCRATCH, ERR_HIP = -6, -7, -8, -9, -10, -100
+NOALLOC_SCRATCH_BYTES = 64 << 20
 OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32, OPT_HOUSEHOLDER, OPT_SPECTRAL_SHIFT = 1, 2, 4, 16, 32
 OPT_CHUNKS_SHIFT = 8
 
@@ -36,7 +37,8 @@ NUM_PHASES = 10
 PHASES = ("init", "f32_product", "f32_qr", "f32_backproject", "f64_product", "f64_qr", "f64_backproject",
           "norms", "update", "flags")
 
-EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_adamw_step",
+EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_step_batched_noalloc",
+           "dion_adamw_step",
            "dion_lion_step", "dion_lambda_max_workspace_size", "dion_lambda_max_batched", "dion_strerror",
            "dion_version")
 
@@ -70,6 +72,9 @@ def load() -> ctypes.CDLL:
     lib.dion_step_batched_profiled.restype = ctypes.c_int
     lib.dion_step_batched_profiled.argtypes = lib.dion_step_batched.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     f32, i32 = ctypes.c_float, ctypes.c_int
+    lib.dion_step_batched_noalloc.restype = ctypes.c_int
+    lib.dion_step_batched_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, f32, i32, i32, vp,
+                                              ctypes.c_uint32, vp]
     lib.dion_adamw_step.restype = ctypes.c_int
     lib.dion_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, i32, i32, vp]
     lib.dion_lion_step.restype = ctypes.c_int
@@ -112,6 +117,15 @@ def step_batched_raw(X: int, G: int, M: int, Q: int, m: int, n: int, batch: int,
         return int(load().dion_step_batched(*args))
     arr = (ctypes.c_void_p * (NUM_PHASES + 1))(*[int(e) for e in events])
     return int(load().dion_step_batched_profiled(*args, arr))
+
+
+def step_batched_noalloc_raw(X: int, G: int, M: int, Q: int, m: int, n: int, batch: int, rank: int,
+                             mu: float, lr: float, eps: float, x_dtype: int, g_dtype: int, flags: int, options: int,
+                             stream: int) -> int:
+    """dion_step_batched_noalloc (the built-in scratch, no workspace) with integer addresses; returns the
+    status code."""
+    return int(load().dion_step_batched_noalloc(X or None, G or None, M or None, Q or None, m, n, batch, rank, mu,
+                                                lr, eps, x_dtype, g_dtype, flags or None, options, stream or None))
 
 
 def adamw_step_raw(param: int, grad: int, exp_avg: int, exp_avg_sq: int, n: int, t: int, lr: float, beta1: float,

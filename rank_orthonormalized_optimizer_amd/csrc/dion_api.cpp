@@ -26,6 +26,48 @@ Range span(const void* p, double bytes) {
 
 }  // namespace
 
+namespace dion {
+
+int check_step_args(int64_t m, int64_t n, int64_t batch, int64_t rank, float mu, float lr, float eps, int x_dtype,
+                    int g_dtype, uint32_t options, Plan* p) {
+    if (m < 1 || n < 1 || batch < 0) return DION_ERR_SHAPE;
+    if (rank < 0 || rank > (m < n ? m : n)) return DION_ERR_RANK;
+    if (!(mu >= 0.0f && mu < 1.0f) || !isfinite(lr) || !isfinite(eps) || !(eps >= 0.0f)) return DION_ERR_HYPER;
+    if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
+        return DION_ERR_DTYPE;
+    const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 | DION_OPT_HOUSEHOLDER |
+                           DION_OPT_SPECTRAL_SHIFT | (15u << DION_OPT_CHUNKS_SHIFT);
+    if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)) ||
+        ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)) ||
+        ((options & DION_OPT_SPECTRAL_SHIFT) && (options & DION_OPT_FORCE_F32)))
+        return DION_ERR_OPTION;
+    if (!make_plan(m, n, batch, rank, p)) return DION_ERR_SHAPE;
+    return DION_OK;
+}
+
+int check_step_buffers(const Plan& p, const void* X, const void* G, const float* M, const float* Q, int x_dtype,
+                       int g_dtype, const void* workspace, size_t workspace_bytes, const int32_t* flags) {
+    if (!X || !G || !M || (p.r > 0 && !Q) || !workspace) return DION_ERR_NULL;
+    if (((uintptr_t)X | (uintptr_t)G | (uintptr_t)M | (uintptr_t)Q | (uintptr_t)flags) & 15u) return DION_ERR_ALIGN;
+    if ((uintptr_t)workspace & 255u) return DION_ERR_ALIGN;
+    if (workspace_bytes < p.total) return DION_ERR_WORKSPACE;
+    const double mn = (double)p.b * (double)p.m * (double)p.n;
+    const Range rs[6] = {
+        span(X, mn * (x_dtype == DION_BF16 ? 2 : 4)),
+        span(G, mn * (g_dtype == DION_BF16 ? 2 : 4)),
+        span(M, mn * 4),
+        span(Q, p.r > 0 ? (double)p.b * (double)p.n * (double)p.r * 4 : 0.0),
+        span(workspace, (double)p.total),
+        span(flags, flags ? (double)p.b * 4 : 0.0),
+    };
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    return DION_OK;
+}
+
+}  // namespace dion
+
 extern "C" {
 
 size_t dion_workspace_size(int64_t m, int64_t n, int64_t batch, int64_t rank) {
@@ -38,36 +80,11 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64
                                int64_t rank, float mu, float lr, float eps, int x_dtype, int g_dtype,
                                void* workspace, size_t workspace_bytes, int32_t* flags, uint32_t options,
                                void* stream, void* const* events) {
-    if (m < 1 || n < 1 || batch < 0) return DION_ERR_SHAPE;
-    if (rank < 0 || rank > (m < n ? m : n)) return DION_ERR_RANK;
-    if (!(mu >= 0.0f && mu < 1.0f) || !isfinite(lr) || !isfinite(eps) || !(eps >= 0.0f)) return DION_ERR_HYPER;
-    if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
-        return DION_ERR_DTYPE;
-    const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 | DION_OPT_HOUSEHOLDER |
-                           DION_OPT_SPECTRAL_SHIFT | (15u << DION_OPT_CHUNKS_SHIFT);
-    if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)) ||
-        ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)) ||
-        ((options & DION_OPT_SPECTRAL_SHIFT) && (options & DION_OPT_FORCE_F32)))
-        return DION_ERR_OPTION;
     dion::Plan p;
-    if (!dion::make_plan(m, n, batch, rank, &p)) return DION_ERR_SHAPE;
-    if (batch == 0) return DION_OK;
-    if (!X || !G || !M || (rank > 0 && !Q) || !workspace) return DION_ERR_NULL;
-    if (((uintptr_t)X | (uintptr_t)G | (uintptr_t)M | (uintptr_t)Q | (uintptr_t)flags) & 15u) return DION_ERR_ALIGN;
-    if ((uintptr_t)workspace & 255u) return DION_ERR_ALIGN;
-    if (workspace_bytes < p.total) return DION_ERR_WORKSPACE;
-    const double mn = (double)batch * (double)m * (double)n;
-    const Range rs[6] = {
-        span(X, mn * (x_dtype == DION_BF16 ? 2 : 4)),
-        span(G, mn * (g_dtype == DION_BF16 ? 2 : 4)),
-        span(M, mn * 4),
-        span(Q, rank > 0 ? (double)batch * (double)n * (double)rank * 4 : 0.0),
-        span(workspace, (double)p.total),
-        span(flags, flags ? (double)batch * 4 : 0.0),
-    };
-    for (int i = 0; i < 6; ++i)
-        for (int j = i + 1; j < 6; ++j)
-            if (overlap(rs[i], rs[j])) return DION_ERR_OVERLAP;
+    int st = dion::check_step_args(m, n, batch, rank, mu, lr, eps, x_dtype, g_dtype, options, &p);
+    if (st != DION_OK || batch == 0) return st;
+    st = dion::check_step_buffers(p, X, G, M, Q, x_dtype, g_dtype, workspace, workspace_bytes, flags);
+    if (st != DION_OK) return st;
     const int e = dion::run_step(p, X, G, M, Q, mu, lr, eps, x_dtype == DION_BF16, g_dtype == DION_BF16,
                                  (char*)workspace, flags, options, stream, events);
     return e ? DION_ERR_HIP - e : DION_OK;
@@ -168,6 +185,8 @@ const char* dion_strerror(int status) {
         case DION_ERR_WORKSPACE: return "workspace smaller than dion_workspace_size()";
         case DION_ERR_DTYPE: return "unsupported dtype (DION_F32 or DION_BF16)";
         case DION_ERR_OPTION: return "unknown or contradictory option bits";
+        case DION_ERR_SCRATCH: return "stack too large for the built-in scratch of dion_step_batched_noalloc "
+                                      "(DION_NOALLOC_SCRATCH_BYTES); call dion_step_batched with a workspace";
         default: break;
     }
     if (status <= DION_ERR_HIP) return "HIP runtime error (status = -100 - hipError_t)";

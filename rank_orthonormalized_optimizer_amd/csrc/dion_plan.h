@@ -137,6 +137,14 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     return true;
 }
 
+// Host-side validation of a dion_step_batched call, before anything touches the GPU (DION_*
+// status codes).  check_step_args: sizes, hyper-parameters, dtypes and options, and the
+// workspace plan.  check_step_buffers: null pointers, alignment, workspace size, overlaps.
+int check_step_args(int64_t m, int64_t n, int64_t batch, int64_t rank, float mu, float lr, float eps, int x_dtype,
+                    int g_dtype, uint32_t options, Plan* p);
+int check_step_buffers(const Plan& p, const void* X, const void* G, const float* M, const float* Q, int x_dtype,
+                       int g_dtype, const void* workspace, size_t workspace_bytes, const int32_t* flags);
+
 // Run the step (arguments already validated).  Returns a hipError_t value.
 int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
              float mu, float lr, float eps, int x_bf16, int g_bf16,
