@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the Dion step on one MI355X.
 
-A "step" is one Dion update of every matrix of the workload (all stacks),
-with gradients already resident in HBM.  The default workload is the
-rank-fraction-1/4 attention stack: 24 fp32 matrices of 1024 x 1024 at r = 256
-with low-rank-plus-noise gradients (see workloads/).  Prints one JSON line.
+A "step" is one Dion update of every matrix of a workload (all its stacks), with the
+inputs already resident in HBM.  The headline workload is the rank-fraction-1/4
+attention stack: 24 fp32 matrices of 1024 x 1024 at r = 256 with low-rank-plus-noise
+gradients (see workloads/).  The default run also measures every other workload and
+reports them in a "configs" array.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--configs 1,2,3,4,5 | none]
+                  [--no-cpu-baseline] [--eager]
 
-The K timed steps run twice: eagerly (one host launch per kernel, with the library's phase
-events) and as replays of the same steps captured in HIP graphs (one graph per resident
-gradient).  The replays set the value; both times are reported ("eager_ms_per_step",
+Inputs are drawn on the device with the workloads' recipes (workloads.make_state_device and
+make_grad_device: same distributions as the host generators the parity tests use, drawn by a
+seeded torch generator); --host-inputs draws them on the host instead.
+
+Per workload the K timed steps run twice: eagerly (one host launch per kernel, with the
+library's phase events) and as replays of the same steps captured in HIP graphs (one graph per
+resident gradient).  The replays set the value; both times are reported ("eager_ms_per_step",
 "graph_ms_per_step"), and --eager times the eager steps only.
 
-Metric: updates/s (steps per second over the whole workload), with the
-effective parameter bandwidth (algorithmic bytes / step time) and its share of
-the 8 TB/s HBM peak alongside.  The "roofline" entry times the dominant kernel
-live (HIP events recorded by the library at its phase boundaries, on the
-stream the kernels run on); the "cpu_baseline" entry times the fp64 oracle on
+Metric: updates/s (steps per second over the whole workload), with the effective parameter
+bandwidth (algorithmic bytes / step time) and its share of the 8 TB/s HBM peak alongside.
+Every phase of the step is priced against the roofline that bounds it ("phase_roofline"; the
+phase times come from HIP events the library records at its phase boundaries, on the stream
+the kernels run on), the dominant single-kernel phase is the "roofline" entry, and the
+multi-kernel QR phase has its own "qr_roofline".  "cpu_baseline" times the fp64 oracle on
 the host cores over a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -26,11 +33,14 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3, "bf16": 2500.0}
+METRIC = "Dion updates/s and effective param GB/s (% HBM roofline) at rank frac 1/4"
+HEADLINE = 2
 
 
 def algorithmic_bytes(wl) -> float:
@@ -82,22 +92,39 @@ def measured_traffic(workload: str, phase: str):
     return None if ph is None else ph["bytes_per_launch"]
 
 
-def blas_threads() -> int:
+def blas_info() -> dict:
+    """BLAS vendor, version and thread count numpy runs on (threadpoolctl), with the host's CPU."""
+    info = {"cpu_count": os.cpu_count(), "cpu_model": platform.processor() or None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
-        return int(max(n)) if n else (os.cpu_count() or 1)
+        blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(max(d.get("num_threads", 0) for d in blas))
     except Exception:
-        return os.cpu_count() or 1
+        pass
+    info.setdefault("blas_threads", os.cpu_count() or 1)
+    return info
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
+def blas_threads() -> int:
+    return int(blas_info()["blas_threads"])
+
+
+def cpu_baseline(wl, samples, budget_s: float) -> dict:
     """The fp64 oracle as it stands, on the host cores, over a bounded sample of the workload.
 
-    Every matrix of every stack is stepped once (step-1 inputs); the per-stack pass is
-    repeated while the budget lasts, then the mean time per full step is reported.
-    Stacks whose single matrix already exceeds the budget are sampled: the per-matrix
-    time of the matrices that fit is scaled to the whole stack.
+    ``samples``: per stack, the step-1 inputs (X, G, M, Q as host arrays) of its first matrix.
+    Each stack's matrix is stepped while its share of the budget lasts (at least once); the
+    mean time per matrix is scaled to the stack size and summed over the stacks.
     """
     import numpy as np
 
@@ -105,30 +132,23 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     from oracle import dion_step
     t_all = time.perf_counter()
     per_group = []
-    for gi, g in enumerate(wl.groups):
-        X, M, Q = W.make_state(wl, gi)
-        G = W.make_grad(wl, gi, 1)
-        args = [(W.to_f64(X[i], wl.x_dtype), W.to_f64(G[i], wl.g_dtype), M[i].astype(np.float64),
-                 Q[i].astype(np.float64)) for i in range(g.batch)]
+    for (g, (X, G, M, Q)) in zip(wl.groups, samples):
+        args = (W.to_f64(X, wl.x_dtype), W.to_f64(G, wl.g_dtype), M.astype(np.float64), Q.astype(np.float64))
         share = budget_s / len(wl.groups)
         times, t0 = [], time.perf_counter()
-        while True:
-            for i in range(g.batch):
-                t1 = time.perf_counter()
-                dion_step(*args[i], wl.mu, wl.lr, wl.eps)
-                times.append(time.perf_counter() - t1)
-                if time.perf_counter() - t0 > share and len(times) >= 1:
-                    break
-            if time.perf_counter() - t0 > share:
-                break
+        while not times or time.perf_counter() - t0 < share:
+            t1 = time.perf_counter()
+            dion_step(*args, wl.mu, wl.lr, wl.eps)
+            times.append(time.perf_counter() - t1)
         per_group.append((g, float(np.mean(times)), len(times)))
     step_s = sum(g.batch * t for g, t, _ in per_group)
-    sample = "; ".join(f"{k} matrix steps of the {g.batch}x{g.m}x{g.n} r={g.rank} stack"
+    sample = "; ".join(f"{k} steps of one matrix of the {g.batch}x{g.m}x{g.n} r={g.rank} stack"
                        for g, _, k in per_group)
-    return {"value": 1.0 / step_s, "unit": "updates/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": sample + f" (step-1 inputs, fp64 numpy/OpenBLAS; mean time per matrix x stack size; "
+    info = blas_info()
+    return {"value": 1.0 / step_s, "unit": "updates/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": sample + f" (step-1 inputs, fp64 numpy; mean time per matrix x stack size; "
                                f"{time.perf_counter() - t_all:.1f} s of CPU work)",
-            "s_per_step": step_s}
+            "s_per_step": step_s, "host": info}
 
 
 EW_N = 64 << 20    # elements of the element-wise measurement (256 MiB per fp32 array)
@@ -250,39 +270,64 @@ def spectral_block(dev, stream, reps: int = 10, with_cpu: bool = True) -> dict:
     return out
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--grads", type=int, default=3, help="distinct resident gradients cycled through")
-    ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
-    ap.add_argument("--no-hint", action="store_true",
-                    help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
-    ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the eager steps only (default: also capture them as HIP graphs and time the replays, "
-                         "which set the reported value)")
-    ap.add_argument("--no-elementwise", action="store_true",
-                    help="skip the AdamW / Lion measurement (the parameters Dion does not take)")
-    ap.add_argument("--elementwise-only", action="store_true",
-                    help="only the AdamW / Lion measurement, printed as one JSON line")
-    ap.add_argument("--no-spectral", action="store_true",
-                    help="skip the lambda_max estimate measurement (the spectral shift of the fallback)")
-    ap.add_argument("--spectral-only", action="store_true",
-                    help="only the lambda_max estimate measurement, printed as one JSON line")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the Dion step here has no multi-GPU path.", file=sys.stderr)
-        return 2
+SPLIT6 = 6.0   # bf16 MFMA products per fp32 product in the exact split form the fp32 contractions use
 
+
+def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
+    """Every phase of the step against the roofline that bounds it.  ``phase_ms``: device time
+    per step of each phase, summed over the stacks; the flops and bytes are algorithmic and
+    counted for the matrices each chain actually owned (flags after the last timed step)."""
+    f64m = [int((s["flags"] & dion.FLAG_F64).ne(0).sum()) for s in stacks]
+    out = {}
+
+    def add(name, kind, amount, peak_key, factor=1.0, what=""):
+        ms = phase_ms[name]
+        secs = ms * 1e-3
+        ent = {"ms": ms, "what": what}
+        if kind == "flops":
+            exe = amount * factor
+            ach = exe / secs / 1e12 if secs > 0 and amount > 0 else 0.0
+            ent.update({"bound": "mfma", "dtype": peak_key, "algorithmic_flops": amount,
+                        "executed_flops": exe, "achieved": ach, "peak": PEAK_TFLOPS[peak_key], "unit": "TFLOP/s",
+                        "frac": ach / PEAK_TFLOPS[peak_key]})
+        else:
+            ach = amount / secs / 1e9 if secs > 0 and amount > 0 else 0.0
+            ent.update({"bound": "hbm", "algorithmic_bytes": amount, "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS})
+        out[name] = ent
+
+    mnr32 = mnr64 = qr32 = qr64 = nb = ub = 0.0
+    for s, k64 in zip(stacks, f64m):
+        g = s["g"]
+        m, n, r, b = g.m, g.n, g.rank, g.batch
+        k32 = b - k64
+        mnr32 += k32 * m * n * r
+        mnr64 += k64 * m * n * r
+        qrf = 6.0 * m * r * r + 2.0 * r ** 3 / 3.0
+        qr32 += k32 * qrf
+        qr64 += k64 * qrf
+        nb += k32 * n * r * 8.0 + k64 * (n * r * 16.0 + m * r * 12.0)
+        bx = 2 if wl.x_dtype == "bf16" else 4
+        ub += b * (m * n * (bx + 8 + 2 * bx) + 4.0 * (m + 2 * n) * r)
+    add("f32_product", "flops", 2.0 * mnr32, "bf16", SPLIT6, "P0 = (M+G) Q, fp32 as six bf16 MFMA products")
+    add("f32_qr", "flops", qr32, "f32", 1.0, "CholeskyQR2 of the fp32 chain, 6 m r^2 + 2 r^3 / 3 per matrix")
+    add("f32_backproject", "flops", 2.0 * mnr32, "bf16", SPLIT6, "R = (M+G)^T P, fp32 as six bf16 MFMA products")
+    add("f64_product", "flops", 2.0 * mnr64, "f64", 1.0, "P0 = (M+G) Q, fp64 MFMA")
+    add("f64_qr", "flops", qr64, "f64", 1.0, "CholeskyQR2 (shifted CholeskyQR3) of the fp64 chain, "
+                                             "6 m r^2 + 2 r^3 / 3 per matrix")
+    add("f64_backproject", "flops", 2.0 * mnr64, "f64", 1.0, "R = (M+G)^T P, fp64 MFMA")
+    add("norms", "bytes", nb, "hbm", 1.0, "column norms of R, Q' = R c; fp64-chain P, R rounded to fp32")
+    add("update", "flops", 4.0 * (mnr32 + mnr64), "bf16", SPLIT6,
+        "P R^T and P Q'^T of the M, X update, fp32 as six bf16 MFMA products")
+    out["update"]["hbm"] = {"algorithmic_bytes": ub,
+                            "achieved": ub / (phase_ms["update"] * 1e-3) / 1e9 if phase_ms["update"] > 0 else 0.0,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    out["update"]["hbm"]["frac"] = out["update"]["hbm"]["achieved"] / HBM_PEAK_GBS
+    return out
+
+
+def measure(wl, dev, stream, args, cpu_s: float, host_inputs: bool) -> dict:
+    """Time one workload: W warm-up steps, K eager steps with phase events, K graph replays."""
     import numpy as np
     import torch
 
@@ -290,37 +335,23 @@ def main() -> int:
     import workloads as W
     from rank_orthonormalized_optimizer_amd._lib import NUM_PHASES, PHASES
     from rank_orthonormalized_optimizer_amd.api import workspace_for
+    from tests.harness import to_numpy, to_torch
 
-    dev = torch.device("cuda:0")
-    if args.spectral_only:
-        print(json.dumps(spectral_block(dev, torch.cuda.current_stream(dev), with_cpu=not args.no_cpu_baseline)),
-              flush=True)
-        return 0
-    if args.elementwise_only:
-        print(json.dumps(elementwise_block(dev, torch.cuda.current_stream(dev), with_cpu=not args.no_cpu_baseline)),
-              flush=True)
-        return 0
-    wl = W.get(args.workload)
-    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
-
-    def dev_t(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    stacks = []
+    print(f"[bench] workload {wl.name}: inputs", file=sys.stderr, flush=True)
+    stacks, samples = [], []
     for gi, g in enumerate(wl.groups):
-        X, M, Q = W.make_state(wl, gi)
-        ngrad = 1 if wl.grad == "decaying_spectrum" else args.grads   # Haar factors cost seconds each
-        grads = []
-        for t in range(1, ngrad + 1):
-            print(f"[bench] gradient {t}/{ngrad} of stack {gi}", file=sys.stderr, flush=True)
-            grads.append(dev_t(W.make_grad(wl, gi, t)))
-        stacks.append(dict(g=g, X=dev_t(X), M=dev_t(M), Q=dev_t(Q), G=grads,
-                           flags=torch.zeros(g.batch, dtype=torch.int32, device=dev),
+        ngrad = 1 if wl.grad == "decaying_spectrum" else args.grads
+        if host_inputs:
+            X, M, Q = (to_torch(a, dev) for a in W.make_state(wl, gi))
+            grads = [to_torch(W.make_grad(wl, gi, t), dev) for t in range(1, ngrad + 1)]
+        else:
+            X, M, Q = W.make_state_device(wl, gi, dev)
+            grads = [W.make_grad_device(wl, gi, t, dev) for t in range(1, ngrad + 1)]
+        samples.append((to_numpy(X[0]), to_numpy(grads[0][0]), to_numpy(M[0]), to_numpy(Q[0])))
+        stacks.append(dict(g=g, X=X, M=M, Q=Q, G=grads, flags=torch.zeros(g.batch, dtype=torch.int32, device=dev),
                            ws=workspace_for(g.m, g.n, g.batch, g.rank, dev)))
+    torch.cuda.synchronize()
     opts = (0 if args.no_sticky else dion.OPT_STICKY_F64) | ((args.chunks & 15) << 8)
-    stream = torch.cuda.current_stream(dev)
     for s in stacks:   # what DionStack does: skip launching the fp32 chain once a stack is all-fp64
         s["hint"] = None if (args.no_sticky or args.no_hint) else dion.StickyF64Hint(s["flags"])
 
@@ -334,18 +365,10 @@ def main() -> int:
             if s["hint"] is not None:
                 s["hint"].after_step(stream)
 
-    if args.calibrate_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written", file=sys.stderr, flush=True)
-        del src, dst
-    print("[bench] warmup", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: warmup", file=sys.stderr, flush=True)
     for k in range(args.warmup):
         one_step(k)
     torch.cuda.synchronize()
-
     # phase events for every call of the timed region (created by one record each beforehand)
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(NUM_PHASES + 1)] for _ in stacks]
            for _ in range(args.steps)]
@@ -354,10 +377,8 @@ def main() -> int:
             for e in call_e:
                 e.record(stream)
     torch.cuda.synchronize()
-
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] {wl.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t0.record(stream)
@@ -384,17 +405,16 @@ def main() -> int:
                 for s_ in stacks:
                     g_ = s_["g"]
                     o = opts if s_["hint"] is None else s_["hint"].options(opts)
-                    dion.step_(s_["X"], s_["G"][j % len(s_["G"])], s_["M"], s_["Q"], g_.rank, wl.mu, wl.lr, wl.eps,
-                               workspace=s_["ws"], flags=s_["flags"], options=o, stream=cap)
+                    dion.step_(s_["X"], s_["G"][j % len(s_["G"])], s_["M"], s_["Q"], g_.rank, wl.mu, wl.lr,
+                               wl.eps, workspace=s_["ws"], flags=s_["flags"], options=o, stream=cap)
                 gph.capture_end()
             graphs.append(gph)
         stream.wait_stream(cap)
         for k in range(2):
             graphs[(args.warmup + args.steps + k) % ng].replay()
         torch.cuda.synchronize()
-        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
+        print(f"[bench] {wl.name}: timing {args.steps} graph replays", file=sys.stderr, flush=True)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record(stream)
         for k in range(args.steps):
             graphs[(args.warmup + args.steps + 2 + k) % ng].replay()
@@ -412,80 +432,156 @@ def main() -> int:
                 phase_ms[p] += call_e[i].elapsed_time(call_e[i + 1]) / args.steps
     n64 = int(sum(int((s["flags"] & dion.FLAG_F64).ne(0).sum()) for s in stacks))
     nbad = int(sum(int((s["flags"] & dion.FLAG_NONFINITE).ne(0).sum()) for s in stacks))
+    nsh = int(sum(int((s["flags"] & dion.FLAG_SHIFTED).ne(0).sum()) for s in stacks))
+    nhh = int(sum(int((s["flags"] & dion.FLAG_HOUSEHOLDER).ne(0).sum()) for s in stacks))
     nmat = sum(g.batch for g in wl.groups)
-
-    # dominant single-kernel phase and its algorithmic flops per launch
-    mnr64 = sum(int((s["flags"] & dion.FLAG_F64).ne(0).sum()) * s["g"].m * s["g"].n * s["g"].rank
-                for s in stacks)
-    mnr = sum(g.batch * g.m * g.n * g.rank for g in wl.groups)
-    # The fp32 contractions run on the bf16 matrix cores as six bf16 products per fp32 product
-    # (fp32-accurate split): their executed bf16 flops are SPLIT6 x the algorithmic fp32 flops and
-    # are priced against the bf16 dense peak.
-    SPLIT6 = 6.0
-    kernels = {
-        "f64_product": ("f64", 2.0 * mnr64, 1.0, "P0 = (M+G) Q, fp64 MFMA"),
-        "f64_backproject": ("f64", 2.0 * mnr64, 1.0, "R = (M+G)^T P, fp64 MFMA"),
-        "f32_product": ("bf16", 2.0 * (mnr - mnr64), SPLIT6, "P0 = (M+G) Q, fp32 as six bf16 MFMA products"),
-        "f32_backproject": ("bf16", 2.0 * (mnr - mnr64), SPLIT6, "R = (M+G)^T P, fp32 as six bf16 MFMA products"),
-        "update": ("bf16", 4.0 * mnr, SPLIT6, "P R^T and P Q'^T of the M, X update, fp32 as six bf16 MFMA products"),
-    }
-    dom = max(kernels, key=lambda k: phase_ms[k])
-    dt_, alg_flops, factor, what = kernels[dom]
-    flops = alg_flops * factor
+    pr = phase_rooflines(wl, stacks, phase_ms, dion)
+    single = ("f32_product", "f32_backproject", "f64_product", "f64_backproject", "update")
+    dom = max(single, key=lambda k: phase_ms[k])
+    d = pr[dom]
     launches = len(stacks)
-    secs = phase_ms[dom] * 1e-3
-    achieved = flops / secs / 1e12 if secs > 0 else 0.0
-
+    roof = {"bound": d["bound"], "kernel": dom, "what": d["what"], "dtype": d["dtype"],
+            "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
+            "flops_per_launch": d["executed_flops"] / launches, "avg_launch_ms": phase_ms[dom] / launches,
+            "algorithmic_flops_per_launch": d["algorithmic_flops"] / launches,
+            "algorithmic_TFLOPs_per_s": (d["algorithmic_flops"] / (phase_ms[dom] * 1e-3) / 1e12
+                                         if phase_ms[dom] > 0 else 0.0),
+            "mfma_flops_per_algorithmic_flop": d["executed_flops"] / d["algorithmic_flops"]
+            if d["algorithmic_flops"] else None,
+            "traffic": measured_traffic(wl.name, dom), "traffic_unit": "bytes/launch"}
+    qr = pr["f64_qr"] if phase_ms["f64_qr"] >= phase_ms["f32_qr"] else pr["f32_qr"]
     eff_gbs = algorithmic_bytes(wl) / (ms * 1e-3) / 1e9
     dtype = "f32" if n64 == 0 else ("f64+f32" if n64 == nmat else "f32|f64+f32")
     if wl.x_dtype == "bf16":
         dtype += " (bf16 X, G)"
+    ent = {
+        "workload": wl.name,
+        "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],
+        "mu": wl.mu, "lr": wl.lr, "eps": wl.eps, "grad": wl.grad,
+        "inputs": "host generators" if host_inputs else "device generators (same recipes)",
+        "value": 1000.0 / ms, "unit": "updates/s", "ms_per_step": ms, "dtype": dtype,
+        "effective_param_GBps": eff_gbs, "pct_hbm_roofline": 100.0 * eff_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": algorithmic_bytes(wl),
+        "algorithmic_flops_per_step": algorithmic_flops(wl),
+        "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,
+        "params": wl.params(), "matrices": nmat, "fp64_chain_matrices": n64, "shifted_matrices": nsh,
+        "householder_matrices": nhh, "nonfinite_matrices": nbad,
+        "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
+        "phase_roofline": pr,
+        "launch": launch, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+        "wall_s_timed_region_eager": wall, "host_enqueue_ms_per_step": 1000.0 * enqueue / args.steps,
+        "roofline": roof,
+        "qr_roofline": {k: qr[k] for k in ("bound", "dtype", "achieved", "peak", "unit", "frac", "ms",
+                                           "algorithmic_flops", "what")},
+    }
+    del stacks
+    torch.cuda.empty_cache()
+    if cpu_s > 0:
+        print(f"[bench] {wl.name}: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        ent["cpu_baseline"] = cpu_baseline(wl, samples, cpu_s)
+    return ent
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5],
+                    help="the headline workload (default: the rank-fraction-1/4 attention stack)")
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="workloads also measured into the 'configs' array ('none' to skip)")
+    ap.add_argument("--host-inputs", action="store_true", help="draw inputs with the host generators")
+    ap.add_argument("--grads", type=int, default=3, help="distinct resident gradients cycled through")
+    ap.add_argument("--no-sticky", action="store_true", help="retry the fp32 chain every step")
+    ap.add_argument("--no-hint", action="store_true",
+                    help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
+    ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager steps only (default: also capture them as HIP graphs and time the replays, "
+                         "which set the reported value)")
+    ap.add_argument("--no-elementwise", action="store_true",
+                    help="skip the AdamW / Lion measurement (the parameters Dion does not take)")
+    ap.add_argument("--elementwise-only", action="store_true",
+                    help="only the AdamW / Lion measurement, printed as one JSON line")
+    ap.add_argument("--no-spectral", action="store_true",
+                    help="skip the lambda_max estimate measurement (the spectral shift of the fallback)")
+    ap.add_argument("--spectral-only", action="store_true",
+                    help="only the lambda_max estimate measurement, printed as one JSON line")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle budget of the headline workload")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0, help="oracle budget of each other workload")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the Dion step here has no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.spectral_only:
+        print(json.dumps(spectral_block(dev, stream, with_cpu=not args.no_cpu_baseline)), flush=True)
+        return 0
+    if args.elementwise_only:
+        print(json.dumps(elementwise_block(dev, stream, with_cpu=not args.no_cpu_baseline)), flush=True)
+        return 0
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written", file=sys.stderr, flush=True)
+        del src, dst
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    head = measure(W.get(args.workload), dev, stream, args, cpu, args.host_inputs)
     out = {
-        "metric": "Dion updates/s and effective param GB/s (% HBM roofline) at rank frac 1/4",
-        "value": 1000.0 / ms,
+        "metric": METRIC,
+        "value": head["value"],
         "unit": "updates/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": wl.name,
-                   "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],
-                   "mu": wl.mu, "lr": wl.lr, "eps": wl.eps, "grad": wl.grad,
-                   "sticky_fp64": not args.no_sticky,
-                   "host_fp64_hint": not (args.no_sticky or args.no_hint), "chunks": args.chunks or "auto"},
-        "effective_param_GBps": eff_gbs,
-        "pct_hbm_roofline": 100.0 * eff_gbs / HBM_PEAK_GBS,
-        "algorithmic_TFLOPs_per_s": algorithmic_flops(wl) / (ms * 1e-3) / 1e12,
-        "matrices": nmat, "fp64_chain_matrices": n64, "nonfinite_matrices": nbad,
-        "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
-        "launch": launch,
-        "eager_ms_per_step": eager_ms,
-        "graph_ms_per_step": graph_ms,
-        "wall_s_timed_region_eager": wall,
-        "host_enqueue_ms_per_step": 1000.0 * enqueue / args.steps,
-        "roofline": {"bound": "mfma", "kernel": dom, "what": what, "dtype": dt_,
-                     "achieved": achieved, "peak": PEAK_TFLOPS[dt_], "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_TFLOPS[dt_],
-                     "flops_per_launch": flops / launches, "avg_launch_ms": phase_ms[dom] / launches,
-                     "algorithmic_flops_per_launch": alg_flops / launches,
-                     "algorithmic_TFLOPs_per_s": alg_flops / secs / 1e12 if secs > 0 else 0.0,
-                     "mfma_flops_per_algorithmic_flop": factor,
-                     "traffic": measured_traffic(wl.name, dom), "traffic_unit": "bytes/launch"},
+        "config": {"workload": head["workload"], "stacks": head["stacks"], "mu": head["mu"], "lr": head["lr"],
+                   "eps": head["eps"], "grad": head["grad"], "inputs": head["inputs"],
+                   "sticky_fp64": not args.no_sticky, "host_fp64_hint": not (args.no_sticky or args.no_hint),
+                   "chunks": args.chunks or "auto"},
     }
+    for k in ("effective_param_GBps", "pct_hbm_roofline", "algorithmic_TFLOPs_per_s", "matrices",
+              "fp64_chain_matrices", "shifted_matrices", "householder_matrices", "nonfinite_matrices", "phase_ms",
+              "phase_roofline", "launch", "eager_ms_per_step", "graph_ms_per_step", "wall_s_timed_region_eager",
+              "host_enqueue_ms_per_step", "roofline", "qr_roofline"):
+        out[k] = head[k]
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if args.configs != "none":
+        out["configs"] = []
+        for wid in [int(x) for x in args.configs.split(",") if x.strip()]:
+            if wid == args.workload:
+                ent = dict(head)
+            else:
+                ccpu = 0.0 if args.no_cpu_baseline else args.config_cpu_seconds
+                ent = measure(W.get(wid), dev, stream, args, ccpu, args.host_inputs)
+            ent["wid"] = wid
+            out["configs"].append(ent)
     if not args.no_elementwise:
         print("[bench] element-wise AdamW / Lion", file=sys.stderr, flush=True)
         out["elementwise"] = elementwise_block(dev, stream, with_cpu=not args.no_cpu_baseline)
     if not args.no_spectral:
         print("[bench] multi-power-iteration lambda_max estimate", file=sys.stderr, flush=True)
         out["spectral"] = spectral_block(dev, stream, with_cpu=not args.no_cpu_baseline)
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

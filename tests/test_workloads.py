@@ -51,3 +51,41 @@ def test_distributions():
     s5 = np.linalg.svd(G5, compute_uv=False)
     n = G5.shape[0]
     assert abs(np.log10(s5[0] / s5[n // 2]) - 3.0) < 0.05
+
+
+def test_device_generators_follow_the_recipes():
+    """The benchmark's on-device draws (run here on torch's CPU device): the same distributions
+    as the host generators, repeatable for a seed, fresh per step."""
+    import torch
+    dev = torch.device("cpu")
+    wl = W.SMALL[1]
+    X, M, Q = W.make_state_device(wl, 0, dev)
+    assert X.dtype == torch.float32 and abs(float(X.std()) - 0.02) < 0.002 and not M.any()
+    assert torch.allclose(torch.linalg.vector_norm(Q[0].double(), dim=0), torch.ones(wl.groups[0].rank,
+                                                                                     dtype=torch.float64), atol=1e-6)
+    G = W.make_grad_device(wl, 0, 1, dev)
+    assert abs(float(G.std()) - 1e-2) < 1e-3
+    assert torch.equal(G, W.make_grad_device(wl, 0, 1, dev)) and not torch.equal(G, W.make_grad_device(wl, 0, 2, dev))
+    wl2 = W.SMALL[2]
+    s = torch.linalg.svdvals(W.make_grad_device(wl2, 0, 1, dev)[0].double())
+    k = wl2.grad_args["k"]
+    assert s[k - 1] > 100 * s[k]
+    wl3 = W.SMALL[3]
+    G3 = W.make_grad_device(wl3, 0, 1, dev)
+    assert G3.dtype == torch.bfloat16
+    sd = G3.double().reshape(G3.shape[0], -1).std(dim=1)
+    assert bool((sd > 0.5e-5).all()) and bool((sd < 2e-2).all())
+    X3, _, _ = W.make_state_device(wl3, 0, dev)
+    assert X3.dtype == torch.bfloat16
+    # Student-t with nu = 3: symmetric, heavy tails (excess kurtosis of t_3 is infinite; the
+    # sample's exceeds the Gaussian's 0 by far) and scale 1e-3 (median |t_3| = 0.765)
+    wl4 = W.SMALL[4]
+    G4 = W.make_grad_device(wl4, 0, 1, dev).double().flatten()
+    med = float(G4.abs().median())
+    assert 0.65e-3 < med < 0.88e-3
+    z = (G4 - G4.mean()) / G4.std()
+    assert float((z ** 4).mean()) - 3.0 > 3.0
+    wl5 = W.SMALL[5]
+    s5 = torch.linalg.svdvals(W.make_grad_device(wl5, 0, 1, dev)[0].double())
+    n = s5.shape[0]
+    assert abs(float(torch.log10(s5[0] / s5[n // 2])) - 3.0) < 0.05

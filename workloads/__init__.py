@@ -294,3 +294,88 @@ def psd_stack(batch: int, r: int, seed: int, kind: str = "gram", decades: float 
             U = _haar(rng, r)
             out[b] = (U * 10.0 ** (-decades * np.arange(r) / r)) @ U.T
     return out
+
+
+# ----------------------------------------------------------------------------
+# the same recipes drawn on the GPU (benchmark inputs at full size)
+# ----------------------------------------------------------------------------
+# The benchmark needs the full-size inputs in HBM quickly; the workload-5 recipe alone costs two
+# 4096^2 Haar QRs per matrix and step on the host.  These draw the same distributions with torch
+# on the device (fp64, rounded once to the storage type, round-to-nearest-even), from a torch
+# generator seeded per (seed, workload, group, step, tag).  They are not the host streams above:
+# parity tests, which need identical bits on both sides, use the host generators.
+def _torch_gen(device, *key):
+    import torch
+    s = np.random.SeedSequence([0x5EED, *key]).generate_state(1, np.uint64)[0]
+    return torch.Generator(device=device).manual_seed(int(s) & ((1 << 63) - 1))
+
+
+def _torch_store(a64, dtype: str):
+    import torch
+    f = a64.to(torch.float32)
+    return f.to(torch.bfloat16) if dtype == "bf16" else f
+
+
+def make_state_device(wl: Workload, gi: int, device, seed: int = 0):
+    """Initial (X, M, Q) of group ``gi`` as device tensors, drawn on the device (see above)."""
+    import torch
+    g = wl.groups[gi]
+    gen = _torch_gen(device, seed, wl.wid, gi, 0, _T_X)
+    X = torch.empty((g.batch, g.m, g.n), dtype=torch.bfloat16 if wl.x_dtype == "bf16" else torch.float32,
+                    device=device)
+    for mi in range(g.batch):
+        X[mi] = _torch_store(0.02 * torch.randn((g.m, g.n), generator=gen, device=device, dtype=torch.float64),
+                             wl.x_dtype)
+    M = torch.zeros((g.batch, g.m, g.n), dtype=torch.float32, device=device)
+    gq = _torch_gen(device, seed, wl.wid, gi, 0, _T_Q)
+    q = torch.randn((g.batch, g.n, g.rank), generator=gq, device=device, dtype=torch.float64)
+    if g.rank:
+        q /= torch.linalg.vector_norm(q, dim=1, keepdim=True)
+    return X, M, q.to(torch.float32).contiguous()
+
+
+def make_grad_device(wl: Workload, gi: int, step: int, device, seed: int = 0):
+    """Gradient G_t of group ``gi`` as a device tensor: make_grad's recipe drawn on the device."""
+    import torch
+    g = wl.groups[gi]
+    a = wl.grad_args
+    dt = wl.g_dtype
+    gen = _torch_gen(device, seed, wl.wid, gi, step, _T_G)
+    out = torch.empty((g.batch, g.m, g.n), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=device)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float64)
+
+    kind = wl.grad
+    if kind == "loguniform_gauss":
+        gs = _torch_gen(device, seed, wl.wid, gi, 0, _T_SCALE)
+        lo, hi = math.log(a["lo"]), math.log(a["hi"])
+        scales = torch.exp(lo + (hi - lo) * torch.rand((g.batch,), generator=gs, device=device,
+                                                        dtype=torch.float64)).tolist()
+    for mi in range(g.batch):
+        if kind == "gauss":
+            v = a["std"] * randn(g.m, g.n)
+        elif kind == "lowrank_noise":
+            v = randn(g.m, a["k"]) @ randn(g.n, a["k"]).T + a["noise_std"] * randn(g.m, g.n)
+        elif kind == "loguniform_gauss":
+            v = scales[mi] * randn(g.m, g.n)
+        elif kind == "student_t":
+            # t_nu = Z / sqrt(chi2_nu / nu), chi2 of integer nu as a sum of nu squared normals
+            nu = int(a["nu"])
+            if nu != a["nu"]:
+                raise ValueError("the device Student-t draw needs an integer nu")
+            chi2 = sum(randn(g.m, g.n) ** 2 for _ in range(nu))
+            v = a["scale"] * randn(g.m, g.n) / torch.sqrt(chi2 / nu)
+        elif kind == "decaying_spectrum":
+            n = g.n
+            sig = 10.0 ** (-a["decades"] * torch.arange(n, device=device, dtype=torch.float64) / n)
+
+            def haar():
+                q, t = torch.linalg.qr(randn(n, n))
+                return q * torch.sign(torch.diagonal(t))[None, :]
+            U, V = haar(), haar()
+            v = (U * sig[None, :]) @ V.T
+        else:
+            raise ValueError(f"unknown gradient recipe {kind!r}")
+        out[mi] = _torch_store(v, dt)
+    return out
