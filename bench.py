@@ -278,6 +278,10 @@ def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
     per step of each phase, summed over the stacks; the flops and bytes are algorithmic and
     counted for the matrices each chain actually owned (flags after the last timed step)."""
     f64m = [int((s["flags"] & dion.FLAG_F64).ne(0).sum()) for s in stacks]
+    # bf16 weights run the three big contractions as plain bf16 products (one MFMA product per
+    # algorithmic one); fp32 weights as the exact six-product split
+    split = 1.0 if wl.x_dtype == "bf16" else SPLIT6
+    how = "plain bf16 MFMA products" if split == 1.0 else "fp32 as six bf16 MFMA products"
     out = {}
 
     def add(name, kind, amount, peak_key, factor=1.0, what=""):
@@ -309,16 +313,23 @@ def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
         nb += k32 * n * r * 8.0 + k64 * (n * r * 16.0 + m * r * 12.0)
         bx = 2 if wl.x_dtype == "bf16" else 4
         ub += b * (m * n * (bx + 8 + 2 * bx) + 4.0 * (m + 2 * n) * r)
-    add("f32_product", "flops", 2.0 * mnr32, "bf16", SPLIT6, "P0 = (M+G) Q, fp32 as six bf16 MFMA products")
+    add("f32_product", "flops", 2.0 * mnr32, "bf16", split, "P0 = (M+G) Q, " + how)
     add("f32_qr", "flops", qr32, "f32", 1.0, "CholeskyQR2 of the fp32 chain, 6 m r^2 + 2 r^3 / 3 per matrix")
-    add("f32_backproject", "flops", 2.0 * mnr32, "bf16", SPLIT6, "R = (M+G)^T P, fp32 as six bf16 MFMA products")
+    add("f32_backproject", "flops", 2.0 * mnr32, "bf16", split, "R = (M+G)^T P, " + how)
     add("f64_product", "flops", 2.0 * mnr64, "f64", 1.0, "P0 = (M+G) Q, fp64 MFMA")
     add("f64_qr", "flops", qr64, "f64", 1.0, "CholeskyQR2 (shifted CholeskyQR3) of the fp64 chain, "
                                              "6 m r^2 + 2 r^3 / 3 per matrix")
     add("f64_backproject", "flops", 2.0 * mnr64, "f64", 1.0, "R = (M+G)^T P, fp64 MFMA")
     add("norms", "bytes", nb, "hbm", 1.0, "column norms of R, Q' = R c; fp64-chain P, R rounded to fp32")
-    add("update", "flops", 4.0 * (mnr32 + mnr64), "bf16", SPLIT6,
-        "P R^T and P Q'^T of the M, X update, fp32 as six bf16 MFMA products")
+    add("update", "flops", 4.0 * (mnr32 + mnr64), "bf16", split, "P R^T and P Q'^T of the M, X update, " + how)
+    for k in ("f32_product", "f32_backproject"):   # the HBM side of the products: B read once
+        bg = sum(s_["g"].batch * s_["g"].m * s_["g"].n for s_ in stacks) * (4 + (2 if wl.g_dtype == "bf16" else 4))
+        if k.startswith("f32") and f64m and sum(f64m) == sum(s_["g"].batch for s_ in stacks):
+            bg = 0.0
+        ms = phase_ms[k]
+        ach = bg / (ms * 1e-3) / 1e9 if ms > 0 and bg > 0 else 0.0
+        out[k]["hbm"] = {"algorithmic_bytes": bg, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS}
     out["update"]["hbm"] = {"algorithmic_bytes": ub,
                             "achieved": ub / (phase_ms["update"] * 1e-3) / 1e9 if phase_ms["update"] > 0 else 0.0,
                             "peak": HBM_PEAK_GBS, "unit": "GB/s"}
@@ -453,7 +464,7 @@ def measure(wl, dev, stream, args, cpu_s: float, host_inputs: bool) -> dict:
     eff_gbs = algorithmic_bytes(wl) / (ms * 1e-3) / 1e9
     dtype = "f32" if n64 == 0 else ("f64+f32" if n64 == nmat else "f32|f64+f32")
     if wl.x_dtype == "bf16":
-        dtype += " (bf16 X, G)"
+        dtype = "bf16 products, f32 QR (bf16 X, G; f32 M, Q)" if n64 == 0 else dtype + " (bf16 X, G)"
     ent = {
         "workload": wl.name,
         "stacks": [f"{g.batch}x{g.m}x{g.n} r={g.rank}" for g in wl.groups],

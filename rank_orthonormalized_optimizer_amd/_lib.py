@@ -25,6 +25,7 @@ ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_HYPER, ERR_ALIGN = -1, -2, -3, -4, -5
 ERR_OVERLAP, ERR_WORKSPACE, ERR_DTYPE, ERR_OPTION, ERR_SCRATCH, ERR_HIP = -6, -7, -8, -9, -10, -100
 NOALLOC_SCRATCH_BYTES = 64 << 20
 OPT_STICKY_F64, OPT_FORCE_F64, OPT_FORCE_F32, OPT_HOUSEHOLDER, OPT_SPECTRAL_SHIFT = 1, 2, 4, 16, 32
+OPT_EXACT_PRODUCTS = 64
 OPT_CHUNKS_SHIFT = 8
 
 

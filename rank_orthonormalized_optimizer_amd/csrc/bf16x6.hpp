@@ -10,6 +10,11 @@
 // Operands stay fp32 in memory and are split while they are staged into LDS, as three bf16
 // part tiles (h, m, l) of one 32-k slab, with zeros beyond the contraction length.
 //
+// The same machinery runs plain bf16 products (operands rounded once to bf16, fp32
+// accumulation) when the template parameter NP, the number of parts staged, is 1: only h is
+// stored and only the hh product is issued.  That is the arithmetic of stacks whose weights
+// are bf16, where the accepted error is that of bf16 (2^-8 relative per operand).
+//
 // Lane layout of v_mfma_f32_16x16x32_bf16 (measured on gfx950 with a one-wave probe):
 //   A: lane l holds A[l % 16][8 (l / 16) + i], i = 0..7
 //   B: lane l holds B[8 (l / 16) + i][l % 16]
@@ -118,11 +123,12 @@ __device__ __forceinline__ Parts4 split4(const float (&v)[4]) {
     r.p[2] = u32x2{l0, l1};
     return r;
 }
-// write them at k (k % 4 == 0 within the slab) of row x of the three part tiles
+// write them at k (k % 4 == 0 within the slab) of row x of the first NP part tiles
+template <int NP>
 __device__ __forceinline__ void store4(uint16_t* lds, int part_stride, int x, int k, const Parts4& q) {
     const int off = part_off(x, k >> 3) + (k & 7);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) *(u32x2*)&lds[p * part_stride + off] = q.p[p];
+    for (int p = 0; p < NP; ++p) *(u32x2*)&lds[p * part_stride + off] = q.p[p];
 }
 
 // NT: the number of staging threads (256 or 512) that share one operand tile
@@ -161,6 +167,7 @@ struct Loader6<BX, S6_KC8, ADD, NT> {
                 a[q][e] = (x < op.xext && k + e < op.kext) ? ((const float*)op.p0)[o + e] : 0.f;
         }
     }
+    template <int NP = 3>
     __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -169,7 +176,7 @@ struct Loader6<BX, S6_KC8, ADD, NT> {
             const Parts4 lo = split4(v0), hi = split4(v1);
             const int off = part_off((t >> 2) + 64 * q, t & 3);
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int p = 0; p < NP; ++p)
                 *(u32x4*)&lds[p * BX * kSplitK + off] = u32x4{lo.p[p].x, lo.p[p].y, hi.p[p].x, hi.p[p].y};
         }
     }
@@ -234,9 +241,10 @@ struct Loader6<BX, S6_KC, ADD, NT> {
     }
     __device__ __forceinline__ void store(uint16_t* lds, int t) const {
 #pragma unroll
-        for (int q = 0; q < PER; ++q) store4(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), sp[q]);
+        for (int q = 0; q < PER; ++q) store4<3>(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), sp[q]);
     }
     // split and store group by group (no register copy of the whole split slab)
+    template <int NP = 3>
     __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -246,7 +254,7 @@ struct Loader6<BX, S6_KC, ADD, NT> {
                 if constexpr (ADD == A6_NONE) v[e] = a[q][e];
                 else v[e] = sum6<ADD>(a[q][e], b[q][e]);
             }
-            store4(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), split4(v));
+            store4<NP>(lds, BX * kSplitK, (t >> 3) + RP * q, 4 * (t & 7), split4(v));
         }
     }
 };
@@ -317,6 +325,7 @@ struct Loader6<BX, S6_XC4, ADD, NT> {
             }
         }
     }
+    template <int NP = 3>
     __device__ __forceinline__ void split_store(uint16_t* lds, int t) const {
         const int xl = XW * (t % TX), kl = 4 * (t / TX);
 #pragma unroll
@@ -327,7 +336,7 @@ struct Loader6<BX, S6_XC4, ADD, NT> {
                 if constexpr (ADD == A6_NONE) v[e] = a[XW * e + i];
                 else v[e] = sum6<ADD>(a[XW * e + i], b[XW * e + i]);
             }
-            store4(lds, BX * kSplitK, xl + i, kl, split4(v));
+            store4<NP>(lds, BX * kSplitK, xl + i, kl, split4(v));
         }
     }
 };
@@ -335,22 +344,32 @@ struct Loader6<BX, S6_XC4, ADD, NT> {
 // acc[i][j] (wave sub-tile FM x FN blocks of 16 x 16) += A B over one 32-k slab from the part
 // tiles: B fragments of all three parts held, A fragments one part at a time, the six kept
 // products in increasing size.
-template <int BXA, int BXB, int FM, int FN>
+// NP = 1: the single product of the h parts.
+template <int BXA, int BXB, int FM, int FN, int NP = 3>
 __device__ __forceinline__ void mma6_slab(const uint16_t* lA, const uint16_t* lB, f32x4 (&acc)[FM][FN], int ra,
                                           int rb, int fr, int fc) {
-    u32x4 b[FN][3];
+    u32x4 b[FN][NP];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
+        for (int p = 0; p < NP; ++p)
             b[j][p] = *(const u32x4*)&lB[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
+    if constexpr (NP == 1) {
 #pragma unroll
-    for (int pa = 2; pa >= 0; --pa) {
+        for (int i = 0; i < FM; ++i) {
+            const u32x4 a = *(const u32x4*)&lA[part_off(ra + 16 * i + fr, fc)];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mma_bf16(a, b[j][0], acc[i][j]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int pa = NP - 1; pa >= 0; --pa) {
         u32x4 a[FM];
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[i] = *(const u32x4*)&lA[pa * BXA * kSplitK + part_off(ra + 16 * i + fr, fc)];
 #pragma unroll
-        for (int pb = 2 - pa; pb >= 0; --pb)
+        for (int pb = (NP - 1) - pa; pb >= 0; --pb)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -361,27 +380,27 @@ __device__ __forceinline__ void mma6_slab(const uint16_t* lA, const uint16_t* lB
 // Two products sharing A (acc1 += A B1, acc2 += A B2) over one slab: A fragments of all three
 // parts are read once, then per column block the B1 and B2 fragments of all three parts; the six
 // kept products of each pair in the same increasing order as mma6_slab.
-template <int BXA, int BXB, int FM, int FN>
+template <int BXA, int BXB, int FM, int FN, int NP = 3>
 __device__ __forceinline__ void mma6_slab2(const uint16_t* lA, const uint16_t* lB1, const uint16_t* lB2,
                                            f32x4 (&acc1)[FM][FN], f32x4 (&acc2)[FM][FN], int ra, int rb, int fr,
                                            int fc) {
-    u32x4 a[3][FM];
+    u32x4 a[NP][FM];
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[p][i] = *(const u32x4*)&lA[p * BXA * kSplitK + part_off(ra + 16 * i + fr, fc)];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        u32x4 b1[3], b2[3];
+        u32x4 b1[NP], b2[NP];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
+        for (int p = 0; p < NP; ++p) {
             b1[p] = *(const u32x4*)&lB1[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
             b2[p] = *(const u32x4*)&lB2[p * BXB * kSplitK + part_off(rb + 16 * j + fr, fc)];
         }
 #pragma unroll
-        for (int pa = 2; pa >= 0; --pa)
+        for (int pa = NP - 1; pa >= 0; --pa)
 #pragma unroll
-            for (int pb = 2 - pa; pb >= 0; --pb)
+            for (int pb = (NP - 1) - pa; pb >= 0; --pb)
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     acc1[i][j] = mma_bf16(a[pa][i], b1[pb], acc1[i][j]);

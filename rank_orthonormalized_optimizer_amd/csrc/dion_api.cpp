@@ -36,7 +36,7 @@ int check_step_args(int64_t m, int64_t n, int64_t batch, int64_t rank, float mu,
     if ((x_dtype != DION_F32 && x_dtype != DION_BF16) || (g_dtype != DION_F32 && g_dtype != DION_BF16))
         return DION_ERR_DTYPE;
     const uint32_t known = DION_OPT_STICKY_F64 | DION_OPT_FORCE_F64 | DION_OPT_FORCE_F32 | DION_OPT_HOUSEHOLDER |
-                           DION_OPT_SPECTRAL_SHIFT | (15u << DION_OPT_CHUNKS_SHIFT);
+                           DION_OPT_SPECTRAL_SHIFT | DION_OPT_EXACT_PRODUCTS | (15u << DION_OPT_CHUNKS_SHIFT);
     if ((options & ~known) || ((options & DION_OPT_FORCE_F64) && (options & DION_OPT_FORCE_F32)) ||
         ((options & DION_OPT_HOUSEHOLDER) && ((options & DION_OPT_FORCE_F32) || rank > 4096)) ||
         ((options & DION_OPT_SPECTRAL_SHIFT) && (options & DION_OPT_FORCE_F32)))

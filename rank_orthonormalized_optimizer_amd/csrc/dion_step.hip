@@ -690,7 +690,7 @@ __device__ void failed_tile(const UpdArgs& u, int bz, int m0, int n0) {
 // one pass over the tile of M, G and X.  P, R and Q are read as fp32 and split into their
 // three bf16 parts on the way into LDS; nine part tiles (P, R, Q x h, m, l) per 32-k slab,
 // double-buffered.
-template <int BM, int BN, int WGM, int WGN, bool G_BF16, bool X_BF16>
+template <int BM, int BN, int WGM, int WGN, bool G_BF16, bool X_BF16, int NP>
 __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
     constexpr int NT = WGM * WGN * 64, BK = kSplitK;
     constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
@@ -702,8 +702,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
         failed_tile<BM, BN, G_BF16>(u, bz, m0, n0);
         return;
     }
-    __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][3][BM * BK];   // P h m l
-    __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][6][BN * BK];   // R h m l | Q h m l
+    __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][NP][BM * BK];       // P parts
+    __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][2 * NP][BN * BK];   // R parts | Q parts
     const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
     const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
     const Op6 oR{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
@@ -717,9 +717,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
         lq.load(oQ, n0, k0, t);
     };
     auto lstore = [&](int buf) {
-        lp.split_store(&ldsA[buf][0][0], t);
-        lr.split_store(&ldsB[buf][0][0], t);
-        lq.split_store(&ldsB[buf][3][0], t);
+        lp.template split_store<NP>(&ldsA[buf][0][0], t);
+        lr.template split_store<NP>(&ldsB[buf][0][0], t);
+        lq.template split_store<NP>(&ldsB[buf][NP][0], t);
     };
 
     const int lane = t & 63, wave = t >> 6, wm = wave / WGN, wn = wave % WGN;
@@ -742,26 +742,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
     for (int k0 = 0; k0 < u.kp; k0 += BK) {
         const bool more = k0 + BK < u.kp;
         if (more) gload(k0 + BK);
-        u32x4 a[FM][3], b[FN][3], c[FN][3];
+        u32x4 a[FM][NP], b[FN][NP], c[FN][NP];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int q = 0; q < 3; ++q) a[i][q] = *(const u32x4*)&ldsA[buf][q][ao[i]];
+            for (int q = 0; q < NP; ++q) a[i][q] = *(const u32x4*)&ldsA[buf][q][ao[i]];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
+            for (int q = 0; q < NP; ++q) {
                 b[j][q] = *(const u32x4*)&ldsB[buf][q][bo[j]];
-                c[j][q] = *(const u32x4*)&ldsB[buf][3 + q][bo[j]];
+                c[j][q] = *(const u32x4*)&ldsB[buf][NP + q][bo[j]];
             }
+        constexpr int NTERM = NP == 1 ? 1 : 6;   // plain bf16: the single h h product
 #pragma unroll
-        for (int term = 0; term < 6; ++term)
+        for (int term = 0; term < NTERM; ++term)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    acc1[i][j] = mma_bf16(a[i][kTermA[term]], b[j][kTermB[term]], acc1[i][j]);
-                    acc2[i][j] = mma_bf16(a[i][kTermA[term]], c[j][kTermB[term]], acc2[i][j]);
+                    const int ta = NP == 1 ? 0 : kTermA[term], tb = NP == 1 ? 0 : kTermB[term];
+                    acc1[i][j] = mma_bf16(a[i][ta], b[j][tb], acc1[i][j]);
+                    acc2[i][j] = mma_bf16(a[i][ta], c[j][tb], acc2[i][j]);
                 }
         if (more) lstore(buf ^ 1);
         __syncthreads();
@@ -824,16 +826,19 @@ __device__ __forceinline__ uint2 nt_ld2(const uint16_t* p) {
     return uint2{v[0], v[1]};
 }
 __device__ __forceinline__ void nt_st2(uint16_t* p, uint2 v) { __builtin_nontemporal_store(u32x2{v.x, v.y}, (u32x2*)p); }
-template <bool G_BF16, bool X_BF16, bool FAST>
+template <bool G_BF16, bool X_BF16, bool FAST, int NP>
 __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     constexpr int BM = 128, BN = 64, PA = BM * kSplitK, PB = BN * kSplitK, FM = 4, FN = 2;
+    // the part tiles, reused by the epilogue as a 128 x (64 + 4) fp32 tile
+    constexpr int LDS_PARTS = NP * PA + 2 * NP * PB, LDS_TILE = BM * (BN + 4) * 2;
+    constexpr int LDS_N = LDS_PARTS > LDS_TILE ? LDS_PARTS : LDS_TILE;
     const TileId tid = xcd_tile_id();
     const int bz = tid.z, m0 = tid.y * BM, n0 = tid.x * BN;
     if (u.st[bz] & ST_FAIL) {
         failed_tile<BM, BN, G_BF16>(u, bz, m0, n0);
         return;
     }
-    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * PA + 6 * PB];   // P h m l | R h m l | Q h m l
+    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_N];   // P parts | R parts | Q parts
     const int64_t pr = (int64_t)u.m * u.r, nr = (int64_t)u.n * u.r;
     const Op6 oP{u.P + bz * pr, nullptr, u.r, u.m, u.r, u.vec};
     const Op6 oR{u.R + bz * nr, nullptr, u.r, u.n, u.r, u.vec};
@@ -846,7 +851,8 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) { acc1[i][j] = f32x4{0, 0, 0, 0}; acc2[i][j] = f32x4{0, 0, 0, 0}; }
     auto mma = [&]() {
-        mma6_slab2<BM, BN, FM, FN>(lds, lds + 3 * PA, lds + 3 * PA + 3 * PB, acc1, acc2, wm * 64, wn * 32, fr, fc);
+        mma6_slab2<BM, BN, FM, FN, NP>(lds, lds + NP * PA, lds + NP * PA + NP * PB, acc1, acc2, wm * 64, wn * 32, fr,
+                                       fc);
     };
     if constexpr (FAST) {
         // every tile interior and every slab whole: two register sets, so each slab's loads are
@@ -861,9 +867,9 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
         };
         auto store = [&](auto jc) {
             constexpr int J = decltype(jc)::value;
-            lp[J].split_store(lds, t);
-            lr[J].split_store(lds + 3 * PA, t);
-            lq[J].split_store(lds + 3 * PA + 3 * PB, t);
+            lp[J].template split_store<NP>(lds, t);
+            lr[J].template split_store<NP>(lds + NP * PA, t);
+            lq[J].template split_store<NP>(lds + NP * PA + NP * PB, t);
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
@@ -909,9 +915,9 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
             lq.load(oQ, n0, k, t);
         };
         auto store = [&]() {
-            lp.split_store(lds, t);
-            lr.split_store(lds + 3 * PA, t);
-            lq.split_store(lds + 3 * PA + 3 * PB, t);
+            lp.template split_store<NP>(lds, t);
+            lr.template split_store<NP>(lds + NP * PA, t);
+            lq.template split_store<NP>(lds + NP * PA + NP * PB, t);
         };
         load(0);
         store();
@@ -1110,6 +1116,8 @@ struct ChainCtx {
     // lambda_max(W)) when set, else s = c_shift * trace(W)
     const double* lam = nullptr;
     int64_t lam_stride = 0;
+    // bf16 weights: the two big products of the fp32 chain as plain bf16 products
+    bool plain = false;
     hipError_t open_gate() const {
         if (!gate || *gated) return hipSuccess;
         *gated = true;
@@ -1826,7 +1834,7 @@ struct Prod6Args {
 // Staging side of prod6_kernel: three register sets of raw operand values and three LDS buffers,
 // both indexed by slab % 3, so a slab's global loads are issued three slabs before it is split
 // (enough bytes in flight per CU to cover the memory latency at the matrix-core rate).
-template <int AK, int AADD, int BK6, int NT>
+template <int AK, int AADD, int BK6, int NT, int NP>
 struct Stage6 {
     static constexpr int BT = 128, PT = BT * kSplitK, D = 3;
     Loader6<BT, AK, AADD, NT> la[D];
@@ -1839,8 +1847,8 @@ struct Stage6 {
     template <int J>
     __device__ __forceinline__ void stage(const Op6& A, const Op6& B, int m0, int n0, int k, int K, uint16_t* lds,
                                           int t) {
-        la[J].split_store(lds, t);
-        lb[J].split_store(lds + 3 * PT, t);
+        la[J].template split_store<NP>(lds, t);
+        lb[J].template split_store<NP>(lds + NP * PT, t);
         load<J>(A, B, m0, n0, k + D * kSplitK, K, t);
     }
     // Launches whose tiles are all interior (every slab whole and inside both operands) use the
@@ -1853,33 +1861,33 @@ struct Stage6 {
     template <int J>
     __device__ __forceinline__ void stage_fast(const Op6& A, const Op6& B, int m0, int n0, int knext, uint16_t* lds,
                                                int t) {
-        la[J].split_store(lds, t);
-        lb[J].split_store(lds + 3 * PT, t);
+        la[J].template split_store<NP>(lds, t);
+        lb[J].template split_store<NP>(lds + NP * PT, t);
         load_fast<J>(A, B, m0, n0, knext, t);
     }
     template <int J>
     __device__ __forceinline__ void stage_fast_if(const Op6& A, const Op6& B, int m0, int n0, int knext, int K,
                                                   uint16_t* lds, int t) {
-        la[J].split_store(lds, t);
-        lb[J].split_store(lds + 3 * PT, t);
+        la[J].template split_store<NP>(lds, t);
+        lb[J].template split_store<NP>(lds + NP * PT, t);
         if (knext < K) load_fast<J>(A, B, m0, n0, knext, t);
     }
 };
 
-template <int AK, int AADD, int BK6, bool FAST, int NT>
+template <int AK, int AADD, int BK6, bool FAST, int NT, int NP>
 __global__ __launch_bounds__(256 + NT) void prod6_kernel(Prod6Args g) {
     // Waves 0-3 multiply (a 64 x 64 sub-tile each); the NT / 64 waves after them stage the
     // operands (load, split into bf16 parts, write LDS).  Each SIMD holds one multiplying wave and
     // NT / 256 staging waves, so the staging work issues between the other wave's MFMAs; one
     // barrier per slab.
-    using St = Stage6<AK, AADD, BK6, NT>;
+    using St = Stage6<AK, AADD, BK6, NT, NP>;
     constexpr int BT = St::BT, PT = St::PT;
     const TileId tid = xcd_tile_id();
     const int sp = g.splits > 1 ? g.splits : 1, bz = tid.z / sp, ks = tid.z % sp;
     if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
     if (g.lower && tid.x > tid.y) return;
     const int m0 = tid.y * BT, n0 = tid.x * BT;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[3][6 * PT];   // A h m l | B h m l
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3][2 * NP * PT];   // A parts | B parts
     const int wave = threadIdx.x >> 6;
     const bool stager = wave >= 4;
     const int st_t = threadIdx.x - 256;
@@ -1962,7 +1970,7 @@ __global__ __launch_bounds__(256 + NT) void prod6_kernel(Prod6Args g) {
     __syncthreads();
     int buf = 0;
     for (int k0 = 0; k0 < K; k0 += kSplitK) {
-        mma6_slab<BT, BT, 4, 4>(lds[buf], lds[buf] + 3 * PT, acc, wm * 64, wn * 64, fr, fc);
+        mma6_slab<BT, BT, 4, 4, NP>(lds[buf], lds[buf] + NP * PT, acc, wm * 64, wn * 64, fr, fc);
         __syncthreads();
         buf = buf == 2 ? 0 : buf + 1;
     }
@@ -1983,7 +1991,8 @@ __global__ __launch_bounds__(256 + NT) void prod6_kernel(Prod6Args g) {
 #endif
 constexpr int kStageThreads = DION_STAGE_THREADS;   // staging threads of the split-bf16 product kernel
 
-template <int AK, int AADD, int BK6>
+// NP: bf16 parts per operand, 3 (fp32-accurate split) or 1 (plain bf16 products)
+template <int AK, int AADD, int BK6, int NP = 3>
 static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
     dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128), (unsigned)batch);
@@ -2000,12 +2009,13 @@ static hipError_t launch_prod6(const Prod6Args& g, int64_t batch, hipStream_t s)
                                          g.K - (g.splits - 1) * g.kc >= 3 * kSplitK));
     if constexpr (AK == S6_KC || AK == S6_XC4) {
         if (fast) {
-            hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true, kStageThreads>), grid, dim3(256 + kStageThreads), 0,
-                               s, g);
+            hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, true, kStageThreads, NP>), grid,
+                               dim3(256 + kStageThreads), 0, s, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false, kStageThreads>), grid, dim3(256 + kStageThreads), 0, s, g);
+    hipLaunchKernelGGL((prod6_kernel<AK, AADD, BK6, false, kStageThreads, NP>), grid, dim3(256 + kStageThreads), 0, s,
+                       g);
     return hipGetLastError();
 }
 
@@ -2064,8 +2074,11 @@ static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, co
         g.c = (float*)P; g.ldc = r; g.sc = m * r;
         g.M = (int)m; g.N = (int)r; g.K = (int)n;
         g.st = c.st; g.st_mask = mask; g.st_val = val;
-        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC4>(g, p.b, c.s)
-                                                   : launch_prod6<S6_KC, A6_F32, S6_XC4>(g, p.b, c.s);
+        hipError_t he;
+        if (c.plain) he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC4, 1>(g, p.b, c.s)
+                                               : launch_prod6<S6_KC, A6_F32, S6_XC4, 1>(g, p.b, c.s);
+        else he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_KC, A6_BF16, S6_XC4>(g, p.b, c.s)
+                                       : launch_prod6<S6_KC, A6_F32, S6_XC4>(g, p.b, c.s);
         DION_TRY(he);
         return 0;
     }
@@ -2103,8 +2116,11 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
             g.splits = 2; g.kc = m / 2;
             g.ska = g.kc * n * 4; g.ska1 = g.kc * n * gsz; g.skb = g.kc * r * 4;
             g.scs = (int64_t)(p.R64 - p.R32) / 4;
-            const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b * 2, c.s)
-                                                       : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b * 2, c.s);
+            hipError_t he;
+            if (c.plain) he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4, 1>(g, p.b * 2, c.s)
+                                                   : launch_prod6<S6_XC4, A6_F32, S6_XC4, 1>(g, p.b * 2, c.s);
+            else he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b * 2, c.s)
+                                           : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b * 2, c.s);
             DION_TRY(he);
             dim3 grid(grid_1d(n * r / 4, 1024), (unsigned)p.b);
             hipLaunchKernelGGL(add_split_kernel, grid, dim3(256), 0, c.s, (float*)R, (const float*)(c.ws + p.R64), n * r,
@@ -2112,8 +2128,11 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
             DION_TRY(hipGetLastError());
             return 0;
         }
-        const hipError_t he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b, c.s)
-                                                   : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b, c.s);
+        hipError_t he;
+        if (c.plain) he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4, 1>(g, p.b, c.s)
+                                               : launch_prod6<S6_XC4, A6_F32, S6_XC4, 1>(g, p.b, c.s);
+        else he = ASRC == SRC_SUM_BF16 ? launch_prod6<S6_XC4, A6_BF16, S6_XC4>(g, p.b, c.s)
+                                       : launch_prod6<S6_XC4, A6_F32, S6_XC4>(g, p.b, c.s);
         DION_TRY(he);
         return 0;
     }
@@ -2215,7 +2234,7 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
                   : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, A64, A64);
 }
 
-template <bool GB, bool XB>
+template <bool GB, bool XB, int NP>
 static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, float* M, const void* G, void* X,
                                 float mu, float lr, hipStream_t s) {
     UpdArgs u{};
@@ -2234,11 +2253,11 @@ static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, f
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
         // all tiles interior, whole slabs, vector-legal rows: the two-set branch-free loop
         const bool fast = p.m % 128 == 0 && p.n % 64 == 0 && p.r % kSplitK == 0 && p.r >= 2 * kSplitK && u.vec;
-        if (fast) hipLaunchKernelGGL((update3_kernel<GB, XB, true>), grid, dim3(256), 0, s, u);
-        else hipLaunchKernelGGL((update3_kernel<GB, XB, false>), grid, dim3(256), 0, s, u);
+        if (fast) hipLaunchKernelGGL((update3_kernel<GB, XB, true, NP>), grid, dim3(256), 0, s, u);
+        else hipLaunchKernelGGL((update3_kernel<GB, XB, false, NP>), grid, dim3(256), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
-        hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB>), grid, dim3(256), 0, s, u);
+        hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB, NP>), grid, dim3(256), 0, s, u);
     }
     return hipGetLastError();
 }
@@ -2269,6 +2288,7 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
     const bool sticky = options & DION_OPT_STICKY_F64;
     bool gated = false;
     ChainCtx c{&p, ws, (int*)(ws + p.st), s, gate, &gated};
+    c.plain = x_bf16 && !(options & DION_OPT_EXACT_PRODUCTS);
     DION_TRY(mark(DION_PHASE_INIT));
     hipLaunchKernelGGL(init_state_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, c.st, (const int32_t*)flags, p.b,
                        (int)force64, (int)sticky);
@@ -2308,10 +2328,12 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
     }
     DION_TRY(mark(DION_PHASE_UPDATE));
     hipError_t he;
-    if (g_bf16) he = x_bf16 ? launch_update<true, true>(p, ws, Q, M, G, X, mu, lr, s)
-                            : launch_update<true, false>(p, ws, Q, M, G, X, mu, lr, s);
-    else he = x_bf16 ? launch_update<false, true>(p, ws, Q, M, G, X, mu, lr, s)
-                     : launch_update<false, false>(p, ws, Q, M, G, X, mu, lr, s);
+    if (c.plain) he = g_bf16 ? launch_update<true, true, 1>(p, ws, Q, M, G, X, mu, lr, s)
+                             : launch_update<false, true, 1>(p, ws, Q, M, G, X, mu, lr, s);
+    else if (g_bf16) he = x_bf16 ? launch_update<true, true, 3>(p, ws, Q, M, G, X, mu, lr, s)
+                                 : launch_update<true, false, 3>(p, ws, Q, M, G, X, mu, lr, s);
+    else he = x_bf16 ? launch_update<false, true, 3>(p, ws, Q, M, G, X, mu, lr, s)
+                     : launch_update<false, false, 3>(p, ws, Q, M, G, X, mu, lr, s);
     DION_TRY(he);
     DION_TRY(mark(DION_PHASE_FLAGS));
     if (flags) {

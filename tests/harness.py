@@ -91,11 +91,21 @@ def xband_violations(X0: np.ndarray, Xg: np.ndarray, P: np.ndarray, Qn: np.ndarr
     return int(np.count_nonzero((Xg < lo) | (Xg > hi)))
 
 
-def compare_step(wl, pre, post, G, rank, idx=None, arith: str = "split6"):
+def arith_for(wl, options: int = 0) -> str:
+    """The weight pass's arithmetic: plain bf16 products for bf16 weights (unless the exact-products
+    option asks for the fp32-accurate split), the exact split otherwise."""
+    from rank_orthonormalized_optimizer_amd._lib import OPT_EXACT_PRODUCTS
+    return "bf16" if wl.x_dtype == "bf16" and not (options & OPT_EXACT_PRODUCTS) else "split6"
+
+
+def compare_step(wl, pre, post, G, rank, idx=None, arith: str | None = None):
     """Per-matrix errors of one GPU step against the oracle started from `pre`.
 
-    pre/post: dicts of host arrays X, M, Q (+ post P).  Returns a list of dicts.
+    pre/post: dicts of host arrays X, M, Q (+ post P).  ``arith``: the weight pass's arithmetic
+    ("split6" or "bf16"; default from the workload's weight dtype).  Returns a list of dicts.
     """
+    if arith is None:
+        arith = arith_for(wl)
     out = []
     b = pre["X"].shape[0]
     m, n = pre["X"].shape[1], pre["X"].shape[2]

@@ -33,6 +33,7 @@ def test_header_enums_match_binding():
     assert vals["DION_OPT_FORCE_F32"] == _lib.OPT_FORCE_F32
     assert vals["DION_OPT_HOUSEHOLDER"] == _lib.OPT_HOUSEHOLDER
     assert vals["DION_OPT_SPECTRAL_SHIFT"] == _lib.OPT_SPECTRAL_SHIFT
+    assert vals["DION_OPT_EXACT_PRODUCTS"] == _lib.OPT_EXACT_PRODUCTS
     assert vals["DION_FLAG_F64"] == _lib.FLAG_F64 and vals["DION_FLAG_NONFINITE"] == _lib.FLAG_NONFINITE
     assert vals["DION_NUM_PHASES"] == _lib.NUM_PHASES == len(_lib.PHASES)
     for k, v in vals.items():
@@ -91,7 +92,7 @@ def call(**kw):
     (dict(options=_lib.OPT_FORCE_F32 | _lib.OPT_FORCE_F64), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_HOUSEHOLDER | _lib.OPT_FORCE_F32), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_HOUSEHOLDER, m=4097, n=4097, batch=1, rank=4097), _lib.ERR_OPTION),
-    (dict(options=64), _lib.ERR_OPTION),
+    (dict(options=128), _lib.ERR_OPTION),
     (dict(options=_lib.OPT_SPECTRAL_SHIFT | _lib.OPT_FORCE_F32), _lib.ERR_OPTION),
     (dict(X=0), _lib.ERR_NULL),
     (dict(Q=0), _lib.ERR_NULL),

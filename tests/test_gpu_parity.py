@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import TOL_KEYS, check_errs, compare_step, to_numpy, to_torch, tol_for
+from tests.harness import TOL_KEYS, arith_for, check_errs, compare_step, to_numpy, to_torch, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def run_teacher_forced(wl, device, options=0, steps=None):
             torch.cuda.synchronize()
             P = ws[:4 * g.batch * g.m * g.rank].view(torch.float32).view(g.batch, g.m, g.rank)
             post = {"X": to_numpy(Xd), "M": to_numpy(Md), "Q": to_numpy(Qd), "P": to_numpy(P)}
-            errs = compare_step(wl, pre, post, G, g.rank)
+            errs = compare_step(wl, pre, post, G, g.rank, arith=arith_for(wl, options))
             report.append((gi, t, errs, to_numpy(flags)))
     return report
 
@@ -262,3 +262,18 @@ def test_spectral_shift_chunks_bitwise(cuda):
     assert np.all(outs[0][3] & dion.FLAG_SHIFTED)
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("exact", [False, True])
+def test_bf16_weight_arithmetic(cuda, exact):
+    """bf16 weights: plain bf16 products by default (within the bf16 tolerance), the fp32-accurate
+    split with OPT_EXACT_PRODUCTS (then P Q'^T and the momentum update match the oracle to fp32
+    accuracy; X' differs from the oracle's unrounded X' by its bf16 rounding only)."""
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.SMALL[3]
+    rep = run_teacher_forced(wl, cuda, options=dion.OPT_EXACT_PRODUCTS if exact else 0)
+    worst = check(rep, tol_for(wl))
+    if exact:
+        assert worst["PQ"] <= 1e-4 and worst["dM"] <= 1e-4 and worst["M"] <= 1e-4, worst
+    else:
+        assert worst["PQ"] > 1e-4, "plain bf16 products should show bf16-level error"

@@ -13,7 +13,12 @@ from oracle import dion_step
 from tests.harness import check_errs, compare_step, tol_for
 
 
-def _emulated_step(wl, gi, mistake=None):
+def _rb(a):
+    """RNE_bf16 of fp32 values, as fp32."""
+    return W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.asarray(a, np.float32)))
+
+
+def _emulated_step(wl, gi, mistake=None, arith="split6"):
     g = wl.groups[gi]
     X, M, Q = W.make_state(wl, gi)
     G = W.make_grad(wl, gi, 1)
@@ -22,6 +27,10 @@ def _emulated_step(wl, gi, mistake=None):
     omm = np.float32(1.0 - wl.mu)
     if mistake == "scale":
         lr_s = np.float32(lr_s * 1.01)
+    if mistake == "scale30":
+        lr_s = np.float32(lr_s * 1.3)
+    # the products' operands: fp32 (the exact split) or rounded once to bf16 (plain bf16)
+    op = (lambda a: a) if arith == "split6" else _rb
     if mistake == "mu":
         omm = np.float32(omm * 1.01)
     for i in range(g.batch):
@@ -29,20 +38,20 @@ def _emulated_step(wl, gi, mistake=None):
                       Q[i].astype(np.float64), wl.mu, wl.lr, wl.eps)
         P32, R32, Q32 = o["P"].astype(np.float32), o["R"].astype(np.float32), o["Q"].astype(np.float32)
         B32 = M[i] + W.to_f64(G[i], wl.g_dtype).astype(np.float32)
-        upd_m = P32 @ R32.T
+        upd_m = op(P32) @ op(R32).T
         if mistake == "no_feedback":
             upd_m = np.zeros_like(upd_m)
         post["M"][i] = B32 - omm * upd_m
-        upd_x = P32 @ Q32.T
+        upd_x = op(P32) @ op(Q32).T
         if mistake == "q_rows_reversed":     # a wrong row index into Q'
-            upd_x = P32 @ Q32[::-1].T
+            upd_x = op(P32) @ op(Q32)[::-1].T
         x = W.to_f64(X[i], wl.x_dtype).astype(np.float32) - lr_s * upd_x
         if mistake == "no_update":
             x = W.to_f64(X[i], wl.x_dtype).astype(np.float32)
         post["X"][i] = W.f32_to_bf16_bits(x) if wl.x_dtype == "bf16" else x
         post["Q"][i] = Q32
         post["P"][i] = P32
-    return compare_step(wl, {"X": X, "M": M, "Q": Q}, post, G, g.rank)
+    return compare_step(wl, {"X": X, "M": M, "Q": Q}, post, G, g.rank, arith=arith)
 
 
 def _fails(errs, tol):
@@ -58,10 +67,10 @@ def _fails(errs, tol):
 CASES = {"f32": W.SMALL[1], "bf16": W.SMALL[3]}
 
 
-@pytest.mark.parametrize("case", sorted(CASES))
-def test_correct_emulation_passes(case):
+@pytest.mark.parametrize("case,arith", [("f32", "split6"), ("bf16", "split6"), ("bf16", "bf16")])
+def test_correct_emulation_passes(case, arith):
     wl = CASES[case]
-    errs = _emulated_step(wl, 0)
+    errs = _emulated_step(wl, 0, arith=arith)
     for e in errs:
         check_errs(e, tol_for(wl))
         assert e["Xband"] == 0
@@ -74,3 +83,11 @@ def test_correct_emulation_passes(case):
 def test_planted_update_mistake_is_caught(case, mistake):
     wl = CASES[case]
     assert _fails(_emulated_step(wl, 0, mistake), tol_for(wl)), mistake
+
+
+@pytest.mark.parametrize("mistake", ["no_update", "scale30", "q_rows_reversed", "no_feedback"])
+def test_planted_mistake_is_caught_with_plain_bf16_products(mistake):
+    """Plain bf16 products widen the element-wise band to the bf16 rounding of the operands
+    (about 2^-7 of |P| |Q'|^T); mistakes beyond the bf16 tolerance are still caught."""
+    wl = CASES["bf16"]
+    assert _fails(_emulated_step(wl, 0, mistake, arith="bf16"), tol_for(wl)), mistake
