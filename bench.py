@@ -366,15 +366,31 @@ def measure(wl, dev, stream, args, cpu_s: float, host_inputs: bool) -> dict:
     for s in stacks:   # what DionStack does: skip launching the fp32 chain once a stack is all-fp64
         s["hint"] = None if (args.no_sticky or args.no_hint) else dion.StickyF64Hint(s["flags"])
 
-    def one_step(k, events=None):
+    # independent stacks run concurrently, each on its own stream forked from and joined back
+    # into the launch stream, so one stack's latency-bound QR overlaps another's streaming passes
+    side = [torch.cuda.Stream(device=dev) for _ in stacks] if len(stacks) > 1 and not args.serial_stacks else None
+
+    def issue(k, base, events=None, hints=True):
+        if side is not None:
+            fork = torch.cuda.Event()
+            fork.record(base)
         for si, s in enumerate(stacks):
             g = s["g"]
+            st = base if side is None else side[si]
+            if side is not None:
+                st.wait_event(fork)
             o = opts if s["hint"] is None else s["hint"].options(opts)
             dion.step_(s["X"], s["G"][k % len(s["G"])], s["M"], s["Q"], g.rank, wl.mu, wl.lr, wl.eps,
-                       workspace=s["ws"], flags=s["flags"], options=o, stream=stream,
+                       workspace=s["ws"], flags=s["flags"], options=o, stream=st,
                        events=None if events is None else events[si])
-            if s["hint"] is not None:
-                s["hint"].after_step(stream)
+            if hints and s["hint"] is not None:
+                s["hint"].after_step(st)
+        if side is not None:
+            for st in side:
+                base.wait_stream(st)
+
+    def one_step(k, events=None):
+        issue(k, stream, events)
 
     print(f"[bench] {wl.name}: warmup", file=sys.stderr, flush=True)
     for k in range(args.warmup):
@@ -413,11 +429,7 @@ def measure(wl, dev, stream, args, cpu_s: float, host_inputs: bool) -> dict:
             gph = torch.cuda.CUDAGraph()
             with torch.cuda.stream(cap):
                 gph.capture_begin()
-                for s_ in stacks:
-                    g_ = s_["g"]
-                    o = opts if s_["hint"] is None else s_["hint"].options(opts)
-                    dion.step_(s_["X"], s_["G"][j % len(s_["G"])], s_["M"], s_["Q"], g_.rank, wl.mu, wl.lr,
-                               wl.eps, workspace=s_["ws"], flags=s_["flags"], options=o, stream=cap)
+                issue(j, cap, hints=False)
                 gph.capture_end()
             graphs.append(gph)
         stream.wait_stream(cap)
@@ -479,6 +491,7 @@ def measure(wl, dev, stream, args, cpu_s: float, host_inputs: bool) -> dict:
         "householder_matrices": nhh, "nonfinite_matrices": nbad,
         "phase_ms": {k: round(v, 5) for k, v in phase_ms.items()},
         "phase_roofline": pr,
+        "concurrent_stacks": side is not None,
         "launch": launch, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
         "wall_s_timed_region_eager": wall, "host_enqueue_ms_per_step": 1000.0 * enqueue / args.steps,
         "roofline": roof,
@@ -508,6 +521,8 @@ def main() -> int:
     ap.add_argument("--no-hint", action="store_true",
                     help="launch the fp32 chain every step even when every matrix is on the sticky fp64 chain")
     ap.add_argument("--chunks", type=int, default=0, help="concurrent chunks per stack (0 = library default)")
+    ap.add_argument("--serial-stacks", action="store_true",
+                    help="step a workload's stacks one after another on one stream (default: concurrently)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time the eager steps only (default: also capture them as HIP graphs and time the replays, "

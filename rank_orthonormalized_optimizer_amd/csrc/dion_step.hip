@@ -906,6 +906,8 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
             __syncthreads();
             mma();
         }
+        // the epilogue below reuses the part tiles' LDS: every wave must be done reading them
+        __syncthreads();
     } else {
         Loader6<BM, S6_KC8, A6_NONE> lp;
         Loader6<BN, S6_KC8, A6_NONE> lr, lq;
