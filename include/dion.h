@@ -204,6 +204,35 @@ int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q,
                                void* const* events);
 
 /*
+ * Optional outputs of dion_step_batched_ex (any field may be NULL).
+ *   events  DION_NUM_PHASES + 1 hipEvent_t handles, recorded at the phase boundaries as in
+ *           dion_step_batched_profiled
+ *   rmmc    device fp32 [batch]: each matrix's Relative Maximum Momentum Change over this step,
+ *           max_ij |M'_ij - M_ij| / max_ij |M_ij| (M entering the step, M' leaving it; 0 where
+ *           both maxima are 0, +inf where only max |M| is).  The statistic is named in
+ *           "CurvaDion: Curvature-Adaptive Distributed Orthonormalization" (mlsanity.com,
+ *           "Abstract (arXiv)") as a curvature proxy built from the momentum at O(d) cost per
+ *           layer; the page gives no formula, and this is the reading of its name.  It is taken
+ *           in the pass that writes M' (one more small launch), written on `stream`.
+ */
+typedef struct {
+    void* const* events;
+    float* rmmc;
+} dion_step_outputs;
+
+/*
+ * dion_step_batched with optional outputs (`out` may be NULL).  The rmmc array must be 4-byte
+ * aligned and overlap no other buffer; otherwise as dion_step_batched.
+ */
+int dion_step_batched_ex(void* X, const void* G, float* M, float* Q,
+                         int64_t m, int64_t n, int64_t batch, int64_t rank,
+                         float mu, float lr, float eps,
+                         int x_dtype, int g_dtype,
+                         void* workspace, size_t workspace_bytes,
+                         int32_t* flags, uint32_t options, void* stream,
+                         const dion_step_outputs* out);
+
+/*
  * dion_step_batched without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, step, results and status codes as dion_step_batched, minus the workspace; the

@@ -38,10 +38,16 @@ NUM_PHASES = 10
 PHASES = ("init", "f32_product", "f32_qr", "f32_backproject", "f64_product", "f64_qr", "f64_backproject",
           "norms", "update", "flags")
 
-EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_step_batched_noalloc",
+EXPORTS = ("dion_workspace_size", "dion_step_batched", "dion_step_batched_profiled", "dion_step_batched_ex",
+           "dion_step_batched_noalloc",
            "dion_adamw_step",
            "dion_lion_step", "dion_lambda_max_workspace_size", "dion_lambda_max_batched", "dion_strerror",
            "dion_version")
+
+
+class StepOutputs(ctypes.Structure):
+    """dion_step_outputs: optional phase events and the per-matrix momentum-change output."""
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("rmmc", ctypes.c_void_p)]
 
 
 class DionError(RuntimeError):
@@ -72,6 +78,8 @@ def load() -> ctypes.CDLL:
                                       vp, ctypes.c_uint32, vp]
     lib.dion_step_batched_profiled.restype = ctypes.c_int
     lib.dion_step_batched_profiled.argtypes = lib.dion_step_batched.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+    lib.dion_step_batched_ex.restype = ctypes.c_int
+    lib.dion_step_batched_ex.argtypes = lib.dion_step_batched.argtypes + [ctypes.POINTER(StepOutputs)]
     f32, i32 = ctypes.c_float, ctypes.c_int
     lib.dion_step_batched_noalloc.restype = ctypes.c_int
     lib.dion_step_batched_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, f32, i32, i32, vp,
@@ -107,17 +115,22 @@ def version() -> int:
 def step_batched_raw(X: int, G: int, M: int, Q: int, m: int, n: int, batch: int, rank: int,
                      mu: float, lr: float, eps: float, x_dtype: int, g_dtype: int,
                      workspace: int, workspace_bytes: int, flags: int, options: int, stream: int,
-                     events=None) -> int:
-    """dion_step_batched (or, with ``events``, the profiled entry) with integer addresses.
+                     events=None, rmmc: int = 0) -> int:
+    """dion_step_batched (or, with ``events`` or ``rmmc``, the extended entry) with integer addresses.
 
-    ``events``: sequence of NUM_PHASES + 1 hipEvent_t handles (ints).  Returns the status code.
+    ``events``: sequence of NUM_PHASES + 1 hipEvent_t handles (ints); ``rmmc``: address of a
+    device fp32 [batch] array for the momentum-change statistic.  Returns the status code.
     """
     args = (X or None, G or None, M or None, Q or None, m, n, batch, rank, mu, lr, eps, x_dtype, g_dtype,
             workspace or None, workspace_bytes, flags or None, options, stream or None)
-    if events is None:
+    if events is None and not rmmc:
         return int(load().dion_step_batched(*args))
-    arr = (ctypes.c_void_p * (NUM_PHASES + 1))(*[int(e) for e in events])
-    return int(load().dion_step_batched_profiled(*args, arr))
+    out = StepOutputs()
+    if events is not None:
+        arr = (ctypes.c_void_p * (NUM_PHASES + 1))(*[int(e) for e in events])
+        out.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    out.rmmc = rmmc or None
+    return int(load().dion_step_batched_ex(*args, ctypes.byref(out)))
 
 
 def step_batched_noalloc_raw(X: int, G: int, M: int, Q: int, m: int, n: int, batch: int, rank: int,

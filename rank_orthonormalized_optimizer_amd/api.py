@@ -33,7 +33,8 @@ def workspace_for(m: int, n: int, batch: int, rank: int, device) -> torch.Tensor
 
 def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | None, rank: int,
           mu: float, lr: float, eps: float = 1e-8, *, workspace: torch.Tensor | None = None,
-          flags: torch.Tensor | None = None, options: int = 0, stream=None, events=None) -> None:
+          flags: torch.Tensor | None = None, options: int = 0, stream=None, events=None,
+          rmmc: torch.Tensor | None = None) -> None:
     """One Dion step on a stack, in place on X, M and Q.
 
     X, G: [b, m, n] float32 or bfloat16; M: [b, m, n] float32; Q: [b, n, rank] float32.
@@ -41,6 +42,8 @@ def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | N
     Enqueued on ``stream`` (default: torch's current stream) with no host sync.
     ``events``: optional NUM_PHASES + 1 recorded torch.cuda.Event objects, re-recorded at the
     phase boundaries of the step (profiling).
+    ``rmmc`` (float32 [b], optional) receives each matrix's relative maximum momentum change
+    max |M' - M| / max |M| over the step.
     """
     if X.dim() != 3:
         raise ValueError("X must be a stack [batch, m, n]; route 1-D parameters to AdamW or Lion")
@@ -52,6 +55,8 @@ def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | N
         _check(Q, "Q", (b, n, rank), (torch.float32,))
     if flags is not None:
         _check(flags, "flags", (b,), (torch.int32,))
+    if rmmc is not None:
+        _check(rmmc, "rmmc", (b,), (torch.float32,))
     if workspace is None:
         workspace = workspace_for(m, n, b, rank, X.device)
     if stream is None:
@@ -61,7 +66,8 @@ def step_(X: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor | N
                                workspace.data_ptr(), workspace.numel(),
                                flags.data_ptr() if flags is not None else 0, int(options),
                                int(stream.cuda_stream),
-                               None if events is None else [e.cuda_event for e in events])
+                               None if events is None else [e.cuda_event for e in events],
+                               rmmc.data_ptr() if rmmc is not None else 0)
     if st != _lib.OK:
         raise _lib.DionError(st)
 

@@ -76,18 +76,38 @@ size_t dion_workspace_size(int64_t m, int64_t n, int64_t batch, int64_t rank) {
     return p.total;
 }
 
-int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch,
-                               int64_t rank, float mu, float lr, float eps, int x_dtype, int g_dtype,
-                               void* workspace, size_t workspace_bytes, int32_t* flags, uint32_t options,
-                               void* stream, void* const* events) {
+int dion_step_batched_ex(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch,
+                         int64_t rank, float mu, float lr, float eps, int x_dtype, int g_dtype, void* workspace,
+                         size_t workspace_bytes, int32_t* flags, uint32_t options, void* stream,
+                         const dion_step_outputs* out) {
     dion::Plan p;
     int st = dion::check_step_args(m, n, batch, rank, mu, lr, eps, x_dtype, g_dtype, options, &p);
     if (st != DION_OK || batch == 0) return st;
     st = dion::check_step_buffers(p, X, G, M, Q, x_dtype, g_dtype, workspace, workspace_bytes, flags);
     if (st != DION_OK) return st;
+    float* rmmc = out ? out->rmmc : nullptr;
+    if (rmmc) {
+        if ((uintptr_t)rmmc & 3u) return DION_ERR_ALIGN;
+        const double mn = (double)batch * (double)m * (double)n;
+        const Range r = span(rmmc, (double)batch * 4);
+        const Range others[6] = {span(X, mn * (x_dtype == DION_BF16 ? 2 : 4)), span(G, mn * (g_dtype == DION_BF16 ? 2 : 4)),
+                                 span(M, mn * 4), span(Q, rank > 0 ? (double)batch * (double)n * (double)rank * 4 : 0.0),
+                                 span(workspace, (double)p.total), span(flags, flags ? (double)batch * 4 : 0.0)};
+        for (const Range& o : others)
+            if (overlap(r, o)) return DION_ERR_OVERLAP;
+    }
     const int e = dion::run_step(p, X, G, M, Q, mu, lr, eps, x_dtype == DION_BF16, g_dtype == DION_BF16,
-                                 (char*)workspace, flags, options, stream, events);
+                                 (char*)workspace, flags, options, stream, out ? out->events : nullptr, rmmc);
     return e ? DION_ERR_HIP - e : DION_OK;
+}
+
+int dion_step_batched_profiled(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch,
+                               int64_t rank, float mu, float lr, float eps, int x_dtype, int g_dtype,
+                               void* workspace, size_t workspace_bytes, int32_t* flags, uint32_t options,
+                               void* stream, void* const* events) {
+    const dion_step_outputs out{events, nullptr};
+    return dion_step_batched_ex(X, G, M, Q, m, n, batch, rank, mu, lr, eps, x_dtype, g_dtype, workspace,
+                                workspace_bytes, flags, options, stream, &out);
 }
 
 int dion_step_batched(void* X, const void* G, float* M, float* Q, int64_t m, int64_t n, int64_t batch, int64_t rank,

@@ -40,10 +40,11 @@ struct Plan {
     int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
     int64_t c0;        // index of the first matrix (0, or a chunk's offset in the whole stack)
     // byte offsets into the workspace (all 256-byte aligned)
-    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw;
+    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw, mx;
     size_t total;
     // bytes per matrix of each region (a region is [batch][...] and contiguous)
-    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, spw;
+    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, spw, smx;
+    int64_t nmx;       // momentum-change partials per matrix (one per 64 x 64 block of M)
 };
 
 // The sub-plan of matrices [c0, c0 + cb): same sizes, region offsets advanced to matrix c0.
@@ -55,7 +56,7 @@ inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
     q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart; q.gpart += c * p.sgpart;
-    q.pw += c * p.spw;
+    q.pw += c * p.spw; q.mx += c * p.smx;
     return q;
 }
 
@@ -126,6 +127,8 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.gpart = take(B * gpm);               // Gram partials (either chain)
     const double pw = (2.0 * r * kShiftPool + 2) * 8;
     q.pw = take(B * pw);                   // spectral-shift pool: two r x 32 fp64 buffers, trace, estimate
+    q.nmx = ((m + 63) / 64) * ((n + 63) / 64);
+    q.mx = take(B * q.nmx * 2 * 4);        // per block of M: max |M' - M| and max |M| (fp32)
     q.total = off;
     if (q.total > ((size_t)1 << 46)) return false;
     q.sP32 = (size_t)(m * r * 4); q.sR32 = (size_t)(n * r * 4); q.scs = (size_t)(r * 8); q.sst = 4; q.skap = 16; q.semax = kNearIdParts * 8;
@@ -133,6 +136,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.sP64 = q.sP64b = (size_t)(m * r * 8); q.sR64 = (size_t)(n * r * 8); q.spart = (size_t)(q.nchunk * r * 8);
     q.sgpart = (size_t)gpm;
     q.spw = (size_t)pw;
+    q.smx = (size_t)(q.nmx * 2 * 4);
     *p = q;
     return true;
 }
@@ -146,9 +150,11 @@ int check_step_buffers(const Plan& p, const void* X, const void* G, const float*
                        int g_dtype, const void* workspace, size_t workspace_bytes, const int32_t* flags);
 
 // Run the step (arguments already validated).  Returns a hipError_t value.
+// rmmc: null, or device fp32 [b] for the relative maximum momentum change of each matrix.
 int run_step(const Plan& p, void* X, const void* G, float* M, float* Q,
              float mu, float lr, float eps, int x_bf16, int g_bf16,
-             char* ws, int32_t* flags, uint32_t options, void* stream, void* const* events);
+             char* ws, int32_t* flags, uint32_t options, void* stream, void* const* events,
+             float* rmmc = nullptr);
 
 // Multi-power-iteration estimate of lambda_max for a stack of symmetric PSD matrices (only the
 // lower triangle of W is read).  Per matrix bz: pool and trace in ws + bz * ws_stride (doubles:

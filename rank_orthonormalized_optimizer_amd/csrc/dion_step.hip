@@ -667,13 +667,42 @@ struct UpdArgs {
     int m, n, r, kp;                                  // kp: r rounded up to whole 32-k slabs
     bool vec;                                         // r % 4 == 0: 16-byte row loads
     float one_minus_mu, lr_s;
+    // momentum-change partials (null: not requested): per matrix nmx slots of (max |M' - M|,
+    // max |M|), one per tile, at tile y * tiles_x + x
+    float* mx;
+    int64_t nmx;
 };
+
+// Maxima of a and b over the workgroup (blockDim.x a multiple of 64, every thread calling);
+// thread 0 writes them to out[0] and out[1].
+__device__ void wg_max2_store(float a, float b, float* out) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a = fmaxf(a, __shfl_xor(a, o));
+        b = fmaxf(b, __shfl_xor(b, o));
+    }
+    __shared__ float sa[16], sb[16];
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sa[w] = a; sb[w] = b; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < nw; ++i) { a = fmaxf(a, sa[i]); b = fmaxf(b, sb[i]); }
+        out[0] = a;
+        out[1] = b;
+    }
+}
+
+// Slot of this workgroup's momentum-change partials (tile coordinates x, y).
+__device__ __forceinline__ float* mx_slot(const UpdArgs& u, int bz, int tx, int ty, int tiles_x) {
+    return u.mx + ((int64_t)bz * u.nmx + (int64_t)ty * tiles_x + tx) * 2;
+}
 
 // The tile of a matrix whose orthonormalization broke down with no fallback left (ST_FAIL):
 // there is no factor to update with, so the step is the rank-0 one, M <- M + G, X untouched.
 template <int BM, int BN, bool G_BF16>
 __device__ void failed_tile(const UpdArgs& u, int bz, int m0, int n0) {
     const int64_t mn = (int64_t)u.m * u.n;
+    float dmax = 0.f, smax = 0.f;
     for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
         const int row = m0 + idx / BN, col = n0 + idx % BN;
         if (row >= u.m || col >= u.n) continue;
@@ -681,8 +710,12 @@ __device__ void failed_tile(const UpdArgs& u, int bz, int m0, int n0) {
         float g;
         if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)u.G)[off]);
         else g = ((const float*)u.G)[off];
-        u.M[off] += g;
+        const float mo = u.M[off], mnew = mo + g;
+        u.M[off] = mnew;
+        dmax = fmaxf(dmax, fabsf(mnew - mo));
+        smax = fmaxf(smax, fabsf(mo));
     }
+    if (u.mx) wg_max2_store(dmax, smax, mx_slot(u, bz, n0 / BN, m0 / BM, (u.n + BN - 1) / BN));
 }
 
 // One BM x BN tile of M and X per workgroup of WGM x WGN waves: both rank-kp products on the
@@ -790,6 +823,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
                 if constexpr (X_BF16) xv[i][j][v] = bf16_bits_to_float(((const uint16_t*)u.X)[off]);
                 else xv[i][j][v] = ((const float*)u.X)[off];
             }
+    float dmax = 0.f, smax = 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -800,11 +834,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
                 const int col = n0 + wn * FN * 16 + j * 16 + fr;
                 if (row >= u.m || col >= u.n) continue;
                 const int64_t l = (int64_t)row * u.n + col, off = bz * mn + l;
-                Mp[l] = (mv[i][j][v] + gv[i][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                const float mnew = (mv[i][j][v] + gv[i][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                Mp[l] = mnew;
+                dmax = fmaxf(dmax, fabsf(mnew - mv[i][j][v]));
+                smax = fmaxf(smax, fabsf(mv[i][j][v]));
                 const float x = xv[i][j][v] - u.lr_s * acc2[i][j][v];
                 if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(x);
                 else ((float*)u.X)[off] = x;
             }
+    if (u.mx) wg_max2_store(dmax, smax, mx_slot(u, bz, tid.x, tid.y, (u.n + BN - 1) / BN));
 }
 
 // The weight pass for large stacks: 128 x 64 tiles of M and X, four waves of 64 x 32 that
@@ -938,6 +976,7 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     const int64_t mn = (int64_t)u.m * u.n;
     // full tiles: each product tile goes through LDS to rows of 64 consecutive columns, so M, G
     // and X move as 16-byte (bf16: 8-byte) vectors; all loads of a pass before its stores
+    float dmax = 0.f, smax = 0.f;   // momentum change and size over this tile
     if (m0 + BM <= u.m && n0 + BN <= u.n && (u.n & 3) == 0) {
         constexpr int TP = BN + 4;
         float* tl = (float*)lds;
@@ -982,8 +1021,13 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                 const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
                 if (pass == 0) {
                     const float c = u.one_minus_mu;
-                    nt_st4(u.M + off, float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
-                                                   (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w});
+                    const float4 mnew = float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
+                                               (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w};
+                    nt_st4(u.M + off, mnew);
+                    dmax = fmaxf(fmaxf(fmaxf(dmax, fabsf(mnew.x - xv[q].x)), fmaxf(fabsf(mnew.y - xv[q].y),
+                                 fabsf(mnew.z - xv[q].z))), fabsf(mnew.w - xv[q].w));
+                    smax = fmaxf(fmaxf(fmaxf(smax, fabsf(xv[q].x)), fmaxf(fabsf(xv[q].y), fabsf(xv[q].z))),
+                                 fabsf(xv[q].w));
                 } else {
                     const float c = u.lr_s;
                     const float4 x = float4{xv[q].x - c * av[q].x, xv[q].y - c * av[q].y, xv[q].z - c * av[q].z,
@@ -997,6 +1041,7 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
             }
             __syncthreads();
         }
+        if (u.mx) wg_max2_store(dmax, smax, mx_slot(u, bz, tid.x, tid.y, (u.n + BN - 1) / BN));
         return;
     }
     // partial tiles: in the MFMA layout, in two halves of rows, all loads of a half before its stores
@@ -1029,23 +1074,50 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                     const int row = m0 + wm * 64 + 16 * i + 4 * fc + v, col = n0 + wn * 32 + 16 * j + fr;
                     if (row >= u.m || col >= u.n) continue;
                     const int64_t l = (int64_t)row * u.n + col, off = bz * mn + l;
-                    Mp[l] = (mv[ii][j][v] + gv[ii][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                    const float mnew = (mv[ii][j][v] + gv[ii][j][v]) - u.one_minus_mu * acc1[i][j][v];
+                    Mp[l] = mnew;
+                    dmax = fmaxf(dmax, fabsf(mnew - mv[ii][j][v]));
+                    smax = fmaxf(smax, fabsf(mv[ii][j][v]));
                     const float x = xv[ii][j][v] - u.lr_s * acc2[i][j][v];
                     if constexpr (X_BF16) ((uint16_t*)u.X)[off] = float_to_bf16_bits(x);
                     else ((float*)u.X)[off] = x;
                 }
     }
+    if (u.mx) wg_max2_store(dmax, smax, mx_slot(u, bz, tid.x, tid.y, (u.n + BN - 1) / BN));
 }
 
-// rank 0: M <- M + G
+// rank 0: M <- M + G (grid: blocks per matrix x matrices); with mx set, each block leaves
+// the momentum change and size over its share in its slot of the matrix's partials
 template <bool G_BF16>
-__global__ __launch_bounds__(256) void add_grad_kernel(float* M, const void* G, int64_t total) {
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+__global__ __launch_bounds__(256) void add_grad_kernel(float* M, const void* G, int64_t mn, float* mx,
+                                                       int64_t nmx) {
+    const int64_t bz = blockIdx.y, base = bz * mn;
+    float dmax = 0.f, smax = 0.f;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < mn; idx += (int64_t)gridDim.x * 256) {
         float g;
-        if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)G)[idx]);
-        else g = ((const float*)G)[idx];
-        M[idx] += g;
+        if constexpr (G_BF16) g = bf16_bits_to_float(((const uint16_t*)G)[base + idx]);
+        else g = ((const float*)G)[base + idx];
+        const float mo = M[base + idx], mnew = mo + g;
+        M[base + idx] = mnew;
+        dmax = fmaxf(dmax, fabsf(mnew - mo));
+        smax = fmaxf(smax, fabsf(mo));
     }
+    if (mx) wg_max2_store(dmax, smax, mx + (bz * nmx + blockIdx.x) * 2);
+}
+
+// rmmc[bz] = max |M' - M| / max |M| of matrix bz from its nparts partials (0 or +inf where max
+// |M| = 0: no change, or a change from zero momentum).  One workgroup per matrix.
+__global__ __launch_bounds__(256) void rmmc_kernel(const float* mx, int64_t nmx, int nparts, float* rmmc) {
+    const int64_t bz = blockIdx.x;
+    float d = 0.f, s = 0.f;
+    for (int i = threadIdx.x; i < nparts; i += 256) {
+        d = fmaxf(d, mx[(bz * nmx + i) * 2]);
+        s = fmaxf(s, mx[(bz * nmx + i) * 2 + 1]);
+    }
+    __shared__ float out[2];
+    wg_max2_store(d, s, out);
+    __syncthreads();
+    if (threadIdx.x == 0) rmmc[bz] = out[1] > 0.f ? out[0] / out[1] : (out[0] > 0.f ? INFINITY : 0.f);
 }
 
 __global__ void zero_flags_kernel(int32_t* flags, int64_t b) {
@@ -2236,15 +2308,18 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
                   : btp_gemm<T, SRC_SUM_F32>(c, M, G, gsz, P, R, A64, A64);
 }
 
+// nparts: set to the number of momentum-change partials per matrix (tiles of the launch)
 template <bool GB, bool XB, int NP>
 static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, float* M, const void* G, void* X,
-                                float mu, float lr, hipStream_t s) {
+                                float mu, float lr, hipStream_t s, float* mx, int* nparts) {
     UpdArgs u{};
     u.P = (const float*)(ws + p.P32);
     u.R = (const float*)(ws + p.R32);
     u.Q = Q;
     u.M = M; u.G = G; u.X = X;
     u.st = (const int*)(ws + p.st);
+    u.mx = mx;
+    u.nmx = p.nmx;
     u.m = (int)p.m; u.n = (int)p.n; u.r = (int)p.r; u.kp = (int)p.kp;
     u.vec = (p.r % 4) == 0;
     u.one_minus_mu = 1.0f - mu;
@@ -2253,12 +2328,14 @@ static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, f
     const int64_t big = ((p.n + 63) / 64) * ((p.m + 127) / 128) * p.b;
     if (big >= kUpdBigMinTiles) {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 127) / 128), (unsigned)p.b);
+        *nparts = (int)(grid.x * grid.y);
         // all tiles interior, whole slabs, vector-legal rows: the two-set branch-free loop
         const bool fast = p.m % 128 == 0 && p.n % 64 == 0 && p.r % kSplitK == 0 && p.r >= 2 * kSplitK && u.vec;
         if (fast) hipLaunchKernelGGL((update3_kernel<GB, XB, true, NP>), grid, dim3(256), 0, s, u);
         else hipLaunchKernelGGL((update3_kernel<GB, XB, false, NP>), grid, dim3(256), 0, s, u);
     } else {
         dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)((p.m + 63) / 64), (unsigned)p.b);
+        *nparts = (int)(grid.x * grid.y);
         hipLaunchKernelGGL((update_kernel<64, 64, 2, 2, GB, XB, NP>), grid, dim3(256), 0, s, u);
     }
     return hipGetLastError();
@@ -2267,16 +2344,23 @@ static hipError_t launch_update(const Plan& p, const char* ws, const float* Q, f
 // The whole step for the matrices of one chunk, on stream s.
 static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps,
                      int x_bf16, int g_bf16, char* ws, int32_t* flags, uint32_t options, hipStream_t s,
-                     void* const* ev, hipEvent_t gate = nullptr) {
+                     void* const* ev, hipEvent_t gate = nullptr, float* rmmc = nullptr) {
+    float* mx = rmmc ? (float*)(ws + p.mx) : nullptr;
     auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (p.b == 0) return 0;
     const int64_t mn = p.m * p.n;
     if (p.r == 0) {
         for (int i = 0; i < DION_NUM_PHASES; ++i) DION_TRY(mark(i));
-        dim3 grid(grid_1d(p.b * mn, 8192));
-        if (g_bf16) hipLaunchKernelGGL((add_grad_kernel<true>), grid, dim3(256), 0, s, M, G, p.b * mn);
-        else hipLaunchKernelGGL((add_grad_kernel<false>), grid, dim3(256), 0, s, M, G, p.b * mn);
+        const int64_t per = std::min<int64_t>(p.nmx, std::max<int64_t>(1, 8192 / p.b));
+        dim3 grid(grid_1d(mn, per), (unsigned)p.b);
+        if (g_bf16) hipLaunchKernelGGL((add_grad_kernel<true>), grid, dim3(256), 0, s, M, G, mn, mx, p.nmx);
+        else hipLaunchKernelGGL((add_grad_kernel<false>), grid, dim3(256), 0, s, M, G, mn, mx, p.nmx);
         DION_TRY(hipGetLastError());
+        if (rmmc) {
+            hipLaunchKernelGGL(rmmc_kernel, dim3((unsigned)p.b), dim3(256), 0, s, (const float*)mx, p.nmx,
+                               (int)grid.x, rmmc);
+            DION_TRY(hipGetLastError());
+        }
         if (flags) {  // a fill kernel rather than a memset node, so callers may capture the step in a graph
             hipLaunchKernelGGL(zero_flags_kernel, dim3(grid_1d(p.b)), dim3(256), 0, s, flags, p.b);
             DION_TRY(hipGetLastError());
@@ -2330,13 +2414,18 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
     }
     DION_TRY(mark(DION_PHASE_UPDATE));
     hipError_t he;
-    if (c.plain) he = g_bf16 ? launch_update<true, true, 1>(p, ws, Q, M, G, X, mu, lr, s)
-                             : launch_update<false, true, 1>(p, ws, Q, M, G, X, mu, lr, s);
-    else if (g_bf16) he = x_bf16 ? launch_update<true, true, 3>(p, ws, Q, M, G, X, mu, lr, s)
-                                 : launch_update<true, false, 3>(p, ws, Q, M, G, X, mu, lr, s);
-    else he = x_bf16 ? launch_update<false, true, 3>(p, ws, Q, M, G, X, mu, lr, s)
-                     : launch_update<false, false, 3>(p, ws, Q, M, G, X, mu, lr, s);
+    int nparts = 0;
+    if (c.plain) he = g_bf16 ? launch_update<true, true, 1>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                             : launch_update<false, true, 1>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
+    else if (g_bf16) he = x_bf16 ? launch_update<true, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                                 : launch_update<true, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
+    else he = x_bf16 ? launch_update<false, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                     : launch_update<false, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
     DION_TRY(he);
+    if (rmmc) {
+        hipLaunchKernelGGL(rmmc_kernel, dim3((unsigned)p.b), dim3(256), 0, s, (const float*)mx, p.nmx, nparts, rmmc);
+        DION_TRY(hipGetLastError());
+    }
     DION_TRY(mark(DION_PHASE_FLAGS));
     if (flags) {
         hipLaunchKernelGGL(flags_out_kernel, dim3((unsigned)p.b), dim3(256), 0, s, c.st,
@@ -2387,7 +2476,7 @@ static int auto_chunks(const Plan&) {
 }
 
 int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu, float lr, float eps, int x_bf16,
-             int g_bf16, char* ws, int32_t* flags, uint32_t options, void* stream, void* const* ev) {
+             int g_bf16, char* ws, int32_t* flags, uint32_t options, void* stream, void* const* ev, float* rmmc) {
     hipStream_t s = (hipStream_t)stream;
     if (p.b == 0) return 0;
     int nc = (int)((options >> DION_OPT_CHUNKS_SHIFT) & 15u);
@@ -2395,7 +2484,7 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu
     if (nc > kMaxChunks) nc = kMaxChunks;
     if (nc > p.b) nc = (int)p.b;
     if (nc <= 1)
-        return run_chunk(p, X, G, M, Q, mu, lr, eps, x_bf16, g_bf16, ws, flags, options, s, ev);
+        return run_chunk(p, X, G, M, Q, mu, lr, eps, x_bf16, g_bf16, ws, flags, options, s, ev, nullptr, rmmc);
     std::lock_guard<std::mutex> lock(g_stream_mu);
     StreamSet* ss = nullptr;
     DION_TRY(stream_set(&ss));
@@ -2408,7 +2497,7 @@ int run_step(const Plan& p, void* X, const void* G, float* M, float* Q, float mu
         if (c > 0) DION_TRY(hipStreamWaitEvent(ss->s[c], ss->gate[c - 1], 0));
         int e = run_chunk(q, (char*)X + c0 * mn * xs, (const char*)G + c0 * mn * gs, M + c0 * mn,
                           Q ? Q + c0 * p.n * p.r : nullptr, mu, lr, eps, x_bf16, g_bf16, ws, flags ? flags + c0 : nullptr,
-                          options, ss->s[c], c == 0 ? ev : nullptr, ss->gate[c]);
+                          options, ss->s[c], c == 0 ? ev : nullptr, ss->gate[c], rmmc ? rmmc + c0 : nullptr);
         if (e) return e;
         DION_TRY(hipEventRecord(ss->join[c], ss->s[c]));
         DION_TRY(hipStreamWaitEvent(s, ss->join[c], 0));
