@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libdion_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["dion_step.hip", "elementwise.hip", "spectral.hip", "noalloc.hip", "dion_api.cpp"]
+SOURCES = ["dion_step.hip", "stream16.hip", "elementwise.hip", "spectral.hip", "noalloc.hip", "dion_api.cpp"]
 ARCH = "gfx950"
 
 

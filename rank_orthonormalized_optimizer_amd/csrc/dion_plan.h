@@ -31,6 +31,10 @@ constexpr int kMpiMaxIters = 64;
 constexpr int kShiftPool = 32;
 constexpr int kShiftIters = 10;
 
+// Row pitch (elements) of the transposed bf16 copy of Q or P used by the plain bf16 products:
+// rows padded with zeros to whole 32-wide slabs.
+inline int64_t stream16_pitch(int64_t rows) { return (rows + 31) / 32 * 32; }
+
 struct Plan {
     int64_t m, n, b, r;
     int64_t nblk;      // number of rank column blocks
@@ -40,10 +44,10 @@ struct Plan {
     int64_t kp;        // rank padded to a multiple of 32 (k-slabs of the split-bf16 weight pass)
     int64_t c0;        // index of the first matrix (0, or a chunk's offset in the whole stack)
     // byte offsets into the workspace (all 256-byte aligned)
-    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw, mx;
+    size_t P32, R32, cs, st, kap, emax, W, L, Td, Tf, P64, P64b, R64, part, gpart, pw, mx, t16;
     size_t total;
     // bytes per matrix of each region (a region is [batch][...] and contiguous)
-    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, spw, smx;
+    size_t sP32, sR32, scs, sst, skap, semax, sW, sL, sTd, sTf, sP64, sP64b, sR64, spart, sgpart, spw, smx, st16;
     int64_t nmx;       // momentum-change partials per matrix (one per 64 x 64 block of M)
 };
 
@@ -56,7 +60,7 @@ inline Plan chunk_plan(const Plan& p, int64_t c0, int64_t cb) {
     q.P32 += c * p.sP32; q.R32 += c * p.sR32; q.cs += c * p.scs; q.st += c * p.sst; q.kap += c * p.skap; q.emax += c * p.semax;
     q.W += c * p.sW; q.L += c * p.sL; q.Td += c * p.sTd; q.Tf += c * p.sTf; q.P64 += c * p.sP64;
     q.P64b += c * p.sP64b; q.R64 += c * p.sR64; q.part += c * p.spart; q.gpart += c * p.sgpart;
-    q.pw += c * p.spw; q.mx += c * p.smx;
+    q.pw += c * p.spw; q.mx += c * p.smx; q.t16 += c * p.st16;
     return q;
 }
 
@@ -127,6 +131,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.gpart = take(B * gpm);               // Gram partials (either chain)
     const double pw = (2.0 * r * kShiftPool + 2) * 8;
     q.pw = take(B * pw);                   // spectral-shift pool: two r x 32 fp64 buffers, trace, estimate
+    q.t16 = take(B * r * stream16_pitch(m > n ? m : n) * 2);   // transposed bf16 Q or P (plain bf16 products)
     q.nmx = ((m + 63) / 64) * ((n + 63) / 64);
     q.mx = take(B * q.nmx * 2 * 4);        // per block of M: max |M' - M| and max |M| (fp32)
     q.total = off;
@@ -137,6 +142,7 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.sgpart = (size_t)gpm;
     q.spw = (size_t)pw;
     q.smx = (size_t)(q.nmx * 2 * 4);
+    q.st16 = (size_t)(r * stream16_pitch(m > n ? m : n) * 2);
     *p = q;
     return true;
 }
@@ -177,6 +183,17 @@ struct MpiArgs {
 };
 // Enqueues 1 + (iters + 1) + 1 launches; returns a hipError_t value.
 int run_lambda_max(const MpiArgs& a, int64_t b, int iters, void* stream);
+
+// Plain bf16 products streaming B = M + G once (stream16.hip).  stream16_ok: the shapes and
+// alignments their vector loads need (n % 8 == 0 for the product, n % 4 == 0 for the
+// back-projection; M 16-byte and G 8- or 16-byte aligned).  stream16_product: P0 = (M + G) Q
+// (backproject false, small = Q) or R = (M + G)^T P (true, small = P) into C, for the matrices
+// with (st & mask) == val, using tbuf (>= b r stream16_pitch(rows) bf16) for the transposed
+// small operand; returns a hipError_t value.
+bool stream16_ok(int64_t n, const void* M, const void* G, int g_bf16, bool backproject);
+int stream16_product(const float* M, const void* G, int g_bf16, const float* small, uint16_t* tbuf, float* C,
+                     int64_t m, int64_t n, int64_t r, int64_t b, bool backproject, const int* st, int st_mask,
+                     int st_val, void* stream);
 
 // Element-wise optimizers (arguments already validated).  Return a hipError_t value.
 int run_adamw(void* p, const void* g, float* m, float* v, int64_t n, int64_t t, float lr, float b1, float b2,

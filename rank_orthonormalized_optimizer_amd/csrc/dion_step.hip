@@ -2140,6 +2140,9 @@ static int bq_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, co
     const Plan& p = *c.p;
     const int64_t m = p.m, n = p.n, r = p.r;
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        if (c.plain && stream16_ok(n, M, G, gsz == 2, false))   // bf16 weights: B streamed once
+            return stream16_product(M, G, gsz == 2, Q, (uint16_t*)(c.ws + p.t16), (float*)P, m, n, r, p.b, false,
+                                    c.st, mask, val, c.s);
         const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
         Prod6Args g{};
         g.a = Op6{M, G, n, (int)m, (int)n, va};               // A(i,k) = B[i][k]  (k contiguous)
@@ -2174,6 +2177,9 @@ static int btp_gemm(const ChainCtx& c, const float* M, const void* G, int gsz, c
     const Plan& p = *c.p;
     const int64_t m = p.m, n = p.n, r = p.r;
     if constexpr (sizeof(T) == 4 && DION_PROD6) {
+        if (c.plain && stream16_ok(n, M, G, gsz == 2, true))    // bf16 weights: B streamed once
+            return stream16_product(M, G, gsz == 2, (const float*)P, (uint16_t*)(c.ws + p.t16), (float*)R, m, n, r,
+                                    p.b, true, c.st, mask, val, c.s);
         const bool va = (n % 4 == 0) && aligned4(M, 4) && aligned4(G, gsz);
         Prod6Args g{};
         g.a = Op6{M, G, n, (int)n, (int)m, va};               // A(i,k) = B[k][i]  (i contiguous)

@@ -170,12 +170,13 @@ def test_sticky_hint_is_bitwise_neutral(cuda):
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("base,n", [(1, 1000), (3, 1000), (1, 998)])
+@pytest.mark.parametrize("base,n", [(1, 1000), (3, 1000), (1, 998), (3, 996)])
 def test_wide_update_tiles(cuda, base, n):
     """A stack large enough for the 128 x 64 weight-pass tiles (16 x 520 x n: both edges ragged,
     r = 72 padded to 96 in the split planes), fp32 and bf16 weights.  With n = 1000 the interior
     tiles take the vectorized epilogue and the edge tiles the element-wise one; n = 998 (rows
-    not 16-byte aligned) sends every tile to the element-wise epilogue."""
+    not 16-byte aligned) sends every tile to the element-wise epilogue.  bf16 weights with n = 996
+    (a multiple of 4, not of 8) take the one-part split product and the streaming back-projection."""
     wl = W.SMALL[base].with_groups(W.Group(16, 520, n, 72), name=f"wide-tiles-{base}-{n}", steps=2)
     check(run_teacher_forced(wl, cuda), tol_for(wl))
 
