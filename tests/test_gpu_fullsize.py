@@ -12,13 +12,17 @@ properties that hold at any size are checked on every matrix on the GPU in fp64
 Free-running errors (the first sampled matrix also stepped by the oracle from its own
 fp64 state, never reset to the GPU's) are printed beside the teacher-forced ones and
 not judged: the pages give no multi-step trajectory to pin them to.
+
+The inputs are drawn on the device by the workloads' device generators (the same recipes,
+tested against the host ones), so that only the sampled matrices travel to the host; the
+oracle reads exactly the bits the GPU read.
 """
 import numpy as np
 import pytest
 
 import workloads as W
 from oracle import dion_step
-from tests.harness import check_errs, compare_step, rel, to_numpy, to_torch, tol_for
+from tests.harness import check_errs, compare_step, rel, to_numpy, tol_for
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -29,17 +33,17 @@ def _run(wl, device, steps, samples):
     out = []
     for gi, g in enumerate(wl.groups):
         print(f"[fullsize] {wl.name} group {gi} {g}: inputs", flush=True)
-        X, M, Q = W.make_state(wl, gi)
+        Xd, Md, Qd = W.make_state_device(wl, gi, device)
         idx = sorted(set(i for i in samples(g.batch) if 0 <= i < g.batch))
         f0 = idx[0]
-        free = {"X": W.to_f64(X[f0], wl.x_dtype), "M": M[f0].astype(np.float64), "Q": Q[f0].astype(np.float64)}
-        Xd, Md, Qd = to_torch(X, device), to_torch(M, device), to_torch(Q, device)
-        del X, M, Q
+        free = {"X": W.to_f64(to_numpy(Xd[f0]), wl.x_dtype), "M": to_numpy(Md[f0]).astype(np.float64),
+                "Q": to_numpy(Qd[f0]).astype(np.float64)}
         flags = torch.zeros(g.batch, dtype=torch.int32, device=device)
         ws = dion.api.workspace_for(g.m, g.n, g.batch, g.rank, device)
         for t in range(1, steps + 1):
-            G = W.make_grad(wl, gi, t)
-            Gd = to_torch(G, device)
+            print(f"[fullsize] {wl.name} group {gi} step {t}: gradient", flush=True)
+            Gd = W.make_grad_device(wl, gi, t, device)
+            G = to_numpy(Gd[idx])                       # the sampled matrices, in idx order
             pre = {"X": to_numpy(Xd[idx]), "M": to_numpy(Md[idx]), "Q": to_numpy(Qd[idx])}
             Bpre = (Md.double() + Gd.double()) if g.rank == min(g.m, g.n) else None
             print(f"[fullsize] {wl.name} group {gi} step {t}: GPU step", flush=True)
@@ -62,11 +66,11 @@ def _run(wl, device, steps, samples):
             fl = to_numpy(flags)
             post = {"X": to_numpy(Xd[idx]), "M": to_numpy(Md[idx]), "Q": to_numpy(Qd[idx]), "P": to_numpy(P[idx])}
             print(f"[fullsize] {wl.name} group {gi} step {t}: oracle on matrices {idx}", flush=True)
-            errs = compare_step(wl, pre, post, G[idx], g.rank)
+            errs = compare_step(wl, pre, post, G, g.rank)
             # free-running: the oracle's own trajectory for matrix f0
-            fo = dion_step(free["X"], W.to_f64(G[f0], wl.g_dtype), free["M"], free["Q"], wl.mu, wl.lr, wl.eps)
-            free = {"X": fo["X"], "M": fo["M"], "Q": fo["Q"]}
             k0 = idx.index(f0)
+            fo = dion_step(free["X"], W.to_f64(G[k0], wl.g_dtype), free["M"], free["Q"], wl.mu, wl.lr, wl.eps)
+            free = {"X": fo["X"], "M": fo["M"], "Q": fo["Q"]}
             P0 = post["P"][k0].astype(np.float64)
             freerun = {"PQ": rel(P0 @ post["Q"][k0].astype(np.float64).T, fo["P"] @ fo["Q"].T),
                        "M": rel(post["M"][k0].astype(np.float64), fo["M"]),

@@ -303,7 +303,8 @@ def psd_stack(batch: int, r: int, seed: int, kind: str = "gram", decades: float 
 # 4096^2 Haar QRs per matrix and step on the host.  These draw the same distributions with torch
 # on the device (fp64, rounded once to the storage type, round-to-nearest-even), from a torch
 # generator seeded per (seed, workload, group, step, tag).  They are not the host streams above:
-# parity tests, which need identical bits on both sides, use the host generators.
+# the reduced-size parity tests draw on the host; the full-size ones draw here and copy the
+# sampled matrices back, so the oracle reads exactly the bits the GPU read.
 def _torch_gen(device, *key):
     import torch
     s = np.random.SeedSequence([0x5EED, *key]).generate_state(1, np.uint64)[0]
