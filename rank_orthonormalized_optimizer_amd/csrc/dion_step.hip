@@ -285,61 +285,85 @@ __device__ __forceinline__ T rsqrt_newton(T d) {
     }
 }
 
-// acc += A B over K (a multiple of 4) for one 16 x 16 block held by the calling wave, with
-// A(i,k) = a[i * ai + k * ak] and B(k,j) = b[k * bk + j * bj] in LDS.
+// acc += A B over K (a multiple of 16) for one 16 x 16 block held by the calling wave, with
+// A(i,k) = a[i * ai + k * ak] and B(k,j) = b[k * bk + j * bj] in LDS; the operands of four
+// k-steps are read before their four products.
 template <typename T>
 __device__ __forceinline__ void blk_mma(const T* a, int ai, int ak, const T* b, int bk, int bj, int K,
                                         typename Mfma<T>::acc_t& acc, int lane) {
     const int r = lane & 15, kk = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4) acc = Mfma<T>::mma(a[r * ai + (k0 + kk) * ak], b[(k0 + kk) * bk + r * bj], acc);
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        T av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            av[u] = a[r * ai + (k0 + 4 * u + kk) * ak];
+            bv[u] = b[(k0 + 4 * u + kk) * bk + r * bj];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = Mfma<T>::mma(av[u], bv[u], acc);
+    }
 }
 
-// One column K of the panel sweep (lane = row of the panel).  d, r: this column's pivot and
-// 1 / sqrt(pivot); returns the next column's through the recursion.
-template <typename T, int K>
-struct PanelCol {
-    static __device__ __forceinline__ void run(T (&a)[kSB], T d, T r, int lane, T* col, T (&dgv)[kSB],
-                                               T (&rdv)[kSB], bool& bad) {
-        if constexpr (K < kSB) {
-            bad |= !(d > T(0)) || !(d < T(INFINITY));
-            const T lkk = d * r;
-            const T l = lane > K ? a[K] * r : (lane == K ? lkk : T(0));
-            a[K] = l;
-            dgv[K] = lkk;
-            rdv[K] = r;
-            T dn = T(1), rn = T(1), ln = T(0);
-            if constexpr (K + 1 < kSB) {   // next pivot from lane K + 1 alone
-                ln = read_lane<T>(l, K + 1);
-                const T an = read_lane<T>(a[K + 1], K + 1);
-                dn = __builtin_fma(-ln, ln, an);
-                rn = rsqrt_newton<T>(dn);
-            }
-            T* c = col + (K & 1) * 64;
-            c[lane] = l;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // column K + 1, which the next step scales, takes lane K + 1's value from the
-            // v_readlane above rather than from LDS, so no LDS round trip is on the pivot chain
-            if constexpr (K + 1 < kSB) a[K + 1] = __builtin_fma(-l, ln, a[K + 1]);
-#pragma unroll
-            for (int j = K + 2; j < kSB; ++j) a[j] = __builtin_fma(-l, c[j], a[j]);
-            PanelCol<T, K + 1>::run(a, dn, rn, lane, col, dgv, rdv, bad);
-        }
-    }
-};
-
-// Sweep of panel p by one wave: columns 16 p .. 16 p + 15, rows 16 p .. 63.  False on a bad pivot.
+// Sweep of panel p by one wave: columns 16 p .. 16 p + 15, rows 16 p .. 63 (lane = row of the
+// panel, its 16 values in registers).  False on a bad pivot.  Column K scales its column by the
+// pivot's reciprocal square root and subtracts l_iK l_jK from the later columns j.  The pivot
+// chain never waits for LDS: each lane also keeps its own diagonal element a_ll in a register
+// (the same updates, l_lK^2, in the same order), so the next pivot is one v_readlane of it; the
+// two following columns take this column's multipliers l_jK by v_readlane as well, and only the
+// columns from K + 3 on take them from an LDS broadcast, whose reads are consumed one column
+// later, behind the next pivot's reciprocal square root.  Every element receives the same fused
+// multiply-adds in the same order as in a plain column-by-column sweep.
 template <typename T>
 __device__ bool panel_sweep(DiagSmem<T>& sm, int p, int lane) {
     const int o = kSB * p, R = o + lane;
     const bool valid = R < kNB;
-    T a[kSB], dgv[kSB], rdv[kSB];
+    T a[kSB], dgv[kSB], rdv[kSB], pc[kSB];
 #pragma unroll
-    for (int j = 0; j < kSB; ++j) a[j] = valid ? sm.a[R * kDLD + o + j] : T(0);
-    const T d0 = read_lane<T>(a[0], 0);
+    for (int j = 0; j < kSB; ++j) {
+        a[j] = valid ? sm.a[R * kDLD + o + j] : T(0);
+        pc[j] = T(0);
+    }
+    T dg = T(0);   // a_ll of this lane's row l = lane (lanes < 16)
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) dg = (lane == j) ? a[j] : dg;
+    T d = read_lane<T>(dg, 0), r = rsqrt_newton<T>(d), pl = T(0);
     bool bad = false;
-    PanelCol<T, 0>::run(a, d0, rsqrt_newton<T>(d0), lane, &sm.col[0][0], dgv, rdv, bad);
+#pragma unroll
+    for (int K = 0; K < kSB; ++K) {
+        bad |= !(d > T(0)) || !(d < T(INFINITY));
+        const T lkk = d * r;
+        const T l = lane > K ? a[K] * r : (lane == K ? lkk : T(0));
+        a[K] = l;
+        dgv[K] = lkk;
+        rdv[K] = r;
+        // next pivot: a_(K+1)(K+1) - l_(K+1)K^2 from lane K + 1's register alone, and the next
+        // column's values, which take this column's multipliers by v_readlane
+        dg = __builtin_fma(-l, l, dg);
+        T dn = T(1), rn = T(1);
+        if (K + 1 < kSB) {
+            dn = read_lane<T>(dg, K + 1);
+            a[K + 1] = __builtin_fma(-l, read_lane<T>(l, K + 1), a[K + 1]);
+            rn = rsqrt_newton<T>(dn);
+        }
+        // the pivot chain above is issued before anything that waits for LDS
+        __builtin_amdgcn_sched_barrier(0);
+        // the previous column's LDS multipliers, read one column ago (columns j >= K + 2)
+#pragma unroll
+        for (int j = K + 2; j < kSB; ++j) a[j] = __builtin_fma(-pl, pc[j], a[j]);
+        if (K + 2 < kSB) a[K + 2] = __builtin_fma(-l, read_lane<T>(l, K + 2), a[K + 2]);
+        if (K + 3 < kSB) {
+            T* c = &sm.col[K & 1][0];
+            c[lane] = l;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int j = K + 3; j < kSB; ++j) pc[j] = c[j];
+        }
+        pl = l;
+        d = dn;
+        r = rn;
+    }
     if (bad) return false;
     if (valid) {
 #pragma unroll
@@ -471,17 +495,21 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         if (tid == 0) p.st[bz] |= p.fail_bit;
         return false;
     }
-    if (tid == 0) {
-        double mn = (double)sm.dg[0], mx = (double)sm.dg[0];
-        for (int q = 1; q < nbj; ++q) {
-            const double d = (double)sm.dg[q];
-            mn = d < mn ? d : mn;
-            mx = d > mx ? d : mx;
+    if (tid < 64) {   // min and max of diag(L) over the block: a wave reduction
+        const double d0 = (double)sm.dg[0];
+        double mn = tid < nbj ? (double)sm.dg[tid] : d0, mx = mn;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double on = __shfl_xor(mn, off), ox = __shfl_xor(mx, off);
+            mn = on < mn ? on : mn;
+            mx = ox > mx ? ox : mx;
         }
-        double* kp = p.kap + 2 * bz;
-        if (!p.first) { mn = kp[0] < mn ? kp[0] : mn; mx = kp[1] > mx ? kp[1] : mx; }
-        kp[0] = mn; kp[1] = mx;
-        if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
+        if (tid == 0) {
+            double* kp = p.kap + 2 * bz;
+            if (!p.first) { mn = kp[0] < mn ? kp[0] : mn; mx = kp[1] > mx ? kp[1] : mx; }
+            kp[0] = mn; kp[1] = mx;
+            if (p.last && p.tau > 0.0 && mx > p.tau * mn) p.st[bz] |= p.tau_bit;
+        }
     }
     T* Td = (T*)p.Td + bz * p.sTd + (int64_t)p.jblk * p.blkTd;
 #pragma unroll
@@ -1278,23 +1306,26 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = 
     return 0;
 }
 
-// arguments of panel_inv_kernel (defined with the tile device GEMM below)
-struct PanelInvArgs {
-    const void* S; void* L; void* Tf;
-    void* Y;            // scratch, [b][nblk][64][64]: the partial products of the inverse tiles
+// arguments of chol_step_kernel (defined with the tile device GEMM below)
+struct CholStepArgs {
+    const void* S;       // source of the panel and trailing blocks at this step
+    void* L; void* Tf;
     int64_t r;
-    int jb, nblk;
-    const int* st;
-    int st_mask, st_val;
+    int nblk, jb;
+    const int* st; int st_mask, st_val;
+    PotrfArgs diag;      // the next diagonal block (task 0), base pointers
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void panel_inv_kernel(PanelInvArgs a);
+__global__ __launch_bounds__(256) void chol_step_kernel(CholStepArgs a);
 
 // Blocked right-looking Cholesky L = chol(W (+ s I)).  With `with_inverse` (ranks up to
-// kFusedMaxBlocks blocks) the panel launches also build Tf = L^-1 (panel_inv_kernel); a matrix
-// that tau_bit marks at the last diagonal block skips the last inverse tiles (a later shifted
-// call refactors it).
+// kFusedMaxBlocks blocks) Tf = L^-1 is built alongside, in nblk + 1 launches: the first diagonal
+// block, then one chol_step_kernel launch per block step (trailing tiles with their panel blocks,
+// the next diagonal block, the inverse tiles of the step's block row) and one for the last
+// block row of the inverse.  A matrix that tau_bit marks at the last diagonal block skips the
+// last inverse tiles (a later shifted call refactors it).  Without the inverse: a diagonal,
+// panel and trailing launch per block.
 template <typename T>
 static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit, int tau_bit, int shift,
                   bool with_inverse) {
@@ -1317,6 +1348,32 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
                            c.lam, c.lam_stride);
         DION_TRY(hipGetLastError());
     }
+    auto diag_args = [&](int64_t jb) {
+        PotrfArgs pa{};
+        pa.L = L; pa.ldl = r; pa.sL = r * r; pa.S = (jb == 0 && !shift) ? W : L;
+        // the inverted diagonal blocks go straight into the diagonal of Tf = L^-1
+        pa.Td = Tf; pa.sTd = r * r; pa.ldTd = r; pa.blkTd = kNB * (r + 1); pa.tdfull = 0;
+        pa.j0 = (int)(jb * kNB); pa.nbj = (int)((r - jb * kNB) < kNB ? (r - jb * kNB) : kNB); pa.jblk = (int)jb;
+        pa.st = c.st; pa.st_mask = mask; pa.st_val = val;
+        pa.kap = kap; pa.first = jb == 0; pa.last = jb == p.nblk - 1;
+        pa.tau = tau; pa.fail_bit = fail_bit; pa.tau_bit = tau_bit;
+        return pa;
+    };
+    if (with_inverse) {
+        hipLaunchKernelGGL((potrf_diag_kernel<T>), dim3((unsigned)b), dim3(256), 0, c.s, diag_args(0));
+        DION_TRY(hipGetLastError());
+        for (int64_t jb = 0; jb < p.nblk && p.nblk > 1; ++jb) {
+            const int64_t n = p.nblk - 1 - jb, tasks = n * (n + 1) / 2 + jb;
+            CholStepArgs sa{};
+            sa.S = (jb == 0 && !shift) ? W : L; sa.L = L; sa.Tf = Tf;
+            sa.r = r; sa.nblk = (int)p.nblk; sa.jb = (int)jb;
+            sa.st = c.st; sa.st_mask = jb == p.nblk - 1 ? (mask | tau_bit) : mask; sa.st_val = val;
+            if (n > 0) { sa.diag = diag_args(jb + 1); sa.diag.S = L; }
+            hipLaunchKernelGGL((chol_step_kernel<T>), dim3((unsigned)tasks, (unsigned)b), dim3(256), 0, c.s, sa);
+            DION_TRY(hipGetLastError());
+        }
+        return 0;
+    }
     for (int64_t jb = 0; jb < p.nblk; ++jb) {
         const int j0 = (int)(jb * kNB);
         const int nbj = (int)((r - j0) < kNB ? (r - j0) : kNB);
@@ -1332,15 +1389,6 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
         pa.tau = tau; pa.fail_bit = fail_bit; pa.tau_bit = tau_bit;
         hipLaunchKernelGGL((potrf_diag_kernel<T>), dim3((unsigned)b), dim3(256), 0, c.s, pa);
         DION_TRY(hipGetLastError());
-        if (with_inverse && p.nblk > 1) {
-            PanelInvArgs pi{};
-            pi.S = src; pi.L = L; pi.Tf = Tf; pi.Y = c.ws + p.Td;
-            pi.r = r; pi.jb = (int)jb; pi.nblk = (int)p.nblk;
-            pi.st = c.st; pi.st_mask = jb == p.nblk - 1 ? (mask | tau_bit) : mask; pi.st_val = val;
-            hipLaunchKernelGGL((panel_inv_kernel<T>), dim3((unsigned)(p.nblk - 1), (unsigned)b), dim3(256), 0, c.s,
-                               pi);
-            DION_TRY(hipGetLastError());
-        }
         if (rest > 0) {
             const int64_t ob = (int64_t)(j0 + nbj) * r + j0, ot = (int64_t)(j0 + nbj) * (r + 1);
             T* below = L + ob;
@@ -1354,7 +1402,7 @@ static int factor(const ChainCtx& c, int mask, int val, double tau, int fail_bit
             g.M = rest; g.N = nbj; g.K = nbj;
             g.alpha = 1; g.beta = 0;
             g.st = c.st; g.st_mask = mask; g.st_val = val;
-            if (!with_inverse) DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
+            DION_TRY((launch_gemm<T, 64, 64, true, S, true, S>(g, b, c.s)));
             // trailing: L22 <- L22 - L21 L21^T (lower tiles only)
             GemmArgs h = g;
             h.a = Operand{below, nullptr, r, rest, nbj, vr};
@@ -1494,12 +1542,13 @@ struct CholInvArgs {
     double ntau;
 };
 
-// C (M x N <= 64 x 64, ldc) = alpha A B + beta C with A(i,k) k-contiguous and B either
-// k-contiguous (BKC) or row-contiguous; all loads of C happen before its stores, and the
-// workgroup synchronizes at the end (C is read back by the next tile).
-template <typename T, bool BKC>
+// C (M x N <= 64 x 64, ldc) = alpha A B + beta C0 with A(i,k) k-contiguous (AKC) or
+// row-contiguous, B k-contiguous (BKC) or row-contiguous, and C0 read from Csrc (same layout as
+// C) when given, else from C.  All loads of C0 happen before the stores of C, and the workgroup
+// synchronizes at the end (C is read back by the next tile).  Operands and C may sit in LDS.
+template <typename T, bool BKC, bool AKC = true>
 __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int K, T* Cp, int64_t ldc, T alpha,
-                          T beta, T* As, T* Bs) {
+                          T beta, T* As, T* Bs, const T* Csrc = nullptr) {
     using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
     constexpr int S = SrcOf<T>::v;
     typename C::acc_t acc[C::FM][C::FN];
@@ -1507,7 +1556,8 @@ __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int 
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{0, 0, 0, 0};
-    mainloop<T, C, true, S, BKC, S>(A, B, 0, 0, 0, K, As, Bs, acc);
+    mainloop<T, C, AKC, S, BKC, S>(A, B, 0, 0, 0, K, As, Bs, acc);
+    const T* C0 = Csrc ? Csrc : Cp;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
     T sv[C::FM][C::FN][4];
 #pragma unroll
@@ -1517,7 +1567,7 @@ __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = wm * C::WTM + i * 16 + Mfma<T>::row(lane, v), col = wn * C::WTN + j * 16 + (lane & 15);
-                sv[i][j][v] = (beta != T(0) && row < M && col < N) ? Cp[(int64_t)row * ldc + col] : T(0);
+                sv[i][j][v] = (beta != T(0) && row < M && col < N) ? C0[(int64_t)row * ldc + col] : T(0);
             }
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -1531,17 +1581,25 @@ __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int 
     __syncthreads();
 }
 
-// Off-diagonal tiles of step jb of the right-looking factorization, with L^-1 built alongside
-// (ranks up to kFusedMaxBlocks blocks; grid: nblk - 1 tiles x matrices):
-//   below the diagonal block (ib > jb):  L_ib,jb = S_ib,jb Td_jb^T   (S: the updated block)
-//   left of it in L^-1 (kb < jb):        X_jb,kb = -Td_jb (sum_{kb<=q<jb} L_jb,q X_q,kb)
-// The inverse tiles need only blocks finished at earlier steps, so they ride along with the
-// panel; the last step is a launch of inverse tiles only.  No separate inversion launches.
+// Step jb of the right-looking factorization with L^-1 built alongside, in one launch (grid:
+// tasks x matrices), for ranks up to kFusedMaxBlocks blocks.  Tasks 0 .. ntr - 1 are the trailing
+// tiles (i, k), jb < k <= i, column by column; each computes the panel blocks it needs itself,
+//   L_i,jb = S_i,jb Td_jb^T,   L_k,jb = S_k,jb Td_jb^T   (S: W at the first unshifted step, else L)
+//   L_ik   = S_ik - L_i,jb L_k,jb^T,
+// so the panel needs no launch of its own.  The tiles of column jb + 1 keep L_i,jb, transposed,
+// in the upper block (jb, i) of L, which the factorization leaves unused (writing it in place
+// would race with the other tiles still reading S_i,jb).  Task 0, tile (jb + 1, jb + 1), then
+// factors and inverts that diagonal block (as potrf_diag_kernel does).  The last jb tasks are the
+// inverse tiles of block row jb,
+//   X_jb,kb = -Td_jb (sum_{kb <= q < jb} L_jb,q X_q,kb),   kb < jb,
+// which read L_jb,q from the upper blocks (q, jb) kept by earlier steps.  The step after the last
+// diagonal block (jb = nblk - 1) has inverse tiles only.
 template <typename T>
-__global__ __launch_bounds__(256) void panel_inv_kernel(PanelInvArgs a) {
+__global__ __launch_bounds__(256) void chol_step_kernel(CholStepArgs a) {
     const int bz = blockIdx.y, t = blockIdx.x;
     if ((a.st[bz] & a.st_mask) != a.st_val) return;
     using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
+    __shared__ DiagSmem<T> sm;
     __shared__ T As[2 * C::A_STAGE];
     __shared__ T Bs[2 * C::B_STAGE];
     const int64_t r = a.r, rr = r * r;
@@ -1550,24 +1608,41 @@ __global__ __launch_bounds__(256) void panel_inv_kernel(PanelInvArgs a) {
     T* Tf = (T*)a.Tf + bz * rr;
     const bool vr = (r % 4) == 0;
     auto nb = [&](int q) { return (int)((r - (int64_t)q * kNB) < kNB ? (r - (int64_t)q * kNB) : kNB); };
-    const int jb = a.jb, j0 = jb * kNB, nbj = nb(jb), nL = a.nblk - 1 - jb;
+    const int jb = a.jb, j0 = jb * kNB, nbj = nb(jb), n = a.nblk - 1 - jb, ntr = n * (n + 1) / 2;
     const Operand Td{Tf + (int64_t)j0 * (r + 1), nullptr, r, nbj, nbj, vr};   // Td(i,k) = X_jb,jb[i][k]
-    if (t < nL) {
-        // one tile holds all nbj columns, so in place (S == L once shifted) is safe
-        const int64_t i0 = (int64_t)(jb + 1 + t) * kNB;
-        const int nbi = nb(jb + 1 + t);
-        tile_gemm<T, true>(Operand{S + i0 * r + j0, nullptr, r, nbi, nbj, vr}, Td, nbi, nbj, nbj, L + i0 * r + j0, r,
-                           T(1), T(0), As, Bs);
-    } else {
-        const int kb = t - nL, k0 = kb * kNB, nbk = nb(kb), K = j0 - k0;
-        T* Y = (T*)a.Y + ((int64_t)bz * a.nblk + kb) * kNB * kNB;
-        // Y = L_jb,[kb,jb) X_[kb,jb),kb  (nbj x nbk, ld 64); X_jb,kb = -Td Y
-        const Operand A{L + (int64_t)j0 * r + k0, nullptr, r, nbj, K, vr};
-        const Operand B{Tf + (int64_t)k0 * r + k0, nullptr, r, nbk, K, vr};
-        tile_gemm<T, false>(A, B, nbj, nbk, K, Y, kNB, T(1), T(0), As, Bs);
-        const Operand B2{Y, nullptr, kNB, nbk, nbj, true};
-        tile_gemm<T, false>(Td, B2, nbj, nbk, nbj, Tf + (int64_t)j0 * r + k0, r, T(-1), T(0), As, Bs);
+    if (t < ntr) {
+        int k = jb + 1, rem = t;
+        while (rem >= a.nblk - k) { rem -= a.nblk - k; ++k; }
+        const int i = k + rem;
+        const int64_t i0 = (int64_t)i * kNB, k0 = (int64_t)k * kNB;
+        const int nbi = nb(i), nbk = nb(k);
+        tile_gemm<T, true>(Operand{S + i0 * r + j0, nullptr, r, nbi, nbj, vr}, Td, nbi, nbj, nbj, sm.a, kDLD, T(1),
+                           T(0), As, Bs);
+        const T* Lk = sm.a;
+        if (k != i) {
+            tile_gemm<T, true>(Operand{S + k0 * r + j0, nullptr, r, nbk, nbj, vr}, Td, nbk, nbj, nbj, sm.x, kDLD,
+                               T(1), T(0), As, Bs);
+            Lk = sm.x;
+        }
+        if (k == jb + 1)
+            for (int idx = threadIdx.x; idx < nbj * nbi; idx += 256) {
+                const int u = idx / nbi, v = idx % nbi;
+                L[(int64_t)(j0 + u) * r + i0 + v] = sm.a[v * kDLD + u];
+            }
+        tile_gemm<T, true>(Operand{sm.a, nullptr, kDLD, nbi, nbj, false}, Operand{Lk, nullptr, kDLD, nbk, nbj, false},
+                           nbi, nbk, nbj, L + i0 * r + k0, r, T(-1), T(1), As, Bs, S + i0 * r + k0);
+        if (t == 0) {
+            diag_block<T>(a.diag, bz, sm);   // the updated block, read back from L
+        }
+        return;
     }
+    const int kb = t - ntr, k0 = kb * kNB, nbk = nb(kb), K = j0 - k0;
+    // Y = sum_q L_jb,q X_q,kb in LDS: A(i, k) = L_jb,(k0 + k) = L[(k0 + k) r + j0 + i] (upper blocks)
+    tile_gemm<T, false, false>(Operand{L + (int64_t)k0 * r + j0, nullptr, r, nbj, K, vr},
+                               Operand{Tf + (int64_t)k0 * r + k0, nullptr, r, nbk, K, vr}, nbj, nbk, K, sm.a, kDLD,
+                               T(1), T(0), As, Bs);
+    tile_gemm<T, false>(Td, Operand{sm.a, nullptr, kDLD, nbk, nbj, false}, nbj, nbk, nbj, Tf + (int64_t)j0 * r + k0,
+                        r, T(-1), T(0), As, Bs);
 }
 
 template <typename T>
@@ -1731,7 +1806,7 @@ static int factor_invert(const ChainCtx& c, int mask, int val, double tau, int f
     const Plan& p = *c.p;
     if (!rare || p.nblk > kFusedMaxBlocks) {
         int e;
-        const bool inv = p.nblk <= kFusedMaxBlocks;   // L^-1 built by the panel launches
+        const bool inv = p.nblk <= kFusedMaxBlocks;   // L^-1 built alongside the factorization
         if ((e = factor<T>(c, mask, val, tau, fail_bit, tau_bit, shift, inv))) return e;
         if (inv) return 0;
         // a matrix marked by tau_bit here is refactored (shifted) by a later call, which inverts
