@@ -43,15 +43,20 @@
  *   state buffers must not overlap each other or the workspace.
  *
  * Arithmetic
- *   fp32 weights (x_dtype DION_F32): every product is fp32-accurate.  The rank-r contractions
- *   run on the bf16 matrix cores with each fp32 operand split exactly into three bf16 parts
- *   (six part products kept, fp32 accumulation); ill-conditioned matrices take an fp64 chain
- *   (P0, the QR and R in fp64).
+ *   fp32 weights (x_dtype DION_F32): P0 = B Q, the orthonormalization and R = B^T P are
+ *   fp32-accurate: the contractions run on the bf16 matrix cores with each fp32 operand split
+ *   exactly into three bf16 parts (six part products kept, fp32 accumulation), and
+ *   ill-conditioned matrices take an fp64 chain (P0, the QR and R in fp64).  The weight pass's
+ *   two rank-r products P R^T and P Q'^T, whose operands are final (no conditioning amplifies
+ *   their error), split each operand into two bf16 parts (hi + lo, 16 significant bits) and
+ *   keep the three part products hi hi, hi lo, lo hi: relative error at most about 3 * 2^-16
+ *   per term, fp32 accumulation.
  *   bf16 weights (x_dtype DION_BF16): the three big contractions (P0 = B Q, R = B^T P and the
  *   rank-r products of the weight pass) are plain bf16 products: operands rounded once to bf16,
  *   fp32 accumulation (relative error about 2^-8), the precision bf16 weights carry.  The
  *   orthonormalization keeps the fp32-accurate arithmetic, so P^T P = I to fp32 accuracy.
- *   DION_OPT_EXACT_PRODUCTS gives bf16 weights the fp32-accurate products too.
+ *   DION_OPT_EXACT_PRODUCTS makes every product fp32-accurate: the six-product split for the
+ *   weight pass of fp32 weights and for the three big contractions of bf16 weights.
  *
  * Execution
  *   Asynchronous: the call returns without a host synchronization.  The stack
@@ -122,8 +127,9 @@ enum {
                                  exceeds it by up to the rank.  Adds 13 launches to the fp64
                                  chain, which return at once for the matrices not shifted; not
                                  with DION_OPT_FORCE_F32 */
-    DION_OPT_EXACT_PRODUCTS = 64, /* bf16 weights: keep the fp32-accurate products (see Arithmetic)
-                                 instead of plain bf16 ones */
+    DION_OPT_EXACT_PRODUCTS = 64, /* fp32-accurate products everywhere (see Arithmetic): the
+                                 six-product split in the weight pass of fp32 weights, and in
+                                 place of plain bf16 products for bf16 weights */
     DION_OPT_CHUNKS_SHIFT = 8 /* bits 8..11: number of concurrent chunks the stack is split into
                                  (0 = automatic, 1 = everything on `stream`); see Execution */
 };

@@ -815,14 +815,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void update_kernel(UpdArgs u) {
                 b[j][q] = *(const u32x4*)&ldsB[buf][q][bo[j]];
                 c[j][q] = *(const u32x4*)&ldsB[buf][NP + q][bo[j]];
             }
-        constexpr int NTERM = NP == 1 ? 1 : 6;   // plain bf16: the single h h product
+        // the part products smallest first: six for three parts, the last three of them for two
+        // parts (hl, lh, hh), the single hh product for plain bf16
+        constexpr int NTERM = NP == 1 ? 1 : NP == 2 ? 3 : 6;
 #pragma unroll
         for (int term = 0; term < NTERM; ++term)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int ta = NP == 1 ? 0 : kTermA[term], tb = NP == 1 ? 0 : kTermB[term];
+                    const int ta = NP == 1 ? 0 : kTermA[6 - NTERM + term];
+                    const int tb = NP == 1 ? 0 : kTermB[6 - NTERM + term];
                     acc1[i][j] = mma_bf16(a[i][ta], b[j][tb], acc1[i][j]);
                     acc2[i][j] = mma_bf16(a[i][ta], c[j][tb], acc2[i][j]);
                 }
@@ -2496,12 +2499,17 @@ static int run_chunk(const Plan& p, void* X, const void* G, float* M, float* Q, 
     DION_TRY(mark(DION_PHASE_UPDATE));
     hipError_t he;
     int nparts = 0;
+    // the weight pass's products: plain bf16 for bf16 weights, two-part split (three part
+    // products) for fp32 weights, the fp32-accurate three-part split (six) on request
+    const bool exact = options & DION_OPT_EXACT_PRODUCTS;
     if (c.plain) he = g_bf16 ? launch_update<true, true, 1>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
                              : launch_update<false, true, 1>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
-    else if (g_bf16) he = x_bf16 ? launch_update<true, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
-                                 : launch_update<true, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
-    else he = x_bf16 ? launch_update<false, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
-                     : launch_update<false, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
+    else if (x_bf16) he = g_bf16 ? launch_update<true, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                                 : launch_update<false, true, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
+    else if (exact) he = g_bf16 ? launch_update<true, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                                : launch_update<false, false, 3>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
+    else he = g_bf16 ? launch_update<true, false, 2>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts)
+                     : launch_update<false, false, 2>(p, ws, Q, M, G, X, mu, lr, s, mx, &nparts);
     DION_TRY(he);
     if (rmmc) {
         hipLaunchKernelGGL(rmmc_kernel, dim3((unsigned)p.b), dim3(256), 0, s, (const float*)mx, p.nmx, nparts, rmmc);

@@ -39,11 +39,16 @@ def update_gamma(rank: int, arith: str = "split6") -> float:
     split6: fp32 operands split exactly into three bf16 parts, six of the nine part
     products kept (the three dropped ones are below 2^-24 |a||b| each: at most 2.1 u),
     exact bf16 x bf16 products accumulated in fp32 (at most 6 r additions, 6 r u), plus
-    the fp32 rounding of lr s (u).  bf16: both operands rounded once to bf16 (2 * 2^-8),
-    accumulated in fp32 (r u), plus lr s (u).  u = 2^-24."""
+    the fp32 rounding of lr s (u).  split3: each operand split into two bf16 parts, a = h + l + e
+    with |l| <= 2^-8 (1 + 2^-8) |a| and |e| <= 2^-16 |a|; the kept products h h, h l, l h drop
+    l l and the e terms, together below 3.01 * 2^-16 |a||b|, then 3 r fp32 additions and lr s.
+    bf16: both operands rounded once to bf16 (2 * 2^-8), accumulated in fp32 (r u), plus lr s
+    (u).  u = 2^-24."""
     u = 2.0 ** -24
     if arith == "split6":
         return (6 * rank + 4) * u
+    if arith == "split3":
+        return 3.01 * 2.0 ** -16 + (3 * rank + 2) * u
     if arith == "bf16":
         return 2.0 * 2.0 ** -8 + 2.0 ** -16 + (rank + 2) * u
     raise ValueError(arith)
@@ -92,17 +97,19 @@ def xband_violations(X0: np.ndarray, Xg: np.ndarray, P: np.ndarray, Qn: np.ndarr
 
 
 def arith_for(wl, options: int = 0) -> str:
-    """The weight pass's arithmetic: plain bf16 products for bf16 weights (unless the exact-products
-    option asks for the fp32-accurate split), the exact split otherwise."""
+    """The weight pass's arithmetic: with the exact-products option the fp32-accurate six-product
+    split; otherwise plain bf16 products for bf16 weights, the two-part split for fp32 ones."""
     from rank_orthonormalized_optimizer_amd._lib import OPT_EXACT_PRODUCTS
-    return "bf16" if wl.x_dtype == "bf16" and not (options & OPT_EXACT_PRODUCTS) else "split6"
+    if options & OPT_EXACT_PRODUCTS:
+        return "split6"
+    return "bf16" if wl.x_dtype == "bf16" else "split3"
 
 
 def compare_step(wl, pre, post, G, rank, idx=None, arith: str | None = None):
     """Per-matrix errors of one GPU step against the oracle started from `pre`.
 
     pre/post: dicts of host arrays X, M, Q (+ post P).  ``arith``: the weight pass's arithmetic
-    ("split6" or "bf16"; default from the workload's weight dtype).  Returns a list of dicts.
+    ("split6", "split3" or "bf16"; default: arith_for(wl)).  Returns a list of dicts.
     """
     if arith is None:
         arith = arith_for(wl)

@@ -18,6 +18,20 @@ def _rb(a):
     return W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.asarray(a, np.float32)))
 
 
+def _split2(a):
+    """hi + lo of fp32 values: hi = RNE_bf16(a), lo = RNE_bf16(a - hi), as fp64."""
+    a = np.asarray(a, np.float32)
+    hi = _rb(a)
+    return hi.astype(np.float64), _rb(a - hi).astype(np.float64)
+
+
+def _prod3(a, b):
+    """a b^T from two-part operands, the hi hi, hi lo and lo hi products only (then fp32)."""
+    ah, al = _split2(a)
+    bh, bl = _split2(b)
+    return (ah @ bh.T + ah @ bl.T + al @ bh.T).astype(np.float32)
+
+
 def _emulated_step(wl, gi, mistake=None, arith="split6"):
     g = wl.groups[gi]
     X, M, Q = W.make_state(wl, gi)
@@ -38,13 +52,14 @@ def _emulated_step(wl, gi, mistake=None, arith="split6"):
                       Q[i].astype(np.float64), wl.mu, wl.lr, wl.eps)
         P32, R32, Q32 = o["P"].astype(np.float32), o["R"].astype(np.float32), o["Q"].astype(np.float32)
         B32 = M[i] + W.to_f64(G[i], wl.g_dtype).astype(np.float32)
-        upd_m = op(P32) @ op(R32).T
+        prod = _prod3 if arith == "split3" else (lambda a, b: op(a) @ op(b).T)
+        upd_m = prod(P32, R32)
         if mistake == "no_feedback":
             upd_m = np.zeros_like(upd_m)
         post["M"][i] = B32 - omm * upd_m
-        upd_x = op(P32) @ op(Q32).T
+        upd_x = prod(P32, Q32)
         if mistake == "q_rows_reversed":     # a wrong row index into Q'
-            upd_x = op(P32) @ op(Q32)[::-1].T
+            upd_x = prod(P32, Q32[::-1])
         x = W.to_f64(X[i], wl.x_dtype).astype(np.float32) - lr_s * upd_x
         if mistake == "no_update":
             x = W.to_f64(X[i], wl.x_dtype).astype(np.float32)
@@ -67,7 +82,7 @@ def _fails(errs, tol):
 CASES = {"f32": W.SMALL[1], "bf16": W.SMALL[3]}
 
 
-@pytest.mark.parametrize("case,arith", [("f32", "split6"), ("bf16", "split6"), ("bf16", "bf16")])
+@pytest.mark.parametrize("case,arith", [("f32", "split6"), ("f32", "split3"), ("bf16", "split6"), ("bf16", "bf16")])
 def test_correct_emulation_passes(case, arith):
     wl = CASES[case]
     errs = _emulated_step(wl, 0, arith=arith)
@@ -83,6 +98,13 @@ def test_correct_emulation_passes(case, arith):
 def test_planted_update_mistake_is_caught(case, mistake):
     wl = CASES[case]
     assert _fails(_emulated_step(wl, 0, mistake), tol_for(wl)), mistake
+
+
+@pytest.mark.parametrize("mistake", ["no_update", "scale", "mu", "q_rows_reversed", "no_feedback"])
+def test_planted_mistake_is_caught_with_two_part_products(mistake):
+    """The two-part split of fp32 weights widens the band to about 3 * 2^-16 of |P| |Q'|^T."""
+    wl = CASES["f32"]
+    assert _fails(_emulated_step(wl, 0, mistake, arith="split3"), tol_for(wl)), mistake
 
 
 @pytest.mark.parametrize("mistake", ["no_update", "scale30", "q_rows_reversed", "no_feedback"])
