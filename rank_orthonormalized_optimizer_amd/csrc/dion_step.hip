@@ -1065,8 +1065,7 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                                             xv[q].w - c * av[q].w};
                     if constexpr (X_BF16)
                         nt_st2((uint16_t*)u.X + off,
-                            uint2{(uint32_t)float_to_bf16_bits(x.x) | ((uint32_t)float_to_bf16_bits(x.y) << 16),
-                                  (uint32_t)float_to_bf16_bits(x.z) | ((uint32_t)float_to_bf16_bits(x.w) << 16)});
+                            uint2{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)});
                     else nt_st4((float*)u.X + off, x);
                 }
             }

@@ -59,12 +59,15 @@ enum Src : int {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).
-__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Round-to-nearest-even float -> bfloat16 bits, by the hardware conversion (v_cvt_pk_bf16_f32;
+// a NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two values rounded to bfloat16 and packed, a in the low half: one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // Storage of an operand source: the raw element types read from p0 and p1.

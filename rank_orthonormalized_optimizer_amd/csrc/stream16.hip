@@ -23,10 +23,6 @@ namespace dion {
 
 constexpr int kStreamD = 4;   // slabs of global loads in flight per register set rotation
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
-}
-
 // out[bz][c][i] = bf16(in[bz][i][c]) for i < rows, c < cols, zero for rows <= i < pitch: the
 // transposed bf16 copy of an fp32 [rows][cols] array, its rows padded with zeros to `pitch` (a
 // multiple of 32, so that every 32-wide slab read stays inside its row).
@@ -208,10 +204,17 @@ constexpr int kP16KS = DION_P16_KS, kP16D = DION_P16_D;   // k-steps per super-s
 
 // R = (M + G)^T P.  Workgroup: 128 columns j of one matrix (rows of R) by output columns
 // [256 y, 256 y + 256); the contraction runs over the m rows of B in 32-row slabs.  Each thread
-// loads two consecutive rows by four columns of M and G (16- and 8-byte vectors), forms bf16 B and
-// writes it transposed into LDS ([j][i], 16-byte rows of eight i per MFMA fragment); P^T's slab
-// goes through LDS as in p16_kernel.  Waves 2 x 4, each 64 j by 64 output columns.
+// loads two consecutive rows (pair p) by four columns (group c) of M and G (16- and 8-byte
+// vectors), forms bf16 B and writes it transposed into LDS ([j][i], 16-byte chunks of eight i per
+// MFMA fragment); P^T's slab goes through LDS as in p16_kernel.  Waves 2 x 4, each 64 j by 64
+// output columns.  A wave stages four pairs by sixteen groups (16 lanes read 256 contiguous bytes
+// of a row of M), and the chunk of row j sits at chunk ^ ((j >> 4) & 3): the transposed 4-byte
+// writes of a wave then fall in 64 distinct banks, and a fragment read (16 consecutive rows, one
+// chunk) in distinct 16-byte slots.
 constexpr int kR16Pitch = 40;   // bf16 per LDS row of the transposed B slab (32 + 8: rows 16-byte aligned)
+__device__ __forceinline__ int r16_off(int j, int i) {   // bf16 offset of (j, i), i even
+    return j * kR16Pitch + 8 * (((i >> 3) ^ (j >> 4)) & 3) + (i & 7);
+}
 
 template <bool G_BF16>
 __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
@@ -222,8 +225,8 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
     const int64_t j0 = (int64_t)tid.x * 128, col0 = (int64_t)tid.y * kT16Rows;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, fr = lane & 15, fg = lane >> 4;
     const int wm = w >> 2, wn = w & 3;
-    // staging share of the B slab: rows 2 p, 2 p + 1 (p = t / 32), columns 4 c .. 4 c + 3 (c = t % 32)
-    const int p = t >> 5, c4 = 4 * (t & 31);
+    // staging share of the B slab: rows 2 p, 2 p + 1 and columns 4 c .. 4 c + 3 (see above)
+    const int p = 4 * (w & 3) + (lane >> 4), c4 = 4 * (16 * (w >> 2) + (lane & 15));
     const bool cok = j0 + c4 < a.n;          // n % 4 == 0: a group of four is all in or all out
     const int64_t mn = a.m * a.n;
     const int64_t cofs = bz * mn + (cok ? j0 + c4 : 0);
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
         const float r1[4] = {v1 ? m1.x + g1[0] : 0.f, v1 ? m1.y + g1[1] : 0.f, v1 ? m1.z + g1[2] : 0.f,
                              v1 ? m1.w + g1[3] : 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) *(uint32_t*)&l[(c4 + e) * kR16Pitch + 2 * p] = pack_bf16x2(r0[e], r1[e]);
+        for (int e = 0; e < 4; ++e) *(uint32_t*)&l[r16_off(c4 + e, 2 * p)] = pack_bf16x2(r0[e], r1[e]);
     };
     f32x4 acc[4][4];
 #pragma unroll
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
             __syncthreads();
             u32x4 af[4], bf[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *(const u32x4*)&ba[(wm * 64 + 16 * i + fr) * kR16Pitch + 8 * fg];
+            for (int i = 0; i < 4; ++i) af[i] = *(const u32x4*)&ba[r16_off(wm * 64 + 16 * i + fr, 8 * fg)];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = *(const u32x4*)&bb[part_off(wn * 64 + 16 * j + fr, fg)];
 #pragma unroll
