@@ -147,6 +147,27 @@ class DionStack:
         if self.hint is not None:
             self.hint.after_step(stream)
 
+    def state_dict(self) -> dict:
+        """The state a checkpoint needs, as CPU tensors: the momentum M, the right factor Q and
+        the per-matrix flags (their fp64 mark keeps a matrix on the fp64 chain), with the
+        sizes and hyper-parameters.  The workspace carries nothing from one step to the next, so
+        a stack restored with load_state_dict continues bitwise as if it had not stopped."""
+        return {"M": self.M.cpu(), "Q": self.Q.cpu(), "flags": self.flags.cpu(),
+                "shape": [self.batch, self.m, self.n], "rank": self.rank, "mu": self.mu, "lr": self.lr,
+                "eps": self.eps, "options": self.options}
+
+    def load_state_dict(self, sd: dict) -> None:
+        """Restore a state_dict() of a stack with the same sizes (copied into this stack's
+        device tensors; the host's fp64 hint starts over, which selects the same work)."""
+        if list(sd["shape"]) != [self.batch, self.m, self.n] or int(sd["rank"]) != self.rank:
+            raise ValueError(f"state of a {sd['shape']} r={sd['rank']} stack, this one is "
+                             f"{[self.batch, self.m, self.n]} r={self.rank}")
+        self.M.copy_(sd["M"])
+        self.Q.copy_(sd["Q"])
+        self.flags.copy_(sd["flags"])
+        self.mu, self.lr, self.eps, self.options = float(sd["mu"]), float(sd["lr"]), float(sd["eps"]), int(sd["options"])
+        self.hint = StickyF64Hint(self.flags) if self.options & _lib.OPT_STICKY_F64 else None
+
     @property
     def P(self) -> torch.Tensor:
         """This step's orthonormal factor P [b, m, r] (fp32), read from the workspace."""
