@@ -189,7 +189,7 @@ int run_lambda_max(const MpiArgs& a, int64_t b, int iters, void* stream);
 // back-projection; M 16-byte and G 8- or 16-byte aligned).  stream16_product: P0 = (M + G) Q
 // (backproject false, small = Q) or R = (M + G)^T P (true, small = P) into C, for the matrices
 // with (st & mask) == val, using tbuf (>= b r stream16_pitch(rows) bf16) for the transposed
-// small operand; returns a hipError_t value.
+// small operand, stored in contiguous 32-row slabs; returns a hipError_t value.
 bool stream16_ok(int64_t n, const void* M, const void* G, int g_bf16, bool backproject);
 int stream16_product(const float* M, const void* G, int g_bf16, const float* small, uint16_t* tbuf, float* C,
                      int64_t m, int64_t n, int64_t r, int64_t b, bool backproject, const int* st, int st_mask,

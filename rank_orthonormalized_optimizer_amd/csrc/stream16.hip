@@ -23,9 +23,9 @@ namespace dion {
 
 constexpr int kStreamD = 4;   // slabs of global loads in flight per register set rotation
 
-// out[bz][c][i] = bf16(in[bz][i][c]) for i < rows, c < cols, zero for rows <= i < pitch: the
-// transposed bf16 copy of an fp32 [rows][cols] array, its rows padded with zeros to `pitch` (a
-// multiple of 32, so that every 32-wide slab read stays inside its row).
+// The transposed bf16 copy of an fp32 [rows][cols] array in 32-row slabs: element (i, c) goes to
+// out[bz][i / 32][c][i % 32], zero for rows <= i < pitch (pitch a multiple of 32).  A slab of the
+// transposed operand (all cols x 32) is then one contiguous block, read with whole cache lines.
 // 64 x 64 tiles through LDS; grid (ceil(cols / 64), ceil(pitch / 64), batch).
 __global__ __launch_bounds__(256) void t16_kernel(const float* in, uint16_t* out, int64_t rows, int64_t cols,
                                                   int64_t pitch, const int* st, int st_mask, int st_val) {
@@ -42,10 +42,18 @@ __global__ __launch_bounds__(256) void t16_kernel(const float* in, uint16_t* out
         tile[ty + 4 * q][tx] = (i < rows && c < cols) ? in[i * cols + c] : 0.f;
     }
     __syncthreads();
+    // eight consecutive rows of one column per thread, one 16-byte store; four threads fill the
+    // 64 bytes of a (slab, column) row, so a wave writes 1 KB of consecutive memory
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int64_t c = c0 + ty + 4 * q, i = i0 + tx;
-        if (c < cols && i < pitch) out[c * pitch + i] = float_to_bf16_bits(tile[tx][ty + 4 * q]);
+    for (int q = 0; q < 2; ++q) {
+        const int idx = threadIdx.x + 256 * q, i8 = idx & 3, cl = (idx >> 2) & 63, il = 32 * (idx >> 8) + 8 * i8;
+        const int64_t c = c0 + cl, i = i0 + il;
+        if (c < cols && i < pitch) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(tile[il + 2 * e][cl], tile[il + 2 * e + 1][cl]);
+            *(uint4*)&out[((i >> 5) * cols + c) * kSplitK + (i & 31)] = uint4{w[0], w[1], w[2], w[3]};
+        }
     }
 }
 
@@ -60,9 +68,9 @@ constexpr int kT16Rows = 256;
 struct SmallSlab {
     uint4 v[2];
     bool ok;
-    __device__ __forceinline__ void load(const uint16_t* rowp, int64_t k, bool in) {
-        v[0] = *(const uint4*)(rowp + k);
-        v[1] = *(const uint4*)(rowp + k + 8);
+    __device__ __forceinline__ void load(const uint16_t* p, bool in) {
+        v[0] = *(const uint4*)p;
+        v[1] = *(const uint4*)(p + 8);
         ok = in;
     }
     __device__ __forceinline__ void store(uint16_t* lds, int j, int half) const {
@@ -75,7 +83,7 @@ struct SmallSlab {
 struct Stream16Args {
     const float* M;
     const void* G;
-    const uint16_t* T;   // transposed bf16 small operand [b][r][pitch]
+    const uint16_t* T;   // transposed bf16 small operand [b][pitch / 32][r][32] (t16_kernel)
     float* C;            // output [b][rows][r] (P0: rows = m; R: rows = n)
     int64_t m, n, r, pitch;
     const int* st;
@@ -101,7 +109,8 @@ __global__ __launch_bounds__(512) void p16_kernel(Stream16Args a) {
     const int64_t rbase = bz * mn + (rok ? row : 0) * a.n;   // this lane's row (row 0 when outside)
     const int jb = t >> 1, half = t & 1;
     const bool jok = col0 + jb < a.r;
-    const uint16_t* Tr = a.T + ((int64_t)bz * a.r + (jok ? col0 + jb : 0)) * a.pitch + 16 * half;
+    const uint16_t* Tr = a.T + (int64_t)bz * a.r * a.pitch + (int64_t)(jok ? col0 + jb : 0) * kSplitK + 16 * half;
+    const int64_t slab = a.r * kSplitK;   // elements per 32-k slab of the small operand
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][KS][kT16Rows * kSplitK];
 
     const int nstep = (int)((a.n + kSplitK - 1) / kSplitK);     // 32-k steps
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(512) void p16_kernel(Stream16Args a) {
                 ag[d][kk][1] = *(const uint4*)((const float*)a.G + o + 4);
             }
             aok[d][kk] = kin && rok;                              // zeroed in frag(), once loaded
-            sb[d][kk].load(Tr, k, st < nstep && jok);
+            sb[d][kk].load(Tr + sc * slab, st < nstep && jok);
         }
     };
     auto frag = [&](int d, int kk) -> u32x4 {
@@ -232,7 +241,8 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
     const int64_t cofs = bz * mn + (cok ? j0 + c4 : 0);
     const int jb = t >> 1, half = t & 1;
     const bool tok = col0 + jb < a.r;
-    const uint16_t* Tr = a.T + ((int64_t)bz * a.r + (tok ? col0 + jb : 0)) * a.pitch + 16 * half;
+    const uint16_t* Tr = a.T + (int64_t)bz * a.r * a.pitch + (int64_t)(tok ? col0 + jb : 0) * kSplitK + 16 * half;
+    const int64_t slab = a.r * kSplitK;
     __shared__ __attribute__((aligned(16))) uint16_t la[2][128 * kR16Pitch];
     __shared__ __attribute__((aligned(16))) uint16_t lb[2][kT16Rows * kSplitK];
 
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
         }
         ok0[d] = i0ok && cok;                                    // zeroed in stage(), once loaded
         ok1[d] = i1ok && cok;
-        sb[d].load(Tr, (int64_t)sc * kSplitK, s < nslab && tok);
+        sb[d].load(Tr + sc * slab, s < nslab && tok);
     };
     // B values of the two rows, summed in fp32 and rounded to bf16, written at [c4 + e][2 p]
     auto stage = [&](int d, uint16_t* l) {
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(512) void r16_kernel(Stream16Args a) {
 }
 
 // Host side: a transposed bf16 copy of the small operand (Q for the product, P for the
-// back-projection) into tbuf ([b][r][stream16_pitch(rows)] bf16), then the product.  Returns a
+// back-projection) into tbuf ([b][stream16_pitch(rows) / 32][r][32] bf16), then the product.  Returns a
 // hipError_t value.  The caller has checked stream16_ok().
 bool stream16_ok(int64_t n, const void* M, const void* G, int g_bf16, bool backproject) {
     const int64_t need = backproject ? 4 : 8;
