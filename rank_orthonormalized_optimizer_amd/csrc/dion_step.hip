@@ -85,17 +85,12 @@ struct GemmArgs {
 // fp64 tiles are held to 128 registers a lane so that four workgroups share a CU (their LDS
 // is 40 KB each): the fp64 MFMA has a long issue time, and more resident waves keep it fed
 // across the per-slab barriers.
+// One output tile (tx, ty) of matrix bz (group grp) of a batched GEMM; the workgroup synchronizes
+// before returning only through mainloop's barriers, so a caller that reuses As / Bs for another
+// tile must synchronize first.
 template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
-__global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int bz, int grp, int tx, int ty, T* As, T* Bs) {
     using C = TileCfg<T, BM, BN, BK>;
-    const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
-    const TileId tid = xcd_tile_id();
-    const int bz = tid.z / zdiv, grp = tid.z % zdiv;
-    if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
-    // triangular K ranges: the longest tiles get the lowest dispatch order, so the launch does
-    // not end on them
-    const int tx = g.kskip == 1 ? (int)gridDim.x - 1 - tid.x : tid.x;
-    const int ty = g.kskip == 3 ? (int)gridDim.y - 1 - tid.y : tid.y;
     const int m0 = ty * BM, n0 = tx * BN;
     if (g.lower && n0 >= m0 + BM) return;
     int kbeg = 0, kend = g.K;
@@ -108,9 +103,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmA
         kext = min(g.K, g.ksplit_total - grp * g.K);
         kend = min(kend, kext);
     }
-
-    __shared__ T As[2 * C::A_STAGE];
-    __shared__ T Bs[2 * C::B_STAGE];
 
     Operand A = g.a, B = g.b;
     A.p0 = (const char*)A.p0 + bz * g.sa0 + grp * g.ga0;
@@ -163,11 +155,56 @@ __global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmA
 }
 
 template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
+__global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_kernel(GemmArgs g) {
+    using C = TileCfg<T, BM, BN, BK>;
+    const int zdiv = g.zdiv > 1 ? g.zdiv : 1;
+    const TileId tid = xcd_tile_id();
+    const int bz = tid.z / zdiv, grp = tid.z % zdiv;
+    if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
+    // triangular K ranges: the longest tiles get the lowest dispatch order, so the launch does
+    // not end on them
+    const int tx = g.kskip == 1 ? (int)gridDim.x - 1 - tid.x : tid.x;
+    const int ty = g.kskip == 3 ? (int)gridDim.y - 1 - tid.y : tid.y;
+    __shared__ T As[2 * C::A_STAGE];
+    __shared__ T Bs[2 * C::B_STAGE];
+    gemm_tile<T, BM, BN, BK, AKC, ASRC, BKC, BSRC>(g, bz, grp, tx, ty, As, Bs);
+}
+
+// The same GEMM with a fixed number of workgroups per matrix (grid: workgroups x 1 x matrices),
+// each looping over tiles, for the rarely taken paths: a launch that finds no matrix to work on
+// then costs as little as a small grid, while a selected matrix still spreads over many CUs.
+template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
+__global__ __launch_bounds__(256, sizeof(T) == 8 ? 4 : 1) void gemm_stride_kernel(GemmArgs g) {
+    using C = TileCfg<T, BM, BN, BK>;
+    const int bz = blockIdx.z;
+    if (g.st && (g.st[bz] & g.st_mask) != g.st_val) return;
+    __shared__ T As[2 * C::A_STAGE];
+    __shared__ T Bs[2 * C::B_STAGE];
+    const int64_t tiles_x = (g.N + BN - 1) / BN, tiles = tiles_x * ((g.M + BM - 1) / BM);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        gemm_tile<T, BM, BN, BK, AKC, ASRC, BKC, BSRC>(g, bz, 0, (int)(t % tiles_x), (int)(t / tiles_x), As, Bs);
+        __syncthreads();   // As / Bs are rewritten by the next tile
+    }
+}
+
+template <typename T, int BM, int BN, int BK, bool AKC, int ASRC, bool BKC, int BSRC>
 static hipError_t launch_gemm_tile(const GemmArgs& g, int64_t batch, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
     const int64_t zdiv = g.zdiv > 1 ? g.zdiv : 1;
     dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, (unsigned)(batch * zdiv));
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, AKC, ASRC, BKC, BSRC>), grid, dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+constexpr int kRareGemmBlocks = 128;   // workgroups per matrix of a rare-path GEMM
+
+template <typename T, bool AKC, int ASRC, bool BKC, int BSRC>
+static hipError_t launch_gemm_rare(const GemmArgs& g, int64_t batch, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0 || batch <= 0) return hipSuccess;
+    constexpr int BM = 64, BN = 64, BK = sizeof(T) == 8 ? 16 : 32;
+    const int64_t tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
+    dim3 grid((unsigned)(tiles < kRareGemmBlocks ? tiles : kRareGemmBlocks), 1, (unsigned)batch);
+    hipLaunchKernelGGL((gemm_stride_kernel<T, BM, BN, BK, AKC, ASRC, BKC, BSRC>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
@@ -1500,6 +1537,242 @@ __global__ __launch_bounds__(1024) void householder_kernel(double* A, double* Q,
     if (t == 0) st[bz] = (st[bz] & ~ST_FAIL) | ST_HH;
 }
 
+// Blocked form of the same Householder QR for ranks above kFusedMaxBlocks * kNB, where the
+// one-workgroup column loop above would take seconds per matrix: panels of kHHB columns, each
+// factored by one workgroup, the block reflector H_j0 ... H_j0+nb-1 = I - V T V^T kept in compact
+// WY form (V unit lower trapezoidal, T upper triangular: T_cc = tau_c and
+// T[0:c, c] = -tau_c T[0:c, 0:c] V[:, 0:c]^T v_c), and the columns to the right updated by
+// A <- A - V (T^T (V^T A)) as three fp64 matrix-core products.  Q = H_0 ... H_{r-1} [I; 0] is then
+// built backwards by Q <- Q - V (T (V^T Q)) over rows and columns from j0 on, and column c of Q
+// takes the sign of R_cc.  The same reflectors (and tau, beta) as the column loop.
+constexpr int kHHB = 32;
+
+// Panel j0 of matrix bz (grid: matrices; 1024 threads): the reflectors of columns j0 .. j0 + nb - 1,
+// applied within the panel; the panel then holds V explicitly (unit diagonal, zeros above), sgn
+// the signs of R's diagonal and T (nb x nb, row-major, zeros below) goes to Tp.
+__global__ __launch_bounds__(1024) void hh_panel_kernel(double* A, int64_t m, int64_t r, int64_t j0, double* Tp,
+                                                        int64_t sT, double* sgn, int64_t ssg, const int* st,
+                                                        int st_mask, int st_val) {
+    const int bz = blockIdx.x;
+    if ((st[bz] & st_mask) != st_val) return;
+    A += bz * m * r;
+    Tp += bz * sT;
+    sgn += bz * ssg;
+    constexpr int NT = 1024, NB = kHHB, NRG = NT / NB, U = 4, CH = 128;
+    const int nb = (int)((r - j0) < NB ? (r - j0) : NB);
+    __shared__ double red[NT / 64];
+    __shared__ double tau[NB];
+    __shared__ double Y[NB][NB + 1];
+    __shared__ double T[NB][NB + 1];
+    __shared__ double chunk[CH][NB + 1];
+    __shared__ double wred[NRG][NB + 1];
+    __shared__ double wv[NB];
+    // thread (rg, col): rows rg, rg + 32, ... of panel column col, so that a wave reads two
+    // 256-byte row pieces of the panel at a time; U rows of loads in flight per thread
+    const int t = threadIdx.x, col = t % NB, rg = t / NB, lane = t & 63, wave = t >> 6;
+    auto block_sum = [&](double v) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        double s = 0.0;
+#pragma unroll
+        for (int q = 0; q < NT / 64; ++q) s += red[q];
+        __syncthreads();
+        return s;
+    };
+    for (int c = 0; c < nb; ++c) {
+        const int64_t j = j0 + c;
+        const double x0 = A[j * r + j];
+        double ss = 0.0;
+        for (int64_t i = j + 1 + t; i < m; i += NT) { const double a = A[i * r + j]; ss += a * a; }
+        const double s = block_sum(ss);
+        double tj = 0.0, beta = x0;
+        if (s > 0.0) {
+            const double alpha = sqrt(x0 * x0 + s);
+            beta = x0 >= 0.0 ? -alpha : alpha;
+            tj = (beta - x0) / beta;
+            const double scale = 1.0 / (x0 - beta);
+            for (int64_t i = j + 1 + t; i < m; i += NT) A[i * r + j] *= scale;
+        }
+        if (t == 0) { tau[c] = tj; sgn[j] = beta < 0.0 ? -1.0 : 1.0; A[j * r + j] = 1.0; }
+        __syncthreads();
+        if (tj != 0.0 && c + 1 < nb) {   // panel columns to the right: w = tau v^T a, a -= w v
+            const bool act = col > c && col < nb;
+            double w = 0.0;
+            if (act)
+                for (int64_t ib = j + rg; ib < m; ib += U * NRG) {
+                    double v[U], a[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t i = ib + u * NRG;
+                        v[u] = i < m ? A[i * r + j] : 0.0;
+                        a[u] = i < m ? A[i * r + j0 + col] : 0.0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) w += v[u] * a[u];
+                }
+            wred[rg][col] = w;
+            __syncthreads();
+            if (t < NB) {
+                double acc = 0.0;
+                for (int q = 0; q < NRG; ++q) acc += wred[q][t];
+                wv[t] = tj * acc;
+            }
+            __syncthreads();
+            if (act) {
+                const double wc = wv[col];
+                for (int64_t ib = j + rg; ib < m; ib += U * NRG) {
+                    double v[U], a[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t i = ib + u * NRG;
+                        v[u] = i < m ? A[i * r + j] : 0.0;
+                        a[u] = i < m ? A[i * r + j0 + col] : 0.0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t i = ib + u * NRG;
+                        if (i < m) A[i * r + j0 + col] = a[u] - wc * v[u];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // V explicit above the diagonal of the panel's first nb rows
+    for (int idx = t; idx < nb * nb; idx += NT) {
+        const int rr = idx / nb, cc = idx % nb;
+        if (rr < cc) A[(j0 + rr) * r + j0 + cc] = 0.0;
+    }
+    __syncthreads();
+    // Y = V^T V by CH-row chunks through LDS: thread t owns the pair (t / NB, t % NB)
+    double y = 0.0;
+    const int c1 = t / NB, c2 = t % NB;
+    for (int64_t i0 = j0; i0 < m; i0 += CH) {
+#pragma unroll
+        for (int q = 0; q < CH * NB / NT; ++q) {
+            const int idx = t + NT * q, rr = idx / NB, cc = idx % NB;
+            chunk[rr][cc] = (i0 + rr < m && cc < nb) ? A[(i0 + rr) * r + j0 + cc] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int rr = 0; rr < CH; ++rr) y += chunk[rr][c1] * chunk[rr][c2];
+        __syncthreads();
+    }
+    Y[c1][c2] = y;
+    T[c1][c2] = 0.0;
+    __syncthreads();
+    for (int c = 0; c < nb; ++c) {   // column c of T from the columns before it
+        if (t < c) {
+            double acc = 0.0;
+            for (int k = t; k < c; ++k) acc += T[t][k] * Y[k][c];
+            T[t][c] = -tau[c] * acc;
+        }
+        if (t == c) T[c][c] = tau[c];
+        __syncthreads();
+    }
+    Tp[c1 * NB + c2] = (c1 < nb && c2 < nb) ? T[c1][c2] : 0.0;
+}
+
+// Q = [I; 0] ([m][r]) for the selected matrices (grid: blocks x matrices).
+__global__ __launch_bounds__(256) void hh_init_q_kernel(double* Q, int64_t m, int64_t r, const int* st, int st_mask,
+                                                        int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    Q += bz * m * r;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < m * r; idx += (int64_t)gridDim.x * 256)
+        Q[idx] = (idx / r == idx % r) ? 1.0 : 0.0;
+}
+
+// Q[:, c] *= sign(R_cc), and the state bits of a finished Householder QR (grid: blocks x matrices).
+__global__ __launch_bounds__(256) void hh_finish_kernel(double* Q, const double* sgn, int64_t ssg, int64_t m,
+                                                        int64_t r, int* st, int st_mask, int st_val) {
+    const int bz = blockIdx.y;
+    if ((st[bz] & st_mask) != st_val) return;
+    Q += bz * m * r;
+    sgn += bz * ssg;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < m * r; idx += (int64_t)gridDim.x * 256)
+        if (sgn[idx % r] < 0.0) Q[idx] = -Q[idx];
+}
+
+__global__ void hh_done_kernel(int* st, int64_t b, int st_mask, int st_val) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < b && (st[i] & st_mask) == st_val) st[i] = (st[i] & ~ST_FAIL) | ST_HH;
+}
+
+// Blocked Householder QR of the selected matrices: A ([b][m][r], overwritten by V) -> Q ([b][m][r]).
+// Scratch: the Gram and factor regions hold V^T A and T^T (V^T A) ([nb][r] per matrix), the
+// inverse region the panels' T, the column-scale region the signs of diag(R).  Every GEMM runs on
+// a fixed, small grid per matrix (launch_gemm_rare), so that the launches cost little when no
+// matrix is selected.
+static int householder_blocked(const ChainCtx& c, double* A, double* Q, int mask, int val) {
+    const Plan& p = *c.p;
+    const int64_t m = p.m, r = p.r, b = p.b;
+    double* W1 = (double*)(c.ws + p.W);
+    double* W2 = (double*)(c.ws + p.L);
+    double* Tall = (double*)(c.ws + p.Tf);
+    double* sgn = (double*)(c.ws + p.cs);
+    const int64_t rr = r * r, srr = rr * 8, smr = m * r * 8;
+    const bool vr = (r % 4) == 0;
+    constexpr int S = SRC_F64;
+    const int64_t npanel = (r + kHHB - 1) / kHHB;
+    auto args = [&]() {
+        GemmArgs g{};
+        g.st = c.st; g.st_mask = mask; g.st_val = val;
+        return g;
+    };
+    // three products per panel j: W1 = V^T X, W2 = op(T) W1, X -= V W2 (X: rows j0.., columns x0..)
+    auto reflect = [&](int64_t j0, int nb, const double* Tj, bool transpose_t, double* X, int64_t nx) -> int {
+        GemmArgs g = args();
+        g.a = Operand{A + j0 * r + j0, nullptr, r, nb, (int)(m - j0), vr};   // V^T (x-contiguous)
+        g.b = Operand{X, nullptr, r, (int)nx, (int)(m - j0), vr};
+        g.sa0 = smr; g.sb0 = smr;
+        g.c = W1; g.ldc = r; g.sc = srr;
+        g.M = nb; g.N = (int)nx; g.K = (int)(m - j0);
+        g.alpha = 1; g.beta = 0;
+        DION_TRY((launch_gemm_rare<double, false, S, false, S>(g, b, c.s)));
+        GemmArgs h = args();
+        h.a = Operand{Tj, nullptr, kHHB, nb, nb, true};
+        h.b = Operand{W1, nullptr, r, (int)nx, nb, vr};
+        h.sa0 = srr; h.sb0 = srr;
+        h.c = W2; h.ldc = r; h.sc = srr;
+        h.M = nb; h.N = (int)nx; h.K = nb;
+        h.alpha = 1; h.beta = 0;
+        if (transpose_t) DION_TRY((launch_gemm_rare<double, false, S, false, S>(h, b, c.s)));   // T^T: T[k][x]
+        else DION_TRY((launch_gemm_rare<double, true, S, false, S>(h, b, c.s)));                // T: T[x][k]
+        GemmArgs u = args();
+        u.a = Operand{A + j0 * r + j0, nullptr, r, (int)(m - j0), nb, vr};   // V (k-contiguous)
+        u.b = Operand{W2, nullptr, r, (int)nx, nb, vr};
+        u.sa0 = smr; u.sb0 = srr;
+        u.c = X; u.ldc = r; u.sc = smr;
+        u.M = (int)(m - j0); u.N = (int)nx; u.K = nb;
+        u.alpha = -1; u.beta = 1;
+        DION_TRY((launch_gemm_rare<double, true, S, false, S>(u, b, c.s)));
+        return 0;
+    };
+    int e;
+    for (int64_t jb = 0; jb < npanel; ++jb) {
+        const int64_t j0 = jb * kHHB, nb = (r - j0) < kHHB ? (r - j0) : kHHB, nc = r - j0 - nb;
+        double* Tj = Tall + jb * kHHB * kHHB;
+        hipLaunchKernelGGL(hh_panel_kernel, dim3((unsigned)b), dim3(1024), 0, c.s, A, m, r, j0, Tj, rr, sgn, r, c.st,
+                           mask, val);
+        DION_TRY(hipGetLastError());
+        if (nc > 0 && (e = reflect(j0, (int)nb, Tj, true, A + j0 * r + j0 + nb, nc))) return e;
+    }
+    dim3 grid(grid_1d(m * r, 512), (unsigned)b);
+    hipLaunchKernelGGL(hh_init_q_kernel, grid, dim3(256), 0, c.s, Q, m, r, c.st, mask, val);
+    DION_TRY(hipGetLastError());
+    for (int64_t jb = npanel - 1; jb >= 0; --jb) {
+        const int64_t j0 = jb * kHHB, nb = (r - j0) < kHHB ? (r - j0) : kHHB;
+        if ((e = reflect(j0, (int)nb, Tall + jb * kHHB * kHHB, false, Q + j0 * r + j0, r - j0))) return e;
+    }
+    hipLaunchKernelGGL(hh_finish_kernel, grid, dim3(256), 0, c.s, Q, (const double*)sgn, r, m, r, c.st, mask, val);
+    DION_TRY(hipGetLastError());
+    hipLaunchKernelGGL(hh_done_kernel, dim3(grid_1d(b)), dim3(256), 0, c.s, c.st, b, mask, val);
+    return (int)hipGetLastError();
+}
+
 // st |= bits for the matrices with (st & mask) == val.
 __global__ void set_bits_kernel(int* st, int64_t b, int st_mask, int st_val, int bits) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -2378,9 +2651,13 @@ static int run_chain(const ChainCtx& c, const float* M, const void* G, bool g_bf
             hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, (const T*)P, Pb, p.m * p.r, c.st,
                                A64 | F, A64 | F);
             DION_TRY(hipGetLastError());
-            hipLaunchKernelGGL(householder_kernel, dim3((unsigned)p.b), dim3(1024), 0, c.s, (double*)Pb, (double*)P,
-                               p.m, p.r, c.st, A64 | F, A64 | F);
-            DION_TRY(hipGetLastError());
+            if (p.nblk > kFusedMaxBlocks) {   // large ranks: the blocked form on the matrix cores
+                if ((e = householder_blocked(c, (double*)Pb, (double*)P, A64 | F, A64 | F))) return e;
+            } else {
+                hipLaunchKernelGGL(householder_kernel, dim3((unsigned)p.b), dim3(1024), 0, c.s, (double*)Pb,
+                                   (double*)P, p.m, p.r, c.st, A64 | F, A64 | F);
+                DION_TRY(hipGetLastError());
+            }
         }
         hipLaunchKernelGGL((copy_pred_kernel<T>), grid, dim3(256), 0, c.s, Pb, P, p.m * p.r, c.st,
                            A64 | SH | F | ST_HH, A64 | SH);

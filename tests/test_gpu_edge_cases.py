@@ -90,11 +90,14 @@ def test_failed_factorization_takes_the_rank0_step(cuda):
         check_errs(e, tol_for(wl), f"matrix {i}")
 
 
-@pytest.mark.parametrize("kind", ["duplicate", "zero"])
-def test_natural_breakdown_reaches_householder(cuda, kind):
+@pytest.mark.parametrize("kind,shape", [("duplicate", (3, 256, 320, 24)), ("zero", (3, 256, 320, 24)),
+                                        ("duplicate", (2, 640, 600, 560))])
+def test_natural_breakdown_reaches_householder(cuda, kind, shape):
+    """A degenerate Q column makes P0 singular: every CholeskyQR pass breaks down and the matrix
+    reaches the Householder QR without the option (the blocked form at rank 560)."""
     import torch
     import rank_orthonormalized_optimizer_amd as dion
-    wl = W.SMALL[1].with_groups(W.Group(3, 256, 320, 24), name=f"breakdown-{kind}", steps=2)
+    wl = W.SMALL[1].with_groups(W.Group(*shape), name=f"breakdown-{kind}-r{shape[3]}", steps=2)
     g = wl.groups[0]
     X, M, Q = W.make_state(wl, 0)
     j = 7

@@ -125,3 +125,41 @@ def test_full_size_full_rank(cuda):
     P^T P = I and M' = mu B on all eight."""
     wl = W.get(5)
     _check(wl, _run(wl, cuda, wl.steps, lambda b: [0, b - 1]))
+
+
+def test_full_size_householder(cuda):
+    """One 4096^2 matrix of workload 5 (r = 4096) through the blocked Householder QR (requested),
+    against the oracle, and timed beside the same step through the CholeskyQR chain."""
+    import torch
+    import rank_orthonormalized_optimizer_amd as dion
+    wl = W.get(5).with_groups(W.Group(1, 4096, 4096, 4096), name="householder-4096")
+    g = wl.groups[0]
+    X0, M0, Q0 = W.make_state_device(wl, 0, cuda)
+    Gd = W.make_grad_device(wl, 0, 1, cuda)
+    ws = dion.api.workspace_for(g.m, g.n, g.batch, g.rank, cuda)
+    times = {}
+    for name, opts in (("cholesky", dion.OPT_FORCE_F64), ("householder", dion.OPT_FORCE_F64 | dion.OPT_HOUSEHOLDER)):
+        ms = []
+        for rep in range(3):
+            X, M, Q = X0.clone(), M0.clone(), Q0.clone()
+            flags = torch.zeros(1, dtype=torch.int32, device=cuda)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            dion.step_(X, Gd, M, Q, g.rank, wl.mu, wl.lr, wl.eps, workspace=ws, flags=flags, options=opts)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        times[name] = min(ms)
+        print(f"[fullsize] 4096^2 r=4096 step through the {name} path: {min(ms):.1f} ms (best of 3)", flush=True)
+        if name == "householder":
+            fl = to_numpy(flags)
+            assert fl[0] & dion.FLAG_HOUSEHOLDER and not fl[0] & dion.FLAG_NONFINITE, fl
+            P = ws[:4 * g.m * g.rank].view(torch.float32).view(1, g.m, g.rank)
+            pre = {"X": to_numpy(X0), "M": to_numpy(M0), "Q": to_numpy(Q0)}
+            post = {"X": to_numpy(X), "M": to_numpy(M), "Q": to_numpy(Q), "P": to_numpy(P)}
+            errs = compare_step(wl, pre, post, to_numpy(Gd), g.rank)
+            print(f"[fullsize]   householder errs {errs}", flush=True)
+            for e in errs:
+                check_errs(e, tol_for(wl), "householder 4096")
+    assert times["householder"] < 20 * times["cholesky"], times

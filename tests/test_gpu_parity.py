@@ -219,6 +219,21 @@ def test_householder_fallback(cuda, wid):
     check(rep, tol_for(wl))
 
 
+@pytest.mark.parametrize("shape", [(2, 700, 640, 600), (1, 1100, 700, 590)])
+def test_blocked_householder(cuda, shape):
+    """Ranks above 512 take the blocked Householder QR (32-column panels in compact WY form, the
+    panel updates and the formation of Q as fp64 matrix-core products): ragged last panels, a
+    square-ish and a tall shape, requested for every matrix, against the oracle."""
+    import rank_orthonormalized_optimizer_amd as dion
+    b, m, n, r = shape
+    wl = W.SMALL[2].with_groups(W.Group(b, m, n, r), name=f"hh-blocked-{m}x{n}-r{r}", steps=2)
+    rep = run_teacher_forced(wl, cuda, options=dion.OPT_FORCE_F64 | dion.OPT_HOUSEHOLDER, steps=2)
+    for _, _, _, flags in rep:
+        assert np.all(flags & dion.FLAG_HOUSEHOLDER) and np.all(flags & dion.FLAG_F64), flags
+        assert not np.any(flags & dion.FLAG_NONFINITE), flags
+    check(rep, tol_for(wl))
+
+
 @pytest.mark.parametrize("spectral", [False, True])
 @pytest.mark.parametrize("force64", [False, True])
 def test_shifted_first_pass(cuda, force64, spectral):
