@@ -509,10 +509,12 @@ __device__ bool chol_inv64(DiagSmem<T>& sm) {
 // p.L and the inverse to p.Td, and track the diagonal ratio.  Returns false (fail bit set) on
 // a non-positive or non-finite pivot; the decision is the same in every thread.
 template <typename T>
+__device__ bool diag_factor(const PotrfArgs& p, int bz, DiagSmem<T>& sm);
+
+template <typename T>
 __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
     const int tid = threadIdx.x, nbj = p.nbj;
     const T* S = (const T*)p.S + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
-    T* L = (T*)p.L + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
     {   // all sixteen loads of a thread in flight at once (addresses clamped, values selected)
         T v[kNB * kNB / 256];
         const int64_t o0 = (int64_t)(tid >> 6) * p.ldl + (tid & 63), step = 4 * p.ldl;   // row tid / 64 + 4 q
@@ -528,6 +530,15 @@ __device__ bool diag_block(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
         }
     }
     __syncthreads();
+    return diag_factor<T>(p, bz, sm);
+}
+
+// The rest of diag_block for a block already in sm.a (lower part; the identity elsewhere):
+// factor and invert it, track the diagonal ratio, write L and the inverse.
+template <typename T>
+__device__ bool diag_factor(const PotrfArgs& p, int bz, DiagSmem<T>& sm) {
+    const int tid = threadIdx.x, nbj = p.nbj;
+    T* L = (T*)p.L + bz * p.sL + (int64_t)p.j0 * p.ldl + p.j0;
     if (!chol_inv64<T>(sm)) {
         if (tid == 0) p.st[bz] |= p.fail_bit;
         return false;
@@ -1869,55 +1880,169 @@ __device__ void tile_gemm(const Operand& A, const Operand& B, int M, int N, int 
 //   X_jb,kb = -Td_jb (sum_{kb <= q < jb} L_jb,q X_q,kb),   kb < jb,
 // which read L_jb,q from the upper blocks (q, jb) kept by earlier steps.  The step after the last
 // diagonal block (jb = nblk - 1) has inverse tiles only.
+// One thread's sixteen elements of a 64 x 64 block (rows < nr, columns < nc of a row-major array
+// of pitch ld; zero elsewhere): the loads are issued together (addresses clamped, values selected
+// afterwards) and stored to an LDS block of pitch kDLD later, transposed if asked.
+template <typename T>
+struct BlkRegs {
+    T v[kNB * kNB / 256];
+    __device__ __forceinline__ void fetch(const T* src, int64_t ld, int nr, int nc) {
+        const int i0 = threadIdx.x >> 6, j = threadIdx.x & 63;
+#pragma unroll
+        for (int q = 0; q < kNB * kNB / 256; ++q) {
+            const int i = i0 + 4 * q;
+            v[q] = src[(i < nr && j < nc) ? (int64_t)i * ld + j : 0];
+        }
+#pragma unroll
+        for (int q = 0; q < kNB * kNB / 256; ++q) v[q] = (i0 + 4 * q < nr && j < nc) ? v[q] : T(0);
+    }
+    __device__ __forceinline__ void put(T* dst, bool trans) const {
+        const int i0 = threadIdx.x >> 6, j = threadIdx.x & 63;
+#pragma unroll
+        for (int q = 0; q < kNB * kNB / 256; ++q) dst[trans ? j * kDLD + i0 + 4 * q : (i0 + 4 * q) * kDLD + j] = v[q];
+    }
+};
+
+// acc += A B^T for the calling wave's four 16 x 16 output blocks (row block `wave`, column blocks
+// 0..3) of a 64 x 64 product of LDS blocks (pitch kDLD): C(i, j) = sum_k A[i][k] B[j][k], K a
+// multiple of 16 (zero padded).
+template <typename T>
+__device__ __forceinline__ void blk_abt(const T* A, const T* B, int K, typename Mfma<T>::acc_t (&acc)[4], int wave,
+                                        int lane) {
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) blk_mma<T>(&A[16 * wave * kDLD], kDLD, 1, &B[16 * jb * kDLD], 1, kDLD, K, acc[jb], lane);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void chol_step_kernel(CholStepArgs a) {
     const int bz = blockIdx.y, t = blockIdx.x;
     if ((a.st[bz] & a.st_mask) != a.st_val) return;
-    using C = TileCfg<T, 64, 64, sizeof(T) == 8 ? 16 : 32>;
+    using acc_t = typename Mfma<T>::acc_t;
     __shared__ DiagSmem<T> sm;
-    __shared__ T As[2 * C::A_STAGE];
-    __shared__ T Bs[2 * C::B_STAGE];
+    __shared__ T bp[kNB * kDLD];
+    __shared__ T bq[kNB * kDLD];
     const int64_t r = a.r, rr = r * r;
     const T* S = (const T*)a.S + bz * rr;
     T* L = (T*)a.L + bz * rr;
     T* Tf = (T*)a.Tf + bz * rr;
-    const bool vr = (r % 4) == 0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, fr = lane & 15;
     auto nb = [&](int q) { return (int)((r - (int64_t)q * kNB) < kNB ? (r - (int64_t)q * kNB) : kNB); };
     const int jb = a.jb, j0 = jb * kNB, nbj = nb(jb), n = a.nblk - 1 - jb, ntr = n * (n + 1) / 2;
-    const Operand Td{Tf + (int64_t)j0 * (r + 1), nullptr, r, nbj, nbj, vr};   // Td(i,k) = X_jb,jb[i][k]
+    const int K16 = (nbj + 15) / 16 * 16;
+    const T* Td = Tf + (int64_t)j0 * (r + 1);   // X_jb,jb (lower; zero above its diagonal)
+    acc_t acc[4];
+    auto zero = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = acc_t{0, 0, 0, 0};
+    };
+    // the calling thread's elements of the wave's output blocks: (row, col, value)
+    auto each = [&](auto f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) f(16 * wave + Mfma<T>::row(lane, v), 16 * q + fr, acc[q][v]);
+    };
     if (t < ntr) {
         int k = jb + 1, rem = t;
         while (rem >= a.nblk - k) { rem -= a.nblk - k; ++k; }
         const int i = k + rem;
         const int64_t i0 = (int64_t)i * kNB, k0 = (int64_t)k * kNB;
         const int nbi = nb(i), nbk = nb(k);
-        tile_gemm<T, true>(Operand{S + i0 * r + j0, nullptr, r, nbi, nbj, vr}, Td, nbi, nbj, nbj, sm.a, kDLD, T(1),
-                           T(0), As, Bs);
-        const T* Lk = sm.a;
+        // every load of the task in flight at once: Td, S_i,jb, S_k,jb and S_ik (the last in the
+        // accumulator layout of the update)
+        BlkRegs<T> rt, ri, rk;
+        rt.fetch(Td, r, nbj, nbj);
+        ri.fetch(S + i0 * r + j0, r, nbi, nbj);
+        if (k != i) rk.fetch(S + k0 * r + j0, r, nbk, nbj);
+        const T* Sik = S + i0 * r + k0;
+        T sv[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * wave + Mfma<T>::row(lane, v), col = 16 * q + fr;
+                sv[q][v] = Sik[(row < nbi && col < nbk) ? (int64_t)row * r + col : 0];
+            }
+        rt.put(bq, false);
+        ri.put(bp, false);
+        if (k != i) rk.put(sm.x, false);
+        __syncthreads();
+        // L_i,jb = S_i,jb Td^T into sm.a; L_k,jb = S_k,jb Td^T into bp
+        zero();
+        blk_abt<T>(bp, bq, K16, acc, wave, lane);
         if (k != i) {
-            tile_gemm<T, true>(Operand{S + k0 * r + j0, nullptr, r, nbk, nbj, vr}, Td, nbk, nbj, nbj, sm.x, kDLD,
-                               T(1), T(0), As, Bs);
-            Lk = sm.x;
+            acc_t ak[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ak[q] = acc_t{0, 0, 0, 0};
+            blk_abt<T>(sm.x, bq, K16, ak, wave, lane);
+            __syncthreads();   // bp is free
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bp[(16 * wave + Mfma<T>::row(lane, v)) * kDLD + 16 * q + fr] = ak[q][v];
         }
-        if (k == jb + 1)
+        each([&](int row, int col, T v) { sm.a[row * kDLD + col] = v; });
+        const T* Lk = k != i ? bp : sm.a;
+        __syncthreads();
+        if (k == jb + 1)   // this tile's row block keeps L_i,jb, transposed, in the upper block (jb, i)
             for (int idx = threadIdx.x; idx < nbj * nbi; idx += 256) {
                 const int u = idx / nbi, v = idx % nbi;
                 L[(int64_t)(j0 + u) * r + i0 + v] = sm.a[v * kDLD + u];
             }
-        tile_gemm<T, true>(Operand{sm.a, nullptr, kDLD, nbi, nbj, false}, Operand{Lk, nullptr, kDLD, nbk, nbj, false},
-                           nbi, nbk, nbj, L + i0 * r + k0, r, T(-1), T(1), As, Bs, S + i0 * r + k0);
-        if (t == 0) {
-            diag_block<T>(a.diag, bz, sm);   // the updated block, read back from L
+        // L_ik = S_ik - L_i,jb L_k,jb^T
+        zero();
+        blk_abt<T>(sm.a, Lk, K16, acc, wave, lane);
+        if (t != 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * wave + Mfma<T>::row(lane, v), col = 16 * q + fr;
+                    if (row < nbi && col < nbk) L[(i0 + row) * r + k0 + col] = sv[q][v] - acc[q][v];
+                }
+            return;
         }
+        // tile (jb + 1, jb + 1): the updated block goes straight into the diagonal factorization
+        __syncthreads();   // every wave is done reading sm.a
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * wave + Mfma<T>::row(lane, v), col = 16 * q + fr;
+                sm.a[row * kDLD + col] = (row < nbk && col <= row) ? sv[q][v] - acc[q][v] : (row == col ? T(1) : T(0));
+            }
+        __syncthreads();
+        diag_factor<T>(a.diag, bz, sm);
         return;
     }
-    const int kb = t - ntr, k0 = kb * kNB, nbk = nb(kb), K = j0 - k0;
-    // Y = sum_q L_jb,q X_q,kb in LDS: A(i, k) = L_jb,(k0 + k) = L[(k0 + k) r + j0 + i] (upper blocks)
-    tile_gemm<T, false, false>(Operand{L + (int64_t)k0 * r + j0, nullptr, r, nbj, K, vr},
-                               Operand{Tf + (int64_t)k0 * r + k0, nullptr, r, nbk, K, vr}, nbj, nbk, K, sm.a, kDLD,
-                               T(1), T(0), As, Bs);
-    tile_gemm<T, false>(Td, Operand{sm.a, nullptr, kDLD, nbk, nbj, false}, nbj, nbk, nbj, Tf + (int64_t)j0 * r + k0,
-                        r, T(-1), T(0), As, Bs);
+    // inverse tile X_jb,kb = -Td (sum_{kb <= q < jb} L_jb,q X_q,kb), kb = t - ntr; A = L_jb,q (kept
+    // transposed in the upper block (q, jb)), B = X_q,kb^T; the next pair is fetched during a product
+    const int kb = t - ntr, k0 = kb * kNB, nbk = nb(kb);
+    BlkRegs<T> ra, rb, rt;
+    ra.fetch(L + (int64_t)kb * kNB * r + j0, r, kNB, nbj);
+    rb.fetch(Tf + (int64_t)kb * kNB * r + k0, r, kNB, nbk);
+    rt.fetch(Td, r, nbj, nbj);
+    zero();
+    for (int q = kb; q < jb; ++q) {
+        ra.put(bp, true);
+        rb.put(bq, true);
+        __syncthreads();
+        if (q + 1 < jb) {
+            ra.fetch(L + (int64_t)(q + 1) * kNB * r + j0, r, kNB, nbj);
+            rb.fetch(Tf + (int64_t)(q + 1) * kNB * r + k0, r, kNB, nbk);
+        }
+        blk_abt<T>(bp, bq, kNB, acc, wave, lane);
+        __syncthreads();
+    }
+    // Y^T into bp, Td into bq; X_jb,kb = -Td Y
+    each([&](int row, int col, T v) { bp[col * kDLD + row] = v; });
+    rt.put(bq, false);
+    __syncthreads();
+    zero();
+    blk_abt<T>(bq, bp, K16, acc, wave, lane);
+    each([&](int row, int col, T v) {
+        if (row < nbj && col < nbk) Tf[(int64_t)(j0 + row) * r + k0 + col] = -v;
+    });
 }
 
 template <typename T>
