@@ -76,20 +76,17 @@ inline bool make_plan(int64_t m, int64_t n, int64_t b, int64_t r, Plan* p) {
     q.nblk = (r + kNB - 1) / kNB;
     q.nchunk = (n + kNormChunk - 1) / kNormChunk;
     q.kp = (r + 31) / 32 * 32;
-    {   // split the Gram's long K (= m) over the grid: with four 64 x 64 workgroups resident per
-        // CU (the register budget of the fp64 tile), pick the split count minimizing
-        // rounds x (slabs per split + 3 slabs of fill and drain), keeping >= 128 rows per split
-        // and the partials within 512 MB
+    {   // split the Gram's long K (= m) over the grid: the fewest splits that give the launch at
+        // least 1.5 64 x 64 workgroups per CU (measured on 24 x 1024 x 256: two splits, about 1.9
+        // workgroups per CU, beat one split (0.9, too few waves to hide latency) and four (3.75,
+        // twice the partials and each workgroup's fill and drain over a quarter of the K range)),
+        // keeping >= 128 rows per split and the partials within 512 MB
         const int64_t nt = (r + 63) / 64;
         const int64_t tiles = nt * (nt + 1) / 2 * (b > 0 ? b : 1);
-        const int64_t slots = 256 * 4, slabs = (m + 15) / 16;
         int64_t best = 1;
-        double best_cost = 0.0;
-        for (int64_t s = 1; s <= 16; ++s) {
-            if (s > 1 && (s > m / 128 || (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20))) break;
-            const double rounds = (double)((s * tiles + slots - 1) / slots);
-            const double cost = rounds * (double)((slabs + s - 1) / s + 3);
-            if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
+        for (int64_t s = 2; s <= 16 && best * tiles < 384; ++s) {
+            if (s > m / 128 || (double)(b > 0 ? b : 1) * s * r * r * 8 > 512.0 * (1 << 20)) break;
+            best = s;
         }
         q.gsplit = tiles > 0 ? best : 1;
     }

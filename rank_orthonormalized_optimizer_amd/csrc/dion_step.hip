@@ -1326,6 +1326,10 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = 
         if ((e = gram6(c, P, mask, val, splits, kc))) return e;
         if (splits <= 1) return 0;
     } else {
+        // whole 16-k slabs per split where that still leaves the last split some rows, so every
+        // tile takes the branch-free main loop
+        const int64_t kc16 = (kc + 15) / 16 * 16;
+        if ((splits - 1) * kc16 < m) kc = kc16;
         GemmArgs g{};
         g.a = Operand{P, nullptr, r, (int)r, (int)m, vr};   // A(i,k) = P[k][i]
         g.b = Operand{P, nullptr, r, (int)r, (int)m, vr};   // B(k,j) = P[k][j]
