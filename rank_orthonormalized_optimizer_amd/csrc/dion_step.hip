@@ -1059,6 +1059,29 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
     if (m0 + BM <= u.m && n0 + BN <= u.n && (u.n & 3) == 0) {
         constexpr int TP = BN + 4;
         float* tl = (float*)lds;
+        // every HBM load of the tile (M, G and X) is issued before the first product goes through
+        // LDS, so a workgroup keeps all of its streaming bytes in flight at once
+        using GRaw = std::conditional_t<G_BF16, uint2, float4>;
+        using XRaw = std::conditional_t<X_BF16, uint2, float4>;
+        float4 mv[8];
+        GRaw gr[8];
+        XRaw xr[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = 4 * (t + 256 * q), row = e >> 6, col = e & 63;
+            const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
+            mv[q] = nt_ld4(u.M + off);
+            if constexpr (G_BF16) gr[q] = nt_ld2((const uint16_t*)u.G + off);
+            else gr[q] = nt_ld4((const float*)u.G + off);
+            if constexpr (X_BF16) xr[q] = nt_ld2((const uint16_t*)u.X + off);
+            else xr[q] = nt_ld4((const float*)u.X + off);
+        }
+        auto widen4 = [](auto w) -> float4 {
+            if constexpr (std::is_same_v<decltype(w), uint2>)
+                return float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
+                              bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
+            else return w;
+        };
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -1069,51 +1092,26 @@ __global__ __launch_bounds__(256, 2) void update3_kernel(UpdArgs u) {
                     for (int v = 0; v < 4; ++v)
                         tl[(wm * 64 + 16 * i + 4 * fc + v) * TP + wn * 32 + 16 * j + fr] = pass ? acc2[i][j][v] : acc1[i][j][v];
             __syncthreads();
-            float4 av[8], xv[8], gv[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int e = 4 * (t + 256 * q), row = e >> 6, col = e & 63;
-                av[q] = *(const float4*)&tl[row * TP + col];
-                const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
-                if (pass == 0) {
-                    xv[q] = nt_ld4(u.M + off);
-                    if constexpr (G_BF16) {
-                        const uint2 w = nt_ld2((const uint16_t*)u.G + off);
-                        gv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
-                                       bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
-                    } else {
-                        gv[q] = nt_ld4((const float*)u.G + off);
-                    }
-                } else {
-                    if constexpr (X_BF16) {
-                        const uint2 w = nt_ld2((const uint16_t*)u.X + off);
-                        xv[q] = float4{bf16_bits_to_float(w.x & 0xffffu), bf16_bits_to_float(w.x >> 16),
-                                       bf16_bits_to_float(w.y & 0xffffu), bf16_bits_to_float(w.y >> 16)};
-                    } else {
-                        xv[q] = nt_ld4((const float*)u.X + off);
-                    }
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int e = 4 * (t + 256 * q), row = e >> 6, col = e & 63;
+                const float4 av = *(const float4*)&tl[row * TP + col];
                 const int64_t off = bz * mn + (int64_t)(m0 + row) * u.n + n0 + col;
                 if (pass == 0) {
                     const float c = u.one_minus_mu;
-                    const float4 mnew = float4{(xv[q].x + gv[q].x) - c * av[q].x, (xv[q].y + gv[q].y) - c * av[q].y,
-                                               (xv[q].z + gv[q].z) - c * av[q].z, (xv[q].w + gv[q].w) - c * av[q].w};
+                    const float4 mo = mv[q], gv = widen4(gr[q]);
+                    const float4 mnew = float4{(mo.x + gv.x) - c * av.x, (mo.y + gv.y) - c * av.y,
+                                               (mo.z + gv.z) - c * av.z, (mo.w + gv.w) - c * av.w};
                     nt_st4(u.M + off, mnew);
-                    dmax = fmaxf(fmaxf(fmaxf(dmax, fabsf(mnew.x - xv[q].x)), fmaxf(fabsf(mnew.y - xv[q].y),
-                                 fabsf(mnew.z - xv[q].z))), fabsf(mnew.w - xv[q].w));
-                    smax = fmaxf(fmaxf(fmaxf(smax, fabsf(xv[q].x)), fmaxf(fabsf(xv[q].y), fabsf(xv[q].z))),
-                                 fabsf(xv[q].w));
+                    dmax = fmaxf(fmaxf(fmaxf(dmax, fabsf(mnew.x - mo.x)), fmaxf(fabsf(mnew.y - mo.y),
+                                 fabsf(mnew.z - mo.z))), fabsf(mnew.w - mo.w));
+                    smax = fmaxf(fmaxf(fmaxf(smax, fabsf(mo.x)), fmaxf(fabsf(mo.y), fabsf(mo.z))), fabsf(mo.w));
                 } else {
                     const float c = u.lr_s;
-                    const float4 x = float4{xv[q].x - c * av[q].x, xv[q].y - c * av[q].y, xv[q].z - c * av[q].z,
-                                            xv[q].w - c * av[q].w};
+                    const float4 xo = widen4(xr[q]);
+                    const float4 x = float4{xo.x - c * av.x, xo.y - c * av.y, xo.z - c * av.z, xo.w - c * av.w};
                     if constexpr (X_BF16)
-                        nt_st2((uint16_t*)u.X + off,
-                            uint2{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)});
+                        nt_st2((uint16_t*)u.X + off, uint2{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)});
                     else nt_st4((float*)u.X + off, x);
                 }
             }
