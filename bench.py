@@ -248,7 +248,7 @@ def spectral_block(dev, stream, reps: int = 10, with_cpu: bool = True) -> dict:
         tf = flops / (prod_ms * 1e-3) / 1e12 if prod_ms > 0 else 0.0
         case = {"workload": f"{b}x{r}x{r} Gram stack", "ms_per_call": ms_full,
                 "calls_per_s": 1e3 / ms_full, "product_launch_ms": prod_ms,
-                "roofline": {"bound": "alu", "kernel": "mpi_product_kernel", "achieved": tf,
+                "roofline": {"bound": "mfma", "dtype": "f64", "kernel": "mpi_product_kernel", "achieved": tf,
                              "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s", "frac": tf / PEAK_TFLOPS["f64"],
                              "flops_per_launch": flops,
                              "traffic": measured_traffic(f"spectral-{b}x{r}x{r}", "mpi_product_kernel"),
