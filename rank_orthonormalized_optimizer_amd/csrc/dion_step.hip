@@ -1358,7 +1358,7 @@ static int gram(const ChainCtx& c, const T* P, int mask, int val, bool reduce = 
     return 0;
 }
 
-// arguments of chol_step_kernel (defined with the tile device GEMM below)
+// arguments of chol_step_kernel (defined below, with the LDS block helpers it uses)
 struct CholStepArgs {
     const void* S;       // source of the panel and trailing blocks at this step
     void* L; void* Tf;
