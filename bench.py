@@ -271,6 +271,7 @@ def spectral_block(dev, stream, reps: int = 10, with_cpu: bool = True) -> dict:
 
 
 SPLIT6 = 6.0   # bf16 MFMA products per fp32 product in the exact split form the fp32 contractions use
+SPLIT2 = 3.0   # bf16 MFMA products per fp32 product of the weight pass (two-part split: hh, hl, lh)
 
 
 def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
@@ -282,6 +283,9 @@ def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
     # algorithmic one); fp32 weights as the exact six-product split
     split = 1.0 if wl.x_dtype == "bf16" else SPLIT6
     how = "plain bf16 MFMA products" if split == 1.0 else "fp32 as six bf16 MFMA products"
+    # the weight pass of fp32 weights keeps three part products (its operands are final)
+    usplit = 1.0 if wl.x_dtype == "bf16" else SPLIT2
+    uhow = "plain bf16 MFMA products" if usplit == 1.0 else "fp32 as three bf16 part products (two-part split)"
     out = {}
 
     def add(name, kind, amount, peak_key, factor=1.0, what=""):
@@ -321,7 +325,7 @@ def phase_rooflines(wl, stacks, phase_ms, dion) -> dict:
                                              "6 m r^2 + 2 r^3 / 3 per matrix")
     add("f64_backproject", "flops", 2.0 * mnr64, "f64", 1.0, "R = (M+G)^T P, fp64 MFMA")
     add("norms", "bytes", nb, "hbm", 1.0, "column norms of R, Q' = R c; fp64-chain P, R rounded to fp32")
-    add("update", "flops", 4.0 * (mnr32 + mnr64), "bf16", split, "P R^T and P Q'^T of the M, X update, " + how)
+    add("update", "flops", 4.0 * (mnr32 + mnr64), "bf16", usplit, "P R^T and P Q'^T of the M, X update, " + uhow)
     for k in ("f32_product", "f32_backproject"):   # the HBM side of the products: B read once
         bg = sum(s_["g"].batch * s_["g"].m * s_["g"].n for s_ in stacks) * (4 + (2 if wl.g_dtype == "bf16" else 4))
         if k.startswith("f32") and f64m and sum(f64m) == sum(s_["g"].batch for s_ in stacks):
